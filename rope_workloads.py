@@ -1,0 +1,181 @@
+"""Seeded synthetic inputs for the RoPE apply path.
+
+This module only draws inputs; it holds none of the rotation arithmetic.  Both the GPU
+tests/benchmark and the CPU oracle are fed from here, as CPU tensors (PyTorch is used as
+host memory and as a seeded normal generator).
+
+Inputs follow the workloads the pages describe: BSND activations with a partial slice on
+the head dim for the in-place op, 2-D query/key rows with a [maxSeqLen, rotaryDim] cos|sin
+cache for the cache op, and the mrope position layout (text tokens with three equal rows,
+image tokens with temporal/height/width grid indices).  Activations are N(0, 1) in float32,
+rounded to the tensor dtype by PyTorch's own conversion.  cos/sin tables hold the standard
+RoPE angles pos * theta^(-2i/d) (theta = 10000), computed in float64 and rounded once to
+the table dtype, so both sides of a comparison read the very same bytes.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+THETA = 10000.0
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def randn(shape, dtype, gen):
+    return torch.randn(tuple(shape), generator=gen, dtype=torch.float32).to(dtype)
+
+
+def angles(pos: np.ndarray, n_freq: int, dim: int) -> np.ndarray:
+    """float64 [len(pos), n_freq] angles pos * theta^(-2i/dim), i < n_freq."""
+    inv = THETA ** (-2.0 * np.arange(n_freq, dtype=np.float64) / dim)
+    return np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]
+
+
+def pairwise_tables(pos: np.ndarray, length: int, dtype) -> tuple[torch.Tensor, torch.Tensor]:
+    """cos/sin rows of `length` elements for the interleave layout: the angle of pair i is
+    repeated on elements 2i and 2i+1.  Returns float64-derived tensors of `dtype`."""
+    a = angles(pos, length // 2, length)
+    a = np.repeat(a, 2, axis=1)
+    c = torch.from_numpy(np.cos(a)).to(dtype)
+    s = torch.from_numpy(np.sin(a)).to(dtype)
+    return c, s
+
+
+def cos_sin_cache(max_seq: int, rotary_dim: int, dtype) -> torch.Tensor:
+    """[max_seq, rotary_dim] cache: cos of the rotary_dim/2 angles, then their sin."""
+    a = angles(np.arange(max_seq), rotary_dim // 2, rotary_dim)
+    return torch.from_numpy(np.concatenate([np.cos(a), np.sin(a)], axis=1)).to(dtype)
+
+
+# ------------------------------------------------------------------------------------------
+# The in-place op
+# ------------------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class InplaceCase:
+    name: str
+    x: torch.Tensor
+    cos: torch.Tensor
+    sin: torch.Tensor
+    partial_slice: list | None
+    tokens: int           # B*S
+    algo_bytes: int       # bytes the op must move (slice read+write, cos, sin)
+
+
+def inplace_case(name, B, S, N, D, xdtype, cdtype, partial_slice, cos_shape=None, seed=0,
+                 table="angles"):
+    """x ~ N(0,1) of shape [B,S,N,D]; cos/sin of `cos_shape` (default BS1D) over the slice.
+
+    table="angles": cos/sin from angle s * theta^(-2i/L) repeated per pair (s = sequence
+    index of the row); table="randn": independent N(0,1) values (per-element cos/sin).
+    """
+    g = torch.Generator().manual_seed(seed)
+    x = randn((B, S, N, D), xdtype, g)
+    start, end = (0, D) if partial_slice is None else partial_slice
+    L = end - start
+    cshape = list(cos_shape) if cos_shape is not None else [B, S, 1, L]
+    if table == "angles":
+        pos = np.arange(cshape[1]) if cshape[1] > 1 else np.zeros(1)
+        c, s = pairwise_tables(pos, L, cdtype)          # [Sc, L]
+        c = c.reshape(1, cshape[1], 1, L).expand(cshape).contiguous()
+        s = s.reshape(1, cshape[1], 1, L).expand(cshape).contiguous()
+    else:
+        c = randn(cshape, cdtype, g)
+        s = randn(cshape, cdtype, g)
+    xs = x.element_size()
+    cs = c.element_size()
+    rows = B * S * N
+    crow_count = int(np.prod(cshape[:3]))
+    algo = rows * L * xs * 2 + 2 * crow_count * L * cs
+    return InplaceCase(name, x, c, s, partial_slice, B * S, algo)
+
+
+def config_c1():
+    """fp32 x [1,16,2,64], slice [0,64), cos/sin fp32 [1,16,1,64] from angles per pair."""
+    return inplace_case("inplace_f32_1x16x2x64", 1, 16, 2, 64, torch.float32, torch.float32,
+                        [0, 64], seed=1001)
+
+
+def config_c2():
+    """bf16 x [8,4096,1,576], slice [512,576), cos/sin fp32 [8,4096,1,64] (pos = s)."""
+    return inplace_case("inplace_bf16x_f32cs_8x4096x1x576_slice512_576", 8, 4096, 1, 576,
+                        torch.bfloat16, torch.float32, [512, 576], seed=1002)
+
+
+# ------------------------------------------------------------------------------------------
+# The cache op
+# ------------------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class CacheCase:
+    name: str
+    positions: torch.Tensor
+    query: torch.Tensor
+    key: torch.Tensor
+    cache: torch.Tensor
+    mrope_section: list | None
+    head_size: int
+    is_neox: bool
+    tokens: int
+    algo_bytes: int
+
+
+def cache_algo_bytes(T, nq, nk, H, rd, es, npos_rows):
+    """q/k rows read and written in full, one gathered rd-row per token, positions."""
+    return T * ((nq + nk) * H * es * 2 + rd * es + 8 * npos_rows)
+
+
+def cache_case(name, T, nq, nk, H, rd, dtype, is_neox, max_seq, seed, mrope_section=None,
+               positions=None):
+    g = torch.Generator().manual_seed(seed)
+    q = randn((T, nq * H), dtype, g)
+    k = randn((T, nk * H), dtype, g)
+    cache = cos_sin_cache(max_seq, rd, dtype)
+    if positions is None:
+        positions = torch.randint(0, max_seq, (T,), generator=g, dtype=torch.int64)
+    nrows = 1 if positions.dim() == 1 else positions.shape[0]
+    es = q.element_size()
+    return CacheCase(name, positions, q, k, cache, mrope_section, H, is_neox, T,
+                     cache_algo_bytes(T, nq, nk, H, rd, es, nrows))
+
+
+def mrope_positions(T_text: int, frames: int, grid_h: int, grid_w: int, m: int = 3):
+    """[m, T] positions: text tokens carry their index on every row; image tokens carry
+    (frame, row, column) grid indices on rows 0/1/2 (a 4th row, if asked, repeats row 0)."""
+    T_img = frames * grid_h * grid_w
+    text = torch.arange(T_text, dtype=torch.int64)
+    idx = torch.arange(T_img, dtype=torch.int64)
+    t_idx = idx // (grid_h * grid_w)
+    h_idx = (idx // grid_w) % grid_h
+    w_idx = idx % grid_w
+    rows = [torch.cat([text, t_idx]), torch.cat([text, h_idx]), torch.cat([text, w_idx])]
+    if m == 4:
+        rows.append(torch.cat([text, t_idx]))
+    return torch.stack(rows).contiguous()
+
+
+def config_c3():
+    """rope NeoX bf16: T=8192, q [8192, 32*128], k [8192, 8*128], cache [32768, 128]."""
+    return cache_case("cache_rope_neox_bf16_T8192_q32_k8_H128", 8192, 32, 8, 128, 128,
+                      torch.bfloat16, True, 32768, seed=1003)
+
+
+def config_c4():
+    """rope GPT-J fp16 partial: T=32768, q/k [T, 32*128], rd 64, cache [65536, 64]."""
+    return cache_case("cache_rope_gptj_f16_T32768_q32_k32_H128_rd64", 32768, 32, 32, 128, 64,
+                      torch.float16, False, 65536, seed=1004)
+
+
+def config_c5():
+    """mrope [16,24,24] NeoX bf16: T=16384, q [T, 28*128], k [T, 4*128], cache [32768, 128]."""
+    pos = mrope_positions(8192, 2, 64, 64)
+    return cache_case("cache_mrope_16_24_24_neox_bf16_T16384_q28_k4_H128", 16384, 28, 4, 128,
+                      128, torch.bfloat16, True, 32768, seed=1005, mrope_section=[16, 24, 24],
+                      positions=pos)
+
+
+CONFIGS = {"c1": config_c1, "c2": config_c2, "c3": config_c3, "c4": config_c4,
+           "c5": config_c5}
