@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the RoPE apply path on one MI355X: achieved HBM GB/s (and fraction of the
+8 TB/s peak) and tokens/s.
+
+One step is one pass of the in-place partial interleave op over one batch of the headline
+workload: bf16 x [8,4096,1,576], slice [512,576), fp32 cos/sin [8,4096,1,64] (32768 tokens).
+The cos/sin-cache kernel is timed the same way on its three workloads (rope NeoX bf16, rope
+GPT-J fp16 with a pass-through half, mrope bf16) and reported in `kernels`.
+
+Timing: inputs are resident in HBM; launches cycle over enough copies of the inputs that
+every pass touches >= 512 MiB before a buffer is reused (MI355X's 256 MB Infinity Cache
+cannot hold the working set); the host queues the timed launches behind a short GPU spin so
+that they run back to back, and two HIP events on the launch stream bracket exactly `steps`
+launches.  Rank 0 prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+MALL_DEFEAT_BYTES = 512 << 20  # touched bytes between reuses of one buffer set
+KERNEL_SRC = os.path.join(ROOT, "rope_partial_inplace_amd", "csrc", "rope_kernels.hip")
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ------------------------------------------------------------------------------------------
+# GPU timing
+# ------------------------------------------------------------------------------------------
+
+def spin_cycles_per_ms(torch) -> float:
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    torch.cuda._sleep(2_000_000)
+    b.record()
+    torch.cuda.synchronize()
+    return 2_000_000 / max(a.elapsed_time(b), 1e-3)
+
+
+def time_launches(torch, calls, steps: int, warmup: int, cyc_per_ms: float):
+    """Mean GPU time per launch (ms) over `steps` back-to-back launches cycling over calls."""
+    n = len(calls)
+    for i in range(warmup):
+        calls[i % n]()
+    torch.cuda.synchronize()
+    # host enqueue cost per launch, to size the spin that hides it
+    t0 = time.perf_counter()
+    for i in range(min(steps, 20)):
+        calls[i % n]()
+    host_ms = (time.perf_counter() - t0) * 1e3 / min(steps, 20)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for attempt in range(3):
+        spin_ms = 1.0 + 1.5 * host_ms * steps * (1 + attempt)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(spin_ms * cyc_per_ms))
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            calls[i % n]()
+        end.record()
+        enqueue_ms = (time.perf_counter() - t0) * 1e3
+        torch.cuda.synchronize()
+        if enqueue_ms < spin_ms:  # the GPU never waited for the host
+            break
+        log(f"host enqueue {enqueue_ms:.2f} ms exceeded the {spin_ms:.2f} ms spin; retrying")
+    return start.elapsed_time(end) / steps
+
+
+def copy_ceiling_gbs(torch, nbytes=1 << 30) -> float:
+    """Device-to-device copy bandwidth (read + write bytes) at a footprint well above the
+    Infinity Cache: the attainable-bandwidth context for the kernels."""
+    a = torch.empty(nbytes // 2, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(10):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / 10
+    return 2 * a.numel() / (ms * 1e-3) / 1e9
+
+
+# ------------------------------------------------------------------------------------------
+# workloads
+# ------------------------------------------------------------------------------------------
+
+def n_sets_for(algo_bytes: int) -> int:
+    return max(1, math.ceil(MALL_DEFEAT_BYTES / algo_bytes))
+
+
+def inplace_calls(ra, case, n_sets):
+    calls = []
+    for i in range(n_sets):
+        x = case.x if i == 0 else case.x.clone()
+        c = case.cos if i == 0 else case.cos.clone()
+        s = case.sin if i == 0 else case.sin.clone()
+        calls.append(ra.prepare_partial_inplace(x, c, s, 1, case.partial_slice))
+    return calls
+
+
+def cache_calls(ra, torch, case, n_sets):
+    calls = []
+    for i in range(n_sets):
+        q = case.query if i == 0 else case.query.clone()
+        k = case.key if i == 0 else case.key.clone()
+        p = case.positions if i == 0 else case.positions.clone()
+        qo, ko = torch.empty_like(q), torch.empty_like(k)
+        calls.append(ra.prepare_with_cos_sin_cache(p, q, k, case.cache, case.mrope_section,
+                                                   case.head_size, case.is_neox, qo, ko))
+    return calls
+
+
+def describe_case(name, case):
+    if hasattr(case, "x"):
+        return (f"InplacePartialRotaryMul interleave x {str(case.x.dtype)[6:]} "
+                f"{list(case.x.shape)} slice {case.partial_slice} cos/sin "
+                f"{str(case.cos.dtype)[6:]} {list(case.cos.shape)}")
+    mode = f"mrope {case.mrope_section}" if case.mrope_section else "rope"
+    style = "NeoX" if case.is_neox else "GPT-J"
+    return (f"RopeWithSinCosCache {mode} {style} {str(case.query.dtype)[6:]} T={case.tokens} "
+            f"q {list(case.query.shape)} k {list(case.key.shape)} headSize {case.head_size} "
+            f"rotaryDim {case.cache.shape[1]}")
+
+
+def kernel_name(case) -> str:
+    return "inplace_interleave_kernel" if hasattr(case, "x") else "cos_sin_cache_kernel"
+
+
+def traffic_for(workload: str):
+    """Measured HBM bytes per launch from the committed PMC summary, when it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, on the host
+# ------------------------------------------------------------------------------------------
+
+def cpu_baseline(case, budget_s: float):
+    import oracle
+    x = case.x.cpu()
+    c, s = case.cos.cpu(), case.sin.cpu()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        st, _ = oracle.rope_partial_inplace(x, c, s, 1, case.partial_slice)
+        assert st == 0, oracle.last_error()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {
+        "value": round(case.algo_bytes * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"the full headline batch ({case.tokens} tokens) passed {reps} times through "
+                   f"the single-threaded C oracle in {el:.1f} s"),
+        "tokens_per_s": round(case.tokens * reps / el, 1),
+        "host_cpu": platform.processor() or platform.machine(),
+        "host_cores_visible": len(os.sched_getaffinity(0)),
+    }
+
+
+# ------------------------------------------------------------------------------------------
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workloads", default="c2,c1,c3,c4,c5",
+                    help="first is the headline; the rest are reported under `kernels`")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=10.0)
+    ap.add_argument("--resident", action="store_true",
+                    help="also time without buffer rotation (Infinity-Cache-resident)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the RoPE path has no cross-GPU step; see the sharding notes)", file=sys.stderr)
+        return 2
+
+    import torch
+    sys.path.insert(0, ROOT)
+    import rope_partial_inplace_amd as ra
+    import rope_workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), "
+        f"{props.multi_processor_count} CUs")
+    cyc = spin_cycles_per_ms(torch)
+    names = [w.strip() for w in args.workloads.split(",") if w.strip()]
+    results = {}
+    cases = {}
+    for wi, name in enumerate(names):
+        case = W.CONFIGS[name](dev)
+        cases[name] = case
+        n_sets = 1 if name == "c1" else n_sets_for(case.algo_bytes)
+        calls = (inplace_calls(ra, case, n_sets) if hasattr(case, "x")
+                 else cache_calls(ra, torch, case, n_sets))
+        steps = args.steps if wi == 0 else max(20, min(args.steps, 100))
+        ms = time_launches(torch, calls, steps, args.warmup, cyc)
+        gbs = case.algo_bytes / (ms * 1e-3) / 1e9
+        r = {"workload": describe_case(name, case), "kernel": kernel_name(case),
+             "us_per_launch": round(ms * 1e3, 3), "gbs": round(gbs, 1),
+             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+             "tokens_per_s": round(case.tokens / (ms * 1e-3), 1),
+             "algo_bytes_per_launch": case.algo_bytes, "buffer_sets": n_sets, "steps": steps}
+        if args.resident:
+            ms_r = time_launches(torch, calls[:1], steps, args.warmup, cyc)
+            r["resident_us_per_launch"] = round(ms_r * 1e3, 3)
+            r["resident_gbs"] = round(case.algo_bytes / (ms_r * 1e-3) / 1e9, 1)
+        results[name] = r
+        log(f"{name}: {r['us_per_launch']} us/launch, {r['gbs']} GB/s "
+            f"({100 * r['frac_of_hbm_peak']:.1f}% of peak), {n_sets} buffer sets")
+        del calls
+        if wi > 0:
+            del cases[name]
+        torch.cuda.empty_cache()
+
+    head = names[0]
+    hr = results[head]
+    ceiling = copy_ceiling_gbs(torch)
+    log(f"device-to-device copy: {ceiling:.0f} GB/s")
+    out = {
+        "metric": "achieved HBM GB/s (and % of peak) + tokens/sec for RoPE apply on one MI355X",
+        "value": hr["gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": hr["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(hr["us_per_launch"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) activations, RoPE angle tables theta=10000)",
+        "config": {"workload": hr["workload"], "tokens": cases[head].tokens,
+                   "algo_bytes_per_step": hr["algo_bytes_per_launch"],
+                   "buffer_sets": hr["buffer_sets"], "storage_dtypes": "x bf16, cos/sin f32"
+                   if head == "c2" else "see workload"},
+        "tokens_per_s": hr["tokens_per_s"],
+        "roofline": {"bound": "hbm", "achieved": hr["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": hr["frac_of_hbm_peak"],
+                     "traffic": traffic_for(head), "kernel": hr["kernel"]},
+        "kernels": {k: v for k, v in results.items() if k != head},
+        "copy_ceiling_gbs": round(ceiling, 1),
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for ~{args.cpu_budget_s:.0f} s")
+        out["cpu_baseline"] = cpu_baseline(cases[head], args.cpu_budget_s)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,199 @@
+"""Python binding of librope_amd.so, the MI355X (gfx950) RoPE apply library.
+
+Argument marshalling only: tensors are described (pointer, dtype, shape, strides) and handed
+to the C ABI declared in ``include/rope.h`` together with the current HIP stream; every step
+of both operations runs in the library's HIP kernels.  PyTorch provides device memory and
+streams.  There is no fallback: if the library is not built this import fails.
+
+  rope_partial_inplace(x, cos, sin, rotary_mode=1, partial_slice=None, stream=None)
+  rope_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,
+                          head_size, is_neox_style, query_out=None, key_out=None, stream=None)
+
+Pages defining the operations:
+  [IPRM] "CANN ops-transformer 的 aclnnInplacePartialRotaryMul 算子：Inplace 部分旋转位置编码接口详解与实现剖析"
+  [RSCC] "CANN ops-transformer 旋转位置编码算子 RopeWithSinCosCache 深度解析：cache 化 RoPE 的计算原理与 aclnn 两段式调用实战"
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+ROPE_OK = 0
+ROPE_ERR_PARAM_NULLPTR = 161001
+ROPE_ERR_PARAM_INVALID = 161002
+ROPE_ERR_RUNTIME = 361001
+
+ROPE_F32, ROPE_F16, ROPE_BF16, ROPE_I64 = 0, 1, 2, 3
+
+
+class RopeTensor(ctypes.Structure):
+    """Mirror of ``rope_tensor`` in include/rope.h."""
+
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int),
+        ("ndim", ctypes.c_int32),
+        ("shape", ctypes.c_int64 * 4),
+        ("stride", ctypes.c_int64 * 4),
+    ]
+
+
+class RopeError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"rope error {code}: {message}")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m rope_partial_inplace_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.rope_partial_inplace.argtypes = [P(RopeTensor), P(RopeTensor), P(RopeTensor),
+                                         ctypes.c_int64, P(ctypes.c_int64), ctypes.c_int64,
+                                         ctypes.c_void_p]
+    lib.rope_partial_inplace.restype = ctypes.c_int
+    lib.rope_with_cos_sin_cache.argtypes = [P(RopeTensor), P(RopeTensor), P(RopeTensor),
+                                            P(RopeTensor), P(ctypes.c_int64), ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_int, P(RopeTensor),
+                                            P(RopeTensor), ctypes.c_void_p]
+    lib.rope_with_cos_sin_cache.restype = ctypes.c_int
+    lib.rope_last_error.argtypes = []
+    lib.rope_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+
+def last_error() -> str:
+    return LIB.rope_last_error().decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.float32: ROPE_F32, torch.float16: ROPE_F16, torch.bfloat16: ROPE_BF16,
+            torch.int64: ROPE_I64}.get(t.dtype, 99)
+
+
+def describe(t) -> RopeTensor:
+    """A ``rope_tensor`` describing a torch tensor (which must outlive the call)."""
+    if t.dim() > 4:
+        raise RopeError(ROPE_ERR_PARAM_INVALID, "tensors of more than 4 dims are not supported")
+    d = RopeTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = _dtype_code(t)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _int_array(values):
+    if values is None:
+        return None, 0
+    vals = [int(v) for v in values]
+    return (ctypes.c_int64 * max(len(vals), 1))(*vals), len(vals)
+
+
+def _device_of(tensors):
+    dev = None
+    for t in tensors:
+        if t is None or t.numel() == 0:
+            continue
+        if not t.is_cuda:
+            raise RopeError(ROPE_ERR_PARAM_INVALID,
+                            "tensors must live in GPU memory (torch device 'cuda')")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise RopeError(ROPE_ERR_PARAM_INVALID, "tensors are on different devices")
+    return dev
+
+
+def _stream_handle(stream, dev):
+    import torch
+    if stream is None:
+        if dev is None:
+            return None
+        stream = torch.cuda.current_stream(dev)
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(code: int):
+    if code != ROPE_OK:
+        raise RopeError(code, last_error())
+
+
+def rope_partial_inplace(x, cos, sin, rotary_mode: int = 1, partial_slice=None, stream=None):
+    """In-place partial interleave RoPE on x[..., start:end) ([IPRM §计算原理与公式])."""
+    dev = _device_of([x, cos, sin])
+    dx, dc, ds = describe(x), describe(cos), describe(sin)
+    sl, sl_len = _int_array(partial_slice)
+    _check(LIB.rope_partial_inplace(ctypes.byref(dx), ctypes.byref(dc), ctypes.byref(ds),
+                                    int(rotary_mode), sl, sl_len, _stream_handle(stream, dev)))
+
+
+def rope_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section=None,
+                            head_size: int | None = None, is_neox_style: bool = True,
+                            query_out=None, key_out=None, stream=None):
+    """RoPE with a cos/sin cache ([RSCC §设计动机]); returns (query_out, key_out).
+
+    Outputs are allocated (contiguous) when not given; ``head_size`` defaults to the cache's
+    rotaryDim."""
+    import torch
+    if head_size is None:
+        head_size = cos_sin_cache.shape[-1]
+    if query_out is None:
+        query_out = torch.empty(query_in.shape, dtype=query_in.dtype, device=query_in.device)
+    if key_out is None:
+        key_out = torch.empty(key_in.shape, dtype=key_in.dtype, device=key_in.device)
+    dev = _device_of([positions, query_in, key_in, cos_sin_cache, query_out, key_out])
+    descs = [describe(t) for t in (positions, query_in, key_in, cos_sin_cache, query_out,
+                                   key_out)]
+    ms, ms_len = _int_array(mrope_section)
+    _check(LIB.rope_with_cos_sin_cache(ctypes.byref(descs[0]), ctypes.byref(descs[1]),
+                                       ctypes.byref(descs[2]), ctypes.byref(descs[3]), ms,
+                                       ms_len, int(head_size), int(bool(is_neox_style)),
+                                       ctypes.byref(descs[4]), ctypes.byref(descs[5]),
+                                       _stream_handle(stream, dev)))
+    return query_out, key_out
+
+
+class PreparedCall:
+    """A call whose arguments are marshalled once (for tight launch loops): invoking it
+    issues exactly one C-ABI call with the prebuilt descriptors.  The tensors must stay
+    alive and keep their storage while the object is used."""
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self) -> None:
+        _check(self._fn(*self._args))
+
+
+def prepare_partial_inplace(x, cos, sin, rotary_mode: int = 1, partial_slice=None,
+                            stream=None) -> PreparedCall:
+    dev = _device_of([x, cos, sin])
+    dx, dc, ds = describe(x), describe(cos), describe(sin)
+    sl, sl_len = _int_array(partial_slice)
+    args = (ctypes.byref(dx), ctypes.byref(dc), ctypes.byref(ds), int(rotary_mode), sl, sl_len,
+            _stream_handle(stream, dev))
+    return PreparedCall(LIB.rope_partial_inplace, args, (x, cos, sin, dx, dc, ds, sl))
+
+
+def prepare_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,
+                               head_size, is_neox_style, query_out, key_out,
+                               stream=None) -> PreparedCall:
+    tensors = (positions, query_in, key_in, cos_sin_cache, query_out, key_out)
+    dev = _device_of(list(tensors))
+    descs = [describe(t) for t in tensors]
+    ms, ms_len = _int_array(mrope_section)
+    args = (ctypes.byref(descs[0]), ctypes.byref(descs[1]), ctypes.byref(descs[2]),
+            ctypes.byref(descs[3]), ms, ms_len, int(head_size), int(bool(is_neox_style)),
+            ctypes.byref(descs[4]), ctypes.byref(descs[5]), _stream_handle(stream, dev))
+    return PreparedCall(LIB.rope_with_cos_sin_cache, args, (tensors, descs, ms))

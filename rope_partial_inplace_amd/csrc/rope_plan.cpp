@@ -1,0 +1,352 @@
+// rope_plan.cpp -- argument validation and launch planning of librope_amd.so (host only; no
+// HIP call is made here, so every error path runs on a machine without a GPU).
+//
+// Pages:
+//   [IPRM] "CANN ops-transformer 的 aclnnInplacePartialRotaryMul 算子：Inplace 部分旋转位置编码
+//           接口详解与实现剖析"
+//   [RSCC] "CANN ops-transformer 旋转位置编码算子 RopeWithSinCosCache 深度解析：cache 化 RoPE 的
+//           计算原理与 aclnn 两段式调用实战"
+#include <algorithm>
+#include <cstdint>
+#include <string>
+
+#include "rope_plan.h"
+
+namespace ropeamd {
+namespace {
+
+int bytes_of(rope_dtype dt) {
+  switch (dt) {
+    case ROPE_F32: return 4;
+    case ROPE_F16: return 2;
+    case ROPE_BF16: return 2;
+    case ROPE_I64: return 8;
+  }
+  return 0;
+}
+
+bool is_float(rope_dtype dt) { return dt == ROPE_F32 || dt == ROPE_F16 || dt == ROPE_BF16; }
+
+bool valid_rank(const rope_tensor *t) {
+  if (t->ndim < 1 || t->ndim > 4) return false;
+  for (int d = 0; d < t->ndim; ++d)
+    if (t->shape[d] < 0) return false;
+  return true;
+}
+
+int64_t count(const rope_tensor *t) {
+  int64_t n = 1;
+  for (int d = 0; d < t->ndim; ++d) n *= t->shape[d];
+  return n;
+}
+
+bool row_major(const rope_tensor *t) {
+  int64_t want = 1;
+  for (int d = t->ndim - 1; d >= 0; --d) {
+    if (t->shape[d] > 1 && t->stride[d] != want) return false;
+    want *= t->shape[d];
+  }
+  return true;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int reject(std::string *err, int code, const char *why) {
+  if (err) *err = why;
+  return code;
+}
+
+// Bytes [first, last) an N-d view reaches (non-negative strides).
+void extent(const rope_tensor *t, uintptr_t *first, uintptr_t *last) {
+  int64_t far = 0;
+  for (int d = 0; d < t->ndim; ++d) far += (t->shape[d] - 1) * t->stride[d];
+  *first = reinterpret_cast<uintptr_t>(t->data);
+  *last = *first + uintptr_t((far + 1) * bytes_of(t->dtype));
+}
+
+bool overlap(const rope_tensor *a, const rope_tensor *b) {
+  uintptr_t a0, a1, b0, b1;
+  extent(a, &a0, &a1);
+  extent(b, &b0, &b1);
+  return a0 < b1 && b0 < a1;
+}
+
+bool identical_view(const rope_tensor *a, const rope_tensor *b) {
+  if (a->data != b->data || a->ndim != b->ndim || a->dtype != b->dtype) return false;
+  for (int d = 0; d < a->ndim; ++d) {
+    if (a->shape[d] != b->shape[d]) return false;
+    if (a->shape[d] > 1 && a->stride[d] != b->stride[d]) return false;
+  }
+  return true;
+}
+
+const int64_t kMropeLists[5][4] = {
+    {16, 24, 24, 0}, {8, 12, 12, 0}, {24, 20, 20, 0}, {11, 11, 10, 0}, {16, 16, 16, 16}};
+const int kMropeListLen[5] = {3, 3, 3, 3, 4};
+
+}  // namespace
+
+// Validation order: null arguments (161001) first, then dtype, mode, rank/shape, slice and
+// layout checks (161002), [IPRM §返回值与错误码] and [IPRM §约束说明].
+int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor *sin,
+                 int64_t rotary_mode, const int64_t *partial_slice, int64_t partial_slice_len,
+                 InplacePlan *plan, std::string *err) {
+  *plan = InplacePlan();
+  if (x == nullptr || cos == nullptr || sin == nullptr)
+    return reject(err, ROPE_ERR_PARAM_NULLPTR, "xRef, cos or sin is NULL");
+  if (partial_slice == nullptr && partial_slice_len > 0)
+    return reject(err, ROPE_ERR_PARAM_NULLPTR, "partial_slice is NULL with a non-zero length");
+  for (const rope_tensor *t : {x, cos, sin})
+    if (valid_rank(t) && count(t) > 0 && t->data == nullptr)
+      return reject(err, ROPE_ERR_PARAM_NULLPTR, "a non-empty tensor has NULL data");
+
+  if (!is_float(x->dtype)) return reject(err, ROPE_ERR_PARAM_INVALID, "xRef dtype unsupported");
+  if (cos->dtype != sin->dtype)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "cos and sin dtypes differ");
+  if (cos->dtype != x->dtype && cos->dtype != ROPE_F32)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "cos/sin must have xRef's dtype or float32");
+  if (rotary_mode != 1)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "rotary_mode must be 1 (interleave)");
+
+  for (const rope_tensor *t : {x, cos, sin})
+    if (!valid_rank(t) || t->ndim != 4)
+      return reject(err, ROPE_ERR_PARAM_INVALID, "xRef, cos and sin must be 4-D");
+  for (int d = 0; d < 4; ++d)
+    if (cos->shape[d] != sin->shape[d])
+      return reject(err, ROPE_ERR_PARAM_INVALID, "cos and sin shapes differ");
+  const int64_t D = x->shape[3];
+  if (D > 1024) return reject(err, ROPE_ERR_PARAM_INVALID, "D > 1024");
+  if (D % 2 != 0) return reject(err, ROPE_ERR_PARAM_INVALID, "D is odd");
+
+  int64_t start = 0, end = D;
+  if (partial_slice != nullptr || partial_slice_len != 0) {
+    if (partial_slice_len != 2)
+      return reject(err, ROPE_ERR_PARAM_INVALID, "partial_slice must hold 2 values");
+    start = partial_slice[0];
+    end = partial_slice[1];
+  }
+  if (start < 0 || end < 0 || end > D || end < start)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "partial_slice out of range");
+  const int64_t L = end - start;
+  if (L % 2 != 0) return reject(err, ROPE_ERR_PARAM_INVALID, "slice length is odd");
+  if (!row_major(x) || !row_major(cos) || !row_major(sin))
+    return reject(err, ROPE_ERR_PARAM_INVALID, "non-contiguous tensors are not supported");
+
+  if (L == 0) {  // empty slice: no-op, before the cos/sin last-dim check
+    plan->noop = true;
+    return ROPE_OK;
+  }
+  if (cos->shape[3] != L)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "cos/sin last dim != slice length");
+  for (int d = 0; d < 3; ++d)
+    if (cos->shape[d] != 1 && cos->shape[d] != x->shape[d])
+      return reject(err, ROPE_ERR_PARAM_INVALID, "cos/sin do not broadcast to xRef");
+
+  InplacePlan &p = *plan;
+  p.xdt = x->dtype;
+  p.cdt = cos->dtype;
+  p.x = x->data;
+  p.cos = cos->data;
+  p.sin = sin->data;
+  p.B = x->shape[0];
+  p.S = x->shape[1];
+  p.N = x->shape[2];
+  p.D = D;
+  p.start = start;
+  p.L = L;
+  p.rows = p.B * p.S * p.N;
+  if (p.rows == 0) {
+    p.noop = true;
+    return ROPE_OK;
+  }
+  const int64_t Sc = cos->shape[1], Nc = cos->shape[2];
+  p.cn = cos->shape[2] == 1 ? 0 : 1;
+  p.cs = cos->shape[1] == 1 ? 0 : Nc;
+  p.cb = cos->shape[0] == 1 ? 0 : Sc * Nc;
+
+  // 16-byte vectors of x when every chunk start is 16-byte aligned; else element access.
+  const int xs = bytes_of(p.xdt), cs = bytes_of(p.cdt);
+  const int64_t v16 = 16 / xs;
+  const bool ok16 = L % v16 == 0 && (D * xs) % 16 == 0 && (start * xs) % 16 == 0 &&
+                    aligned16(p.x) && aligned16(p.cos) && aligned16(p.sin) &&
+                    (L * cs) % 16 == 0;
+  p.vector_io = ok16;
+  p.vec = ok16 ? uint32_t(v16) : 2u;
+  p.chunks_per_row = uint32_t(L / p.vec);
+  p.items = p.rows * p.chunks_per_row;
+  p.idx32 = p.items < (int64_t(1) << 32);
+  p.div_cpr = make_fastdiv(p.chunks_per_row);
+  p.div_n = make_fastdiv(uint32_t(std::min<int64_t>(p.N, 0xffffffff)));
+  p.div_s = make_fastdiv(uint32_t(std::min<int64_t>(p.S, 0xffffffff)));
+  if (p.N > 0xffffffffLL || p.S > 0xffffffffLL) p.idx32 = false;
+  return ROPE_OK;
+}
+
+// [RSCC §入参校验逻辑] (null, dtype, shape, mropeSection checks) and [RSCC §约束说明]
+// (64-byte alignment of headSize and rotaryDim, rotaryDim <= headSize).
+int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
+               const rope_tensor *key_in, const rope_tensor *cache,
+               const int64_t *mrope_section, int64_t mrope_section_len, int64_t head_size,
+               int is_neox_style, const rope_tensor *query_out, const rope_tensor *key_out,
+               CachePlan *plan, std::string *err) {
+  *plan = CachePlan();
+  const rope_tensor *all[6] = {positions, query_in, key_in, cache, query_out, key_out};
+  for (const rope_tensor *t : all)
+    if (t == nullptr) return reject(err, ROPE_ERR_PARAM_NULLPTR, "a tensor argument is NULL");
+  if (mrope_section == nullptr && mrope_section_len > 0)
+    return reject(err, ROPE_ERR_PARAM_NULLPTR, "mrope_section is NULL with a non-zero length");
+  if (mrope_section_len < 0)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "negative mrope_section length");
+  for (const rope_tensor *t : all)
+    if (valid_rank(t) && count(t) > 0 && t->data == nullptr)
+      return reject(err, ROPE_ERR_PARAM_NULLPTR, "a non-empty tensor has NULL data");
+
+  if (positions->dtype != ROPE_I64)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "positions must be int64");
+  const rope_dtype dt = query_in->dtype;
+  if (!is_float(dt)) return reject(err, ROPE_ERR_PARAM_INVALID, "queryIn dtype unsupported");
+  for (const rope_tensor *t : {key_in, cache, query_out, key_out})
+    if (t->dtype != dt)
+      return reject(err, ROPE_ERR_PARAM_INVALID, "all float tensors must share queryIn's dtype");
+
+  for (const rope_tensor *t : {query_in, key_in, cache, query_out, key_out})
+    if (!valid_rank(t) || t->ndim != 2)
+      return reject(err, ROPE_ERR_PARAM_INVALID, "queryIn, keyIn, cache and outputs must be 2-D");
+  for (const rope_tensor *t : {query_in, key_in, cache})
+    if (t->shape[0] == 0 || t->shape[1] == 0)
+      return reject(err, ROPE_ERR_PARAM_INVALID, "queryIn, keyIn and cache must be non-empty");
+  if (key_in->shape[0] != query_in->shape[0])
+    return reject(err, ROPE_ERR_PARAM_INVALID, "keyIn and queryIn differ in token count");
+  for (int d = 0; d < 2; ++d)
+    if (query_out->shape[d] != query_in->shape[d] || key_out->shape[d] != key_in->shape[d])
+      return reject(err, ROPE_ERR_PARAM_INVALID, "output shape differs from input shape");
+
+  const int64_t T = query_in->shape[0];
+  const int64_t rd = cache->shape[1];
+
+  bool mrope = false;
+  int nsec = 0;
+  int64_t sec[4] = {0, 0, 0, 0};
+  if (mrope_section_len > 0) {
+    if (mrope_section_len != 3 && mrope_section_len != 4)
+      return reject(err, ROPE_ERR_PARAM_INVALID, "mrope_section needs 3 or 4 entries");
+    int64_t total = 0;
+    for (int64_t i = 0; i < mrope_section_len; ++i) {
+      if (mrope_section[i] < 0)
+        return reject(err, ROPE_ERR_PARAM_INVALID, "negative mrope_section entry");
+      total += mrope_section[i];
+    }
+    if (mrope_section[0] > 0) {
+      if (2 * total != rd)
+        return reject(err, ROPE_ERR_PARAM_INVALID, "2*sum(mrope_section) != rotaryDim");
+      bool found = false;
+      for (int w = 0; w < 5 && !found; ++w) {
+        if (kMropeListLen[w] != mrope_section_len) continue;
+        found = std::equal(mrope_section, mrope_section + mrope_section_len, kMropeLists[w]);
+      }
+      if (!found)
+        return reject(err, ROPE_ERR_PARAM_INVALID, "mrope_section is not a supported list");
+      mrope = true;
+      nsec = int(mrope_section_len);
+      for (int i = 0; i < nsec; ++i) sec[i] = mrope_section[i];
+    }
+  }
+
+  const int es = bytes_of(dt);
+  const int64_t align_elems = 64 / es;
+  if (head_size <= 0 || head_size % align_elems != 0)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "headSize must be a positive 64-byte multiple");
+  if (query_in->shape[1] % head_size != 0 || key_in->shape[1] % head_size != 0)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "q/k widths are not multiples of headSize");
+  if (rd > head_size || rd % align_elems != 0)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "rotaryDim must be a 64-byte multiple <= headSize");
+
+  if (!valid_rank(positions)) return reject(err, ROPE_ERR_PARAM_INVALID, "bad positions shape");
+  if (!mrope) {
+    if (positions->ndim != 1 || positions->shape[0] != T)
+      return reject(err, ROPE_ERR_PARAM_INVALID, "rope mode: positions must be [numTokens]");
+  } else if (positions->ndim != 2 || positions->shape[0] != nsec || positions->shape[1] != T) {
+    return reject(err, ROPE_ERR_PARAM_INVALID, "mrope mode: positions must be [m, numTokens]");
+  }
+
+  for (const rope_tensor *t : {query_in, key_in, cache})
+    if (t->stride[1] != 1 || t->stride[0] < 0)
+      return reject(err, ROPE_ERR_PARAM_INVALID, "inputs need unit inner and non-negative row stride");
+  for (int d = 0; d < positions->ndim; ++d)
+    if (positions->stride[d] < 0)
+      return reject(err, ROPE_ERR_PARAM_INVALID, "negative positions stride");
+  if (!row_major(query_out) || !row_major(key_out))
+    return reject(err, ROPE_ERR_PARAM_INVALID, "queryOut/keyOut must be contiguous");
+
+  if (overlap(query_out, key_out))
+    return reject(err, ROPE_ERR_PARAM_INVALID, "queryOut and keyOut overlap");
+  const rope_tensor *inputs[4] = {positions, query_in, key_in, cache};
+  const rope_tensor *outputs[2] = {query_out, key_out};
+  for (int o = 0; o < 2; ++o)
+    for (int i = 0; i < 4; ++i) {
+      if (!overlap(outputs[o], inputs[i])) continue;
+      const bool own_input = (o == 0 && i == 1) || (o == 1 && i == 2);
+      if (own_input && identical_view(outputs[o], inputs[i])) continue;
+      return reject(err, ROPE_ERR_PARAM_INVALID, "an output overlaps another tensor");
+    }
+
+  CachePlan &p = *plan;
+  p.dt = dt;
+  p.neox = is_neox_style != 0;
+  p.mrope = mrope;
+  p.positions = static_cast<const int64_t *>(positions->data);
+  p.q_in = query_in->data;
+  p.k_in = key_in->data;
+  p.cache = cache->data;
+  p.q_out = query_out->data;
+  p.k_out = key_out->data;
+  p.T = T;
+  p.H = head_size;
+  p.rd = rd;
+  p.nq = query_in->shape[1] / head_size;
+  p.nk = key_in->shape[1] / head_size;
+  p.max_seq = cache->shape[0];
+  p.q_stride = query_in->stride[0];
+  p.k_stride = key_in->stride[0];
+  p.cache_stride = cache->stride[0];
+  if (mrope) {
+    p.pos_stride_row = positions->stride[0];
+    p.pos_stride_tok = positions->stride[1];
+  } else {
+    p.pos_stride_row = 0;
+    p.pos_stride_tok = positions->stride[0];
+  }
+  p.nsec = nsec;
+  int64_t acc = 0;
+  for (int i = 0; i < nsec; ++i) {
+    acc += sec[i];
+    p.sec_end[i] = int32_t(acc);
+  }
+
+  // 16-byte vectors when every row start and base pointer is 16-byte aligned.
+  const bool ok16 = aligned16(p.q_in) && aligned16(p.k_in) && aligned16(p.q_out) &&
+                    aligned16(p.k_out) && (p.q_stride * es) % 16 == 0 &&
+                    (p.k_stride * es) % 16 == 0;
+  p.vector_io = ok16;
+  p.vec = uint32_t(16 / es);  // headSize and rotaryDim are 64-byte multiples: always divides
+  p.units = uint32_t(head_size / (2 * p.vec));
+  p.rot_units = uint32_t(rd / (2 * p.vec));
+  const int64_t ipt = (p.nq + p.nk) * int64_t(p.units);
+  if (ipt > 0x7fffffffLL)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "too many heads per token for this library");
+  p.items_per_token = uint32_t(ipt);
+  // Tokens per workgroup: fill about one pass (kBlock * kItemsPerLane items); the LDS tile of
+  // cos|sin (tile_tokens * rd floats) stays within 32 KiB.
+  int64_t tt = std::max<int64_t>(1, int64_t(kBlock) * kItemsPerLane / ipt);
+  tt = std::min<int64_t>(tt, std::max<int64_t>(1, (32 * 1024) / (rd * 4)));
+  tt = std::min<int64_t>(tt, T);
+  if (rd * 4 * tt > 64 * 1024)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "rotaryDim too large for the LDS tile (max 16384)");
+  p.tile_tokens = uint32_t(tt);
+  p.tiles = (T + tt - 1) / tt;
+  p.div_units = make_fastdiv(p.units);
+  p.div_ipt = make_fastdiv(p.items_per_token);
+  return ROPE_OK;
+}
+
+}  // namespace ropeamd

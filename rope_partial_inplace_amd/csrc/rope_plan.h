@@ -1,0 +1,100 @@
+// rope_plan.h -- host-side launch plans shared by the validation code and the HIP launchers
+// of librope_amd.so (library-internal; not part of the C ABI).
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "rope.h"
+
+namespace ropeamd {
+
+// Division of a 32-bit unsigned dividend by a run-time invariant divisor, done as a
+// multiply-high, an add and two shifts (Granlund & Montgomery, "Division by Invariant
+// Integers using Multiplication", PLDI 1994, the round-up method for N = 32).
+//   l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
+//   q = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0) with t = mulhi(m, n).
+struct FastDiv {
+  uint32_t d = 1, m = 1, s1 = 0, s2 = 0;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t l = 0;
+  while (l < 32 && (uint64_t(1) << l) < d) ++l;
+  f.m = uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+  f.s1 = l < 1 ? l : 1;
+  f.s2 = l > 1 ? l - 1 : 0;
+  return f;
+}
+
+// Host evaluation of the same formula (used by the CPU tests of the plan logic).
+inline uint32_t fastdiv_host(const FastDiv &f, uint32_t n) {
+  uint32_t t = uint32_t((uint64_t(f.m) * n) >> 32);
+  return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
+// ---- in-place partial interleave ----------------------------------------------------------
+// The slice of every row (b, s, n) is cut into `chunks_per_row` chunks of `vec` elements;
+// one GPU lane owns one chunk (all pairs of a chunk are lane-local because vec is even and
+// chunks start at even offsets from the slice start).
+struct InplacePlan {
+  rope_dtype xdt = ROPE_F32, cdt = ROPE_F32;
+  bool vector_io = false;  // 16-byte x accesses (else one element at a time)
+  bool noop = false;       // nothing to launch
+  void *x = nullptr;
+  const void *cos = nullptr, *sin = nullptr;
+  int64_t B = 0, S = 0, N = 0, D = 0, start = 0, L = 0;
+  int64_t rows = 0;             // B*S*N
+  int64_t items = 0;            // rows * chunks_per_row
+  uint32_t vec = 2;             // elements per lane chunk
+  uint32_t chunks_per_row = 0;  // L / vec
+  // cos/sin row of x-row (b, s, n) = b*cb + s*cs + n*cn (in rows of L elements)
+  int64_t cb = 0, cs = 0, cn = 0;
+  bool idx32 = true;  // rows and items fit in 32 bits: use FastDiv below
+  FastDiv div_cpr, div_n, div_s;
+};
+
+// ---- cos/sin cache --------------------------------------------------------------------------
+// A workgroup owns a tile of `tile_tokens` tokens.  It first stages the tile's cos|sin rows
+// (gathered, mrope-stitched, raised to float32) in LDS, then its lanes walk the tile's
+// (token, head, unit) items; a unit is two vectors of `vec` elements of one head: either a
+// rotated unit (vector u and vector u + rd/(2 vec) of the rotated part) or a pass-through unit.
+struct CachePlan {
+  rope_dtype dt = ROPE_F32;
+  bool neox = true;
+  bool mrope = false;
+  bool vector_io = false;
+  const int64_t *positions = nullptr;
+  const void *q_in = nullptr, *k_in = nullptr, *cache = nullptr;
+  void *q_out = nullptr, *k_out = nullptr;
+  int64_t T = 0, nq = 0, nk = 0, H = 0, rd = 0, max_seq = 0;
+  int64_t q_stride = 0, k_stride = 0, cache_stride = 0;  // row strides in elements
+  int64_t pos_stride_row = 0, pos_stride_tok = 0;        // positions[k, t] strides
+  int32_t sec_end[4] = {0, 0, 0, 0};  // cumulative mrope section ends (in cos/sin index)
+  int32_t nsec = 0;
+  uint32_t vec = 1;          // elements per vector
+  uint32_t units = 0;        // units per head (H / (2 vec))
+  uint32_t rot_units = 0;    // rotated units per head (rd / (2 vec))
+  uint32_t items_per_token = 0;
+  uint32_t tile_tokens = 1;
+  int64_t tiles = 0;
+  FastDiv div_units, div_ipt;
+};
+
+int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor *sin,
+                 int64_t rotary_mode, const int64_t *partial_slice, int64_t partial_slice_len,
+                 InplacePlan *plan, std::string *err);
+
+int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
+               const rope_tensor *key_in, const rope_tensor *cos_sin_cache,
+               const int64_t *mrope_section, int64_t mrope_section_len, int64_t head_size,
+               int is_neox_style, const rope_tensor *query_out, const rope_tensor *key_out,
+               CachePlan *plan, std::string *err);
+
+// Items (lanes' work units) a workgroup processes per pass; the kernels use this too.
+constexpr int kBlock = 256;
+constexpr int kItemsPerLane = 4;
+
+}  // namespace ropeamd

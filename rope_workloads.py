@@ -24,8 +24,15 @@ THETA = 10000.0
 DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
+def generator(seed: int, device="cpu") -> torch.Generator:
+    """Seeded generator on the device the inputs are drawn on (large inputs are drawn
+    directly in GPU memory; host copies of the very same bytes feed the oracle)."""
+    return torch.Generator(device=torch.device(device)).manual_seed(seed)
+
+
 def randn(shape, dtype, gen):
-    return torch.randn(tuple(shape), generator=gen, dtype=torch.float32).to(dtype)
+    return torch.randn(tuple(shape), generator=gen, dtype=torch.float32,
+                       device=gen.device).to(dtype)
 
 
 def angles(pos: np.ndarray, n_freq: int, dim: int) -> np.ndarray:
@@ -66,13 +73,13 @@ class InplaceCase:
 
 
 def inplace_case(name, B, S, N, D, xdtype, cdtype, partial_slice, cos_shape=None, seed=0,
-                 table="angles"):
+                 table="angles", device="cpu"):
     """x ~ N(0,1) of shape [B,S,N,D]; cos/sin of `cos_shape` (default BS1D) over the slice.
 
     table="angles": cos/sin from angle s * theta^(-2i/L) repeated per pair (s = sequence
     index of the row); table="randn": independent N(0,1) values (per-element cos/sin).
     """
-    g = torch.Generator().manual_seed(seed)
+    g = generator(seed, device)
     x = randn((B, S, N, D), xdtype, g)
     start, end = (0, D) if partial_slice is None else partial_slice
     L = end - start
@@ -80,8 +87,8 @@ def inplace_case(name, B, S, N, D, xdtype, cdtype, partial_slice, cos_shape=None
     if table == "angles":
         pos = np.arange(cshape[1]) if cshape[1] > 1 else np.zeros(1)
         c, s = pairwise_tables(pos, L, cdtype)          # [Sc, L]
-        c = c.reshape(1, cshape[1], 1, L).expand(cshape).contiguous()
-        s = s.reshape(1, cshape[1], 1, L).expand(cshape).contiguous()
+        c = c.reshape(1, cshape[1], 1, L).expand(cshape).contiguous().to(device)
+        s = s.reshape(1, cshape[1], 1, L).expand(cshape).contiguous().to(device)
     else:
         c = randn(cshape, cdtype, g)
         s = randn(cshape, cdtype, g)
@@ -93,16 +100,16 @@ def inplace_case(name, B, S, N, D, xdtype, cdtype, partial_slice, cos_shape=None
     return InplaceCase(name, x, c, s, partial_slice, B * S, algo)
 
 
-def config_c1():
+def config_c1(device="cpu"):
     """fp32 x [1,16,2,64], slice [0,64), cos/sin fp32 [1,16,1,64] from angles per pair."""
     return inplace_case("inplace_f32_1x16x2x64", 1, 16, 2, 64, torch.float32, torch.float32,
-                        [0, 64], seed=1001)
+                        [0, 64], seed=1001, device=device)
 
 
-def config_c2():
+def config_c2(device="cpu"):
     """bf16 x [8,4096,1,576], slice [512,576), cos/sin fp32 [8,4096,1,64] (pos = s)."""
     return inplace_case("inplace_bf16x_f32cs_8x4096x1x576_slice512_576", 8, 4096, 1, 576,
-                        torch.bfloat16, torch.float32, [512, 576], seed=1002)
+                        torch.bfloat16, torch.float32, [512, 576], seed=1002, device=device)
 
 
 # ------------------------------------------------------------------------------------------
@@ -129,13 +136,16 @@ def cache_algo_bytes(T, nq, nk, H, rd, es, npos_rows):
 
 
 def cache_case(name, T, nq, nk, H, rd, dtype, is_neox, max_seq, seed, mrope_section=None,
-               positions=None):
-    g = torch.Generator().manual_seed(seed)
+               positions=None, device="cpu"):
+    g = generator(seed, device)
     q = randn((T, nq * H), dtype, g)
     k = randn((T, nk * H), dtype, g)
-    cache = cos_sin_cache(max_seq, rd, dtype)
+    cache = cos_sin_cache(max_seq, rd, dtype).to(device)
     if positions is None:
-        positions = torch.randint(0, max_seq, (T,), generator=g, dtype=torch.int64)
+        positions = torch.randint(0, max_seq, (T,), generator=g, dtype=torch.int64,
+                                  device=g.device)
+    else:
+        positions = positions.to(device)
     nrows = 1 if positions.dim() == 1 else positions.shape[0]
     es = q.element_size()
     return CacheCase(name, positions, q, k, cache, mrope_section, H, is_neox, T,
@@ -157,24 +167,24 @@ def mrope_positions(T_text: int, frames: int, grid_h: int, grid_w: int, m: int =
     return torch.stack(rows).contiguous()
 
 
-def config_c3():
+def config_c3(device="cpu"):
     """rope NeoX bf16: T=8192, q [8192, 32*128], k [8192, 8*128], cache [32768, 128]."""
     return cache_case("cache_rope_neox_bf16_T8192_q32_k8_H128", 8192, 32, 8, 128, 128,
-                      torch.bfloat16, True, 32768, seed=1003)
+                      torch.bfloat16, True, 32768, seed=1003, device=device)
 
 
-def config_c4():
+def config_c4(device="cpu"):
     """rope GPT-J fp16 partial: T=32768, q/k [T, 32*128], rd 64, cache [65536, 64]."""
     return cache_case("cache_rope_gptj_f16_T32768_q32_k32_H128_rd64", 32768, 32, 32, 128, 64,
-                      torch.float16, False, 65536, seed=1004)
+                      torch.float16, False, 65536, seed=1004, device=device)
 
 
-def config_c5():
+def config_c5(device="cpu"):
     """mrope [16,24,24] NeoX bf16: T=16384, q [T, 28*128], k [T, 4*128], cache [32768, 128]."""
     pos = mrope_positions(8192, 2, 64, 64)
     return cache_case("cache_mrope_16_24_24_neox_bf16_T16384_q28_k4_H128", 16384, 28, 4, 128,
                       128, torch.bfloat16, True, 32768, seed=1005, mrope_section=[16, 24, 24],
-                      positions=pos)
+                      positions=pos, device=device)
 
 
 CONFIGS = {"c1": config_c1, "c2": config_c2, "c3": config_c3, "c4": config_c4,

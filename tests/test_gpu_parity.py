@@ -1,0 +1,357 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Tolerances are in tests/parity.py: bf16/f16 within 1 ulp of the oracle's float32-then-rounded
+value, f32 within 2e-6 of the exact value relative to the magnitude of the products, data
+outside the rotated range bit-exact.  Inputs are seeded and synthetic (rope_workloads.py).
+
+Pages:
+  [IPRM] "CANN ops-transformer 的 aclnnInplacePartialRotaryMul 算子：Inplace 部分旋转位置编码接口详解与实现剖析"
+  [RSCC] "CANN ops-transformer 旋转位置编码算子 RopeWithSinCosCache 深度解析：cache 化 RoPE 的计算原理与 aclnn 两段式调用实战"
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rope_partial_inplace_amd as ra
+import rope_workloads as W
+from parity import (as_f64, bits, cache_scale, check_bits_equal, check_f32, check_half,
+                    gathered_tables, inplace_scale)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+HALF = (torch.float16, torch.bfloat16)
+
+
+# ------------------------------------------------------------------------------------------
+# in-place op
+# ------------------------------------------------------------------------------------------
+
+def check_inplace(x_before, x_after_gpu, cos, sin, sl, what):
+    """x_before: host copy of x before the call; the rest compared to the oracle."""
+    x_cpu = x_before.clone()
+    c_cpu, s_cpu = cos.cpu(), sin.cpu()
+    st, x64 = oracle.rope_partial_inplace(x_cpu, c_cpu, s_cpu, 1, sl, twin=True)
+    assert st == 0, oracle.last_error()
+    D = x_before.shape[-1]
+    start, end = (0, D) if sl is None else sl
+    got = x_after_gpu.cpu()
+    # untouched data: bit-exact
+    check_bits_equal(got[..., :start], x_before[..., :start], what + " [0,start)")
+    check_bits_equal(got[..., end:], x_before[..., end:], what + " [end,D)")
+    if x_before.dtype in HALF:
+        return check_half(got[..., start:end], x_cpu[..., start:end], what)
+    scale = inplace_scale(x_before, c_cpu, s_cpu, start, end)
+    return check_f32(got[..., start:end], x64[..., start:end], scale, what)
+
+
+def run_inplace(case, stream=None):
+    x = case.x.to(DEV)
+    before = x.cpu()
+    ra.rope_partial_inplace(x, case.cos.to(DEV), case.sin.to(DEV), 1, case.partial_slice,
+                            stream=stream)
+    torch.cuda.synchronize()
+    return before, x
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c2"])
+def test_inplace_configs_full(cfg):
+    case = W.CONFIGS[cfg](DEV)
+    before, x = run_inplace(case)
+    check_inplace(before, x, case.cos, case.sin, case.partial_slice, case.name)
+
+
+LAYOUTS = {"BSND": lambda B, S, N: (B, S, N), "BS1D": lambda B, S, N: (B, S, 1),
+           "B1ND": lambda B, S, N: (B, 1, N), "B11D": lambda B, S, N: (B, 1, 1),
+           "111D": lambda B, S, N: (1, 1, 1), "1SND": lambda B, S, N: (1, S, N)}
+DTYPE_PAIRS = [(torch.float32, torch.float32), (torch.float16, torch.float16),
+               (torch.float16, torch.float32), (torch.bfloat16, torch.bfloat16),
+               (torch.bfloat16, torch.float32)]
+
+
+@pytest.mark.parametrize("xdt,cdt", DTYPE_PAIRS, ids=lambda d: str(d).split(".")[-1])
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+@pytest.mark.parametrize("shape,sl", [((3, 37, 5, 96), [16, 80]),    # ragged rows, inner slice
+                                      ((2, 65, 3, 64), None),        # whole D
+                                      ((1, 300, 2, 40), [1, 37]),    # odd start: element path
+                                      ((4, 7, 1, 1024), [0, 1024]),  # D at its maximum
+                                      ((2, 3, 2, 10), [4, 6])])      # one pair per row
+def test_inplace_sweep(xdt, cdt, layout, shape, sl):
+    B, S, N, D = shape
+    start, end = (0, D) if sl is None else sl
+    L = end - start
+    cshape = LAYOUTS[layout](B, S, N) + (L,)
+    case = W.inplace_case("sweep", B, S, N, D, xdt, cdt, sl, cos_shape=cshape, seed=B * 7 + S,
+                          table="randn", device=DEV)
+    before, x = run_inplace(case)
+    check_inplace(before, x, case.cos, case.sin, sl, f"{layout} {shape} {sl} {xdt}/{cdt}")
+
+
+def test_inplace_misaligned_base_uses_element_path():
+    """x starts 2 bytes past a 16-byte boundary: the library must take its element-wise path
+    and still match."""
+    B, S, N, D = 2, 33, 3, 64
+    buf = torch.randn(B * S * N * D + 8, device=DEV).to(torch.bfloat16)
+    x = buf[1:1 + B * S * N * D].view(B, S, N, D)
+    c = torch.randn(B, S, 1, 32, device=DEV)
+    s = torch.randn(B, S, 1, 32, device=DEV)
+    before = x.cpu()
+    ra.rope_partial_inplace(x, c, s, 1, [16, 48])
+    torch.cuda.synchronize()
+    check_inplace(before, x, c, s, [16, 48], "misaligned bf16")
+
+
+def test_inplace_noop_and_empty_leave_x_untouched():
+    x = torch.randn(2, 8, 2, 32, device=DEV).to(torch.float16)
+    ref = x.clone()
+    c = torch.randn(2, 8, 1, 5, device=DEV).to(torch.float16)  # last dim irrelevant for a no-op
+    ra.rope_partial_inplace(x, c, c, 1, [10, 10])
+    e = torch.empty(0, 8, 2, 32, device=DEV, dtype=torch.float16)
+    ra.rope_partial_inplace(e, torch.randn(1, 8, 1, 32, device=DEV).half(),
+                            torch.randn(1, 8, 1, 32, device=DEV).half(), 1, None)
+    torch.cuda.synchronize()
+    check_bits_equal(x, ref, "no-op")
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.float16, torch.bfloat16])
+def test_inplace_canaries_and_specials(dt):
+    """Signalling-NaN canaries outside the slice stay bit-identical; NaN/Inf inside the slice
+    propagate as the oracle says."""
+    B, S, N, D = 2, 50, 2, 48
+    g = W.generator(3, DEV)
+    x = W.randn((B, S, N, D), dt, g)
+    raw = x.view(torch.int32 if dt == torch.float32 else torch.int16)
+    snan = 0x7F800001 if dt == torch.float32 else (0x7C01 if dt == torch.float16 else 0x7F81)
+    raw[..., :8] = snan
+    raw[..., 40:] = -1
+    flat = x.view(-1)
+    flat[8 * 3 + 11] = float("nan")
+    flat[D * 5 + 9] = float("inf")
+    flat[D * 9 + 20] = float("-inf")
+    c = W.randn((B, S, 1, 32), dt, g)
+    s = W.randn((B, S, 1, 32), dt, g)
+    c.view(-1)[17] = float("inf")
+    before = x.cpu()
+    ra.rope_partial_inplace(x, c, s, 1, [8, 40])
+    torch.cuda.synchronize()
+    check_inplace(before, x, c, s, [8, 40], f"specials {dt}")
+
+
+def test_inplace_deterministic_and_stream():
+    case = W.config_c2(DEV)
+    x1 = case.x.clone()
+    x2 = case.x.clone()
+    side = torch.cuda.Stream()
+    ra.rope_partial_inplace(x1, case.cos, case.sin, 1, case.partial_slice)
+    torch.cuda.current_stream().synchronize()
+    with torch.cuda.stream(side):
+        ra.rope_partial_inplace(x2, case.cos, case.sin, 1, case.partial_slice, stream=side)
+    side.synchronize()
+    check_bits_equal(x1, x2, "two runs / two streams")
+
+
+# ------------------------------------------------------------------------------------------
+# cache op
+# ------------------------------------------------------------------------------------------
+
+def oracle_cache(pos, q, k, cache, msec, H, neox):
+    qo = torch.empty(q.shape, dtype=q.dtype)
+    ko = torch.empty(k.shape, dtype=k.dtype)
+    st, q64, k64 = oracle.rope_with_cos_sin_cache(pos, q, k, cache, msec, H, neox, qo, ko,
+                                                  twin=True)
+    assert st == 0, oracle.last_error()
+    return qo, ko, q64, k64
+
+
+def compare_cache(pos, q_in, k_in, cache, msec, H, neox, q_gpu, k_gpu, what):
+    """All arguments on the host; q_gpu/k_gpu are host copies of the GPU outputs."""
+    rd = cache.shape[1]
+    qo, ko, q64, k64 = oracle_cache(pos, q_in, k_in, cache, msec, H, neox)
+    cos_t, sin_t = gathered_tables(cache, pos, msec)
+    exact = 0
+    for name, inp, got, ref, ref64 in (("q", q_in, q_gpu, qo, q64), ("k", k_in, k_gpu, ko, k64)):
+        T = inp.shape[0]
+        g3, r3, i3 = (got.reshape(T, -1, H), ref.reshape(T, -1, H),
+                      inp.contiguous().reshape(T, -1, H))
+        check_bits_equal(g3[..., rd:], i3[..., rd:], f"{what} {name} pass-through")
+        if got.dtype in HALF:
+            exact += check_half(g3[..., :rd], r3[..., :rd], f"{what} {name}")
+        else:
+            sc = cache_scale(inp.contiguous(), cos_t, sin_t, H, rd, neox).reshape(T, -1, H)
+            exact += check_f32(g3[..., :rd], ref64.reshape(T, -1, H)[..., :rd], sc[..., :rd],
+                               f"{what} {name}")
+    return exact
+
+
+def run_cache_case(case, **kw):
+    qo, ko = ra.rope_with_cos_sin_cache(case.positions, case.query, case.key, case.cache,
+                                        case.mrope_section, case.head_size, case.is_neox, **kw)
+    torch.cuda.synchronize()
+    return qo, ko
+
+
+@pytest.mark.parametrize("cfg", ["c3", "c5"])
+def test_cache_configs_full(cfg):
+    case = W.CONFIGS[cfg](DEV)
+    qo, ko = run_cache_case(case)
+    compare_cache(case.positions.cpu(), case.query.cpu(), case.key.cpu(), case.cache.cpu(),
+                  case.mrope_section, case.head_size, case.is_neox, qo.cpu(), ko.cpu(),
+                  case.name)
+
+
+def test_cache_config_c4_sampled_tokens():
+    """The 1 GiB GPT-J workload: every token's pass-through half is checked on the GPU; the
+    rotated half is compared with the oracle on 4096 seeded sample tokens."""
+    case = W.config_c4(DEV)
+    qo, ko = run_cache_case(case)
+    rd, H = case.cache.shape[1], case.head_size
+    T = case.tokens
+    for got, inp in ((qo, case.query), (ko, case.key)):
+        assert torch.equal(got.view(T, -1, H)[..., rd:].view(torch.int16),
+                           inp.view(T, -1, H)[..., rd:].view(torch.int16))
+    idx = torch.randperm(T, generator=torch.Generator().manual_seed(44))[:4096].sort().values
+    gi = idx.to(DEV)
+    compare_cache(case.positions[gi].cpu(), case.query[gi].cpu(), case.key[gi].cpu(),
+                  case.cache.cpu(), None, H, False, qo[gi].cpu(), ko[gi].cpu(), case.name)
+
+
+HEADS = [(torch.bfloat16, 32, 32), (torch.bfloat16, 64, 32), (torch.bfloat16, 96, 96),
+         (torch.bfloat16, 128, 64), (torch.bfloat16, 128, 96), (torch.float16, 64, 64),
+         (torch.float16, 96, 32), (torch.float16, 128, 128), (torch.float32, 16, 16),
+         (torch.float32, 48, 32), (torch.float32, 128, 64), (torch.float32, 96, 96)]
+
+
+@pytest.mark.parametrize("neox", [True, False], ids=["neox", "gptj"])
+@pytest.mark.parametrize("dt,H,rd", HEADS, ids=lambda v: str(v).split(".")[-1])
+@pytest.mark.parametrize("T,nq,nk", [(1, 1, 1), (3, 2, 1), (127, 5, 3), (4097, 4, 2)])
+def test_cache_sweep(dt, H, rd, neox, T, nq, nk):
+    case = W.cache_case("sweep", T, nq, nk, H, rd, dt, neox, 500, seed=T + H + rd, device=DEV)
+    qo, ko = run_cache_case(case)
+    compare_cache(case.positions.cpu(), case.query.cpu(), case.key.cpu(), case.cache.cpu(),
+                  None, H, neox, qo.cpu(), ko.cpu(), f"T{T} {dt} H{H} rd{rd} neox={neox}")
+
+
+@pytest.mark.parametrize("neox", [True, False], ids=["neox", "gptj"])
+@pytest.mark.parametrize("sec", [[16, 24, 24], [8, 12, 12], [24, 20, 20], [11, 11, 10],
+                                 [16, 16, 16, 16]])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16, torch.float32])
+def test_cache_mrope(sec, neox, dt):
+    rd = 2 * sum(sec)
+    H = 128 if rd <= 128 else 256
+    if dt == torch.float32 and rd % 16:
+        pytest.skip("rotaryDim must be a 64-byte multiple")
+    pos = W.mrope_positions(300, 2, 16, 16, m=len(sec))
+    T = pos.shape[1]
+    case = W.cache_case("mrope", T, 6, 2, H, rd, dt, neox, 400, seed=rd, mrope_section=sec,
+                        positions=pos, device=DEV)
+    qo, ko = run_cache_case(case)
+    compare_cache(case.positions.cpu(), case.query.cpu(), case.key.cpu(), case.cache.cpu(),
+                  sec, H, neox, qo.cpu(), ko.cpu(), f"mrope {sec} {dt} neox={neox}")
+
+
+def test_cache_strided_inputs_and_positions():
+    """Row strides larger than the row (qStride/kStride), a row-strided cache, strided
+    positions; outputs contiguous."""
+    T, H, rd = 257, 128, 64
+    g = W.generator(5, DEV)
+    qbig = W.randn((T, 3 * H + 64), torch.bfloat16, g)
+    kbig = W.randn((T, 2 * H + 32), torch.bfloat16, g)
+    q = qbig[:, 32:32 + 3 * H]
+    k = kbig[:, :H]
+    cbig = W.cos_sin_cache(100, 128, torch.bfloat16).to(DEV)
+    cache = cbig[:, :rd]
+    pos_big = torch.randint(0, 100, (2 * T,), generator=g, device=DEV)
+    pos = pos_big[::2]
+    for neox in (True, False):
+        qo, ko = ra.rope_with_cos_sin_cache(pos, q, k, cache, None, H, neox)
+        torch.cuda.synchronize()
+        compare_cache(pos.cpu(), q.cpu(), k.cpu(), cache.cpu(), None, H, neox, qo.cpu(), ko.cpu(),
+                      f"strided neox={neox}")
+
+
+def test_cache_misaligned_rows_use_element_path():
+    T, H = 33, 64
+    g = W.generator(6, DEV)
+    buf = W.randn((T * (2 * H + 1) + 8,), torch.float16, g)
+    q = buf[1:1 + T * (2 * H + 1)].view(T, 2 * H + 1)[:, :2 * H]   # row stride 129 elements
+    k = W.randn((T, H), torch.float16, g)
+    cache = W.cos_sin_cache(64, 64, torch.float16).to(DEV)
+    pos = torch.randint(0, 64, (T,), generator=g, device=DEV)
+    for neox in (True, False):
+        qo, ko = ra.rope_with_cos_sin_cache(pos, q, k, cache, None, H, neox)
+        torch.cuda.synchronize()
+        compare_cache(pos.cpu(), q.cpu(), k.cpu(), cache.cpu(), None, H, neox, qo.cpu(),
+                      ko.cpu(), f"misaligned neox={neox}")
+
+
+def test_cache_exact_alias_in_place():
+    case = W.cache_case("alias", 1000, 8, 2, 128, 64, torch.bfloat16, True, 2048, seed=8,
+                        device=DEV)
+    q_in, k_in = case.query.cpu(), case.key.cpu()
+    q, k = case.query, case.key
+    ra.rope_with_cos_sin_cache(case.positions, q, k, case.cache, None, 128, True,
+                               query_out=q, key_out=k)
+    torch.cuda.synchronize()
+    compare_cache(case.positions.cpu(), q_in, k_in, case.cache.cpu(), None, 128, True, q.cpu(),
+                  k.cpu(), "aliased")
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.float16, torch.bfloat16])
+def test_cache_specials(dt):
+    case = W.cache_case("specials", 64, 3, 1, 64, 32, dt, True, 128, seed=9, device=DEV)
+    q = case.query.view(-1)
+    q[5] = float("nan")
+    q[64 * 3 + 40] = float("inf")      # a pass-through element
+    q[64 * 7 + 17] = float("-inf")
+    case.key.view(-1)[3] = float("nan")
+    case.cache[case.positions[2], 4] = float("inf")
+    qo, ko = run_cache_case(case)
+    compare_cache(case.positions.cpu(), case.query.cpu(), case.key.cpu(), case.cache.cpu(),
+                  None, 64, True, qo.cpu(), ko.cpu(), f"specials {dt}")
+
+
+def test_cache_positions_out_of_range_are_clamped():
+    """Outside the contract ([RSCC §约束说明]: positions < maxSeqLen).  The library documents a
+    clamp into [0, maxSeqLen); the call must complete and match the clamped positions."""
+    case = W.cache_case("oob", 50, 2, 1, 64, 64, torch.bfloat16, True, 32, seed=10, device=DEV)
+    pos = case.positions.clone()
+    pos[3] = 1 << 40
+    pos[7] = -5
+    qo, ko = ra.rope_with_cos_sin_cache(pos, case.query, case.key, case.cache, None, 64, True)
+    torch.cuda.synchronize()
+    clamped = pos.clamp(0, 31).cpu()
+    compare_cache(clamped, case.query.cpu(), case.key.cpu(), case.cache.cpu(), None, 64, True,
+                  qo.cpu(), ko.cpu(), "clamped")
+
+
+def test_cache_max_tokens_and_large_rotary_dim():
+    case = W.cache_case("maxT", 131073, 1, 1, 32, 32, torch.bfloat16, False, 1000, seed=11,
+                        device=DEV)
+    qo, ko = run_cache_case(case)
+    compare_cache(case.positions.cpu(), case.query.cpu(), case.key.cpu(), case.cache.cpu(),
+                  None, 32, False, qo.cpu(), ko.cpu(), "T=131073")
+    big = W.cache_case("bigrd", 40, 2, 1, 4096, 2048, torch.float16, True, 64, seed=12,
+                       device=DEV)
+    qo, ko = run_cache_case(big)
+    compare_cache(big.positions.cpu(), big.query.cpu(), big.key.cpu(), big.cache.cpu(), None,
+                  4096, True, qo.cpu(), ko.cpu(), "rd=2048")
+
+
+def test_cache_deterministic():
+    case = W.config_c5(DEV)
+    a = run_cache_case(case)
+    b = run_cache_case(case)
+    check_bits_equal(a[0], b[0], "q twice")
+    check_bits_equal(a[1], b[1], "k twice")
+
+
+def test_binding_errors_touch_nothing():
+    case = W.cache_case("err", 16, 2, 1, 64, 32, torch.bfloat16, True, 64, seed=13, device=DEV)
+    qo = torch.zeros_like(case.query)
+    ko = torch.zeros_like(case.key)
+    with pytest.raises(ra.RopeError) as e:
+        ra.rope_with_cos_sin_cache(case.positions, case.query, case.key, case.cache, [16, 24, 24],
+                                   64, True, query_out=qo, key_out=ko)
+    assert e.value.code == ra.ROPE_ERR_PARAM_INVALID
+    torch.cuda.synchronize()
+    assert not qo.any() and not ko.any()

@@ -1,0 +1,21 @@
+"""CPU tests of the library's host-side index arithmetic (no GPU).
+
+The kernels decode flat work-item indices with a multiply-high division by run-time
+invariant divisors (rope_plan.h).  A wrong quotient would address memory outside a tensor,
+so the formula is checked here, compiled from the library's own header, against `/`.
+"""
+import os
+import subprocess
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_fastdiv_matches_integer_division(tmp_path):
+    exe = tmp_path / "fastdiv_check"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+                    "-I", os.path.join(ROOT, "rope_partial_inplace_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "fastdiv_check.cpp"), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert out.stdout.startswith("ok")
