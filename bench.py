@@ -197,7 +197,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workloads", default="c2,c1,c3,c4,c5",
+    ap.add_argument("--workloads", default=",".join(
+                        ["inplace_bf16_8x4096x1x576_s512", "inplace_f32_1x16x2x64",
+                         "cache_rope_neox_bf16_t8192", "cache_rope_gptj_f16_t32768_rd64",
+                         "cache_mrope_neox_bf16_t16384"]),
                     help="first is the headline; the rest are reported under `kernels`")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
@@ -228,7 +231,7 @@ def main() -> int:
     for wi, name in enumerate(names):
         case = W.CONFIGS[name](dev)
         cases[name] = case
-        n_sets = 1 if name == "c1" else n_sets_for(case.algo_bytes)
+        n_sets = 1 if name == "inplace_f32_1x16x2x64" else n_sets_for(case.algo_bytes)
         calls = (inplace_calls(ra, case, n_sets) if hasattr(case, "x")
                  else cache_calls(ra, torch, case, n_sets))
         steps = args.steps if wi == 0 else max(20, min(args.steps, 100))
@@ -270,8 +273,7 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) activations, RoPE angle tables theta=10000)",
         "config": {"workload": hr["workload"], "tokens": cases[head].tokens,
                    "algo_bytes_per_step": hr["algo_bytes_per_launch"],
-                   "buffer_sets": hr["buffer_sets"], "storage_dtypes": "x bf16, cos/sin f32"
-                   if head == "c2" else "see workload"},
+                   "buffer_sets": hr["buffer_sets"], "name": head},
         "tokens_per_s": hr["tokens_per_s"],
         "roofline": {"bound": "hbm", "achieved": hr["gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": hr["frac_of_hbm_peak"],

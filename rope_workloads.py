@@ -100,13 +100,13 @@ def inplace_case(name, B, S, N, D, xdtype, cdtype, partial_slice, cos_shape=None
     return InplaceCase(name, x, c, s, partial_slice, B * S, algo)
 
 
-def config_c1(device="cpu"):
+def inplace_f32_small(device="cpu"):
     """fp32 x [1,16,2,64], slice [0,64), cos/sin fp32 [1,16,1,64] from angles per pair."""
     return inplace_case("inplace_f32_1x16x2x64", 1, 16, 2, 64, torch.float32, torch.float32,
                         [0, 64], seed=1001, device=device)
 
 
-def config_c2(device="cpu"):
+def inplace_bf16_slice(device="cpu"):
     """bf16 x [8,4096,1,576], slice [512,576), cos/sin fp32 [8,4096,1,64] (pos = s)."""
     return inplace_case("inplace_bf16x_f32cs_8x4096x1x576_slice512_576", 8, 4096, 1, 576,
                         torch.bfloat16, torch.float32, [512, 576], seed=1002, device=device)
@@ -167,19 +167,19 @@ def mrope_positions(T_text: int, frames: int, grid_h: int, grid_w: int, m: int =
     return torch.stack(rows).contiguous()
 
 
-def config_c3(device="cpu"):
+def cache_rope_neox(device="cpu"):
     """rope NeoX bf16: T=8192, q [8192, 32*128], k [8192, 8*128], cache [32768, 128]."""
     return cache_case("cache_rope_neox_bf16_T8192_q32_k8_H128", 8192, 32, 8, 128, 128,
                       torch.bfloat16, True, 32768, seed=1003, device=device)
 
 
-def config_c4(device="cpu"):
+def cache_rope_gptj_partial(device="cpu"):
     """rope GPT-J fp16 partial: T=32768, q/k [T, 32*128], rd 64, cache [65536, 64]."""
     return cache_case("cache_rope_gptj_f16_T32768_q32_k32_H128_rd64", 32768, 32, 32, 128, 64,
                       torch.float16, False, 65536, seed=1004, device=device)
 
 
-def config_c5(device="cpu"):
+def cache_mrope(device="cpu"):
     """mrope [16,24,24] NeoX bf16: T=16384, q [T, 28*128], k [T, 4*128], cache [32768, 128]."""
     pos = mrope_positions(8192, 2, 64, 64)
     return cache_case("cache_mrope_16_24_24_neox_bf16_T16384_q28_k4_H128", 16384, 28, 4, 128,
@@ -187,5 +187,12 @@ def config_c5(device="cpu"):
                       positions=pos, device=device)
 
 
-CONFIGS = {"c1": config_c1, "c2": config_c2, "c3": config_c3, "c4": config_c4,
-           "c5": config_c5}
+CONFIGS = {
+    "inplace_f32_1x16x2x64": inplace_f32_small,
+    "inplace_bf16_8x4096x1x576_s512": inplace_bf16_slice,
+    "cache_rope_neox_bf16_t8192": cache_rope_neox,
+    "cache_rope_gptj_f16_t32768_rd64": cache_rope_gptj_partial,
+    "cache_mrope_neox_bf16_t16384": cache_mrope,
+}
+HEADLINE = "inplace_bf16_8x4096x1x576_s512"
+

@@ -54,7 +54,7 @@ def run_inplace(case, stream=None):
     return before, x
 
 
-@pytest.mark.parametrize("cfg", ["c1", "c2"])
+@pytest.mark.parametrize("cfg", ["inplace_f32_1x16x2x64", "inplace_bf16_8x4096x1x576_s512"])
 def test_inplace_configs_full(cfg):
     case = W.CONFIGS[cfg](DEV)
     before, x = run_inplace(case)
@@ -138,7 +138,7 @@ def test_inplace_canaries_and_specials(dt):
 
 
 def test_inplace_deterministic_and_stream():
-    case = W.config_c2(DEV)
+    case = W.inplace_bf16_slice(DEV)
     x1 = case.x.clone()
     x2 = case.x.clone()
     side = torch.cuda.Stream()
@@ -190,7 +190,7 @@ def run_cache_case(case, **kw):
     return qo, ko
 
 
-@pytest.mark.parametrize("cfg", ["c3", "c5"])
+@pytest.mark.parametrize("cfg", ["cache_rope_neox_bf16_t8192", "cache_mrope_neox_bf16_t16384"])
 def test_cache_configs_full(cfg):
     case = W.CONFIGS[cfg](DEV)
     qo, ko = run_cache_case(case)
@@ -202,7 +202,7 @@ def test_cache_configs_full(cfg):
 def test_cache_config_c4_sampled_tokens():
     """The 1 GiB GPT-J workload: every token's pass-through half is checked on the GPU; the
     rotated half is compared with the oracle on 4096 seeded sample tokens."""
-    case = W.config_c4(DEV)
+    case = W.cache_rope_gptj_partial(DEV)
     qo, ko = run_cache_case(case)
     rd, H = case.cache.shape[1], case.head_size
     T = case.tokens
@@ -338,7 +338,7 @@ def test_cache_max_tokens_and_large_rotary_dim():
 
 
 def test_cache_deterministic():
-    case = W.config_c5(DEV)
+    case = W.cache_mrope(DEV)
     a = run_cache_case(case)
     b = run_cache_case(case)
     check_bits_equal(a[0], b[0], "q twice")

@@ -324,7 +324,7 @@ def test_exact_angles(dt, cv, sv, kind):
 
 
 def test_norm_preserved_per_pair():
-    c2 = W.config_c2()
+    c2 = W.inplace_bf16_slice()
     x = c2.x[:1, :64]
     y, x64 = run_inplace(x, c2.cos[:1, :64], c2.sin[:1, :64], c2.partial_slice, twin=True)
     sl = slice(*c2.partial_slice)
