@@ -40,7 +40,10 @@ struct Io;
 template <>
 struct Io<float> {
   static constexpr int kPer16 = 4;
+  static constexpr int kPerWord = 1;
   using raw = uint32_t;
+  __device__ static void word_to_floats(uint32_t w, float *f) { f[0] = __uint_as_float(w); }
+  __device__ static uint32_t floats_to_word(const float *f) { return __float_as_uint(f[0]); }
   __device__ static void unpack(const uint4 &v, float *f) {
     f[0] = __uint_as_float(v.x);
     f[1] = __uint_as_float(v.y);
@@ -61,7 +64,10 @@ struct Io<float> {
 template <>
 struct Io<__bf16> {
   static constexpr int kPer16 = 8;
+  static constexpr int kPerWord = 2;
   using raw = uint16_t;
+  __device__ static void word_to_floats(uint32_t w, float *f) { unpack_word(w, f); }
+  __device__ static uint32_t floats_to_word(const float *f) { return pack_word(f[0], f[1]); }
   __device__ static void unpack_word(uint32_t w, float *f) {
     f[0] = __uint_as_float(w << 16);
     f[1] = __uint_as_float(w & 0xffff0000u);
@@ -92,7 +98,10 @@ struct Io<__bf16> {
 template <>
 struct Io<_Float16> {
   static constexpr int kPer16 = 8;
+  static constexpr int kPerWord = 2;
   using raw = uint16_t;
+  __device__ static void word_to_floats(uint32_t w, float *f) { unpack_word(w, f); }
+  __device__ static uint32_t floats_to_word(const float *f) { return pack_word(f[0], f[1]); }
   __device__ static void unpack_word(uint32_t w, float *f) {
     f16x2 h = __builtin_bit_cast(f16x2, w);
     f[0] = static_cast<float>(h.x);
@@ -123,26 +132,86 @@ struct Io<_Float16> {
   }
 };
 
+// 16-byte raw vector (a native vector type, accepted by the non-temporal builtins).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load/store; NT marks the access non-temporal (streamed data that is touched once:
+// it is not kept in the caches, which leaves them to data that is reused).
+template <bool NT>
+__device__ inline u32x4 ld16(const void *p) {
+  const u32x4 *q = static_cast<const u32x4 *>(p);
+  if constexpr (NT) return __builtin_nontemporal_load(q);
+  return *q;
+}
+
+template <bool NT>
+__device__ inline void st16(void *p, u32x4 v) {
+  u32x4 *q = static_cast<u32x4 *>(p);
+  if constexpr (NT) __builtin_nontemporal_store(v, q);
+  else *q = v;
+}
+
+__device__ inline uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
+__device__ inline u32x4 from_uint4(uint4 v) { return u32x4{v.x, v.y, v.z, v.w}; }
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <bool NT>
+__device__ inline u32x2 ld8(const void *p) {
+  const u32x2 *q = static_cast<const u32x2 *>(p);
+  if constexpr (NT) return __builtin_nontemporal_load(q);
+  return *q;
+}
+
+template <bool NT>
+__device__ inline void st8(void *p, u32x2 v) {
+  u32x2 *q = static_cast<u32x2 *>(p);
+  if constexpr (NT) __builtin_nontemporal_store(v, q);
+  else *q = v;
+}
+
 // N consecutive elements starting at element `i` of `p`, as float32.  VEC: the address is
-// 16-byte aligned and N * sizeof(T) is a multiple of 16, so whole 16-byte loads are used.
-template <typename T, int N, bool VEC>
+// aligned to the access size and N * sizeof(T) is 8 bytes or a multiple of 16, so whole
+// 8- or 16-byte loads are used; otherwise one element at a time.
+template <typename T, int N, bool VEC, bool NT>
 __device__ inline void load_n(const void *p, int64_t i, float *f) {
-  if constexpr (VEC) {
-    const uint4 *q = reinterpret_cast<const uint4 *>(static_cast<const T *>(p) + i);
+  constexpr int kBytes = N * int(sizeof(T));
+  constexpr int kPW = Io<T>::kPerWord;
+  if constexpr (VEC && kBytes % 16 == 0) {
+    const char *q = reinterpret_cast<const char *>(static_cast<const T *>(p) + i);
 #pragma unroll
-    for (int c = 0; c < N / Io<T>::kPer16; ++c) Io<T>::unpack(q[c], f + c * Io<T>::kPer16);
+    for (int c = 0; c < kBytes / 16; ++c) {
+      const u32x4 v = ld16<NT>(q + 16 * c);
+      Io<T>::word_to_floats(v.x, f + (4 * c + 0) * kPW);
+      Io<T>::word_to_floats(v.y, f + (4 * c + 1) * kPW);
+      Io<T>::word_to_floats(v.z, f + (4 * c + 2) * kPW);
+      Io<T>::word_to_floats(v.w, f + (4 * c + 3) * kPW);
+    }
+  } else if constexpr (VEC && kBytes == 8) {
+    const u32x2 v = ld8<NT>(static_cast<const T *>(p) + i);
+    Io<T>::word_to_floats(v.x, f);
+    Io<T>::word_to_floats(v.y, f + kPW);
   } else {
 #pragma unroll
     for (int e = 0; e < N; ++e) f[e] = Io<T>::load1(p, i + e);
   }
 }
 
-template <typename T, int N, bool VEC>
+template <typename T, int N, bool VEC, bool NT>
 __device__ inline void store_n(void *p, int64_t i, const float *f) {
-  if constexpr (VEC) {
-    uint4 *q = reinterpret_cast<uint4 *>(static_cast<T *>(p) + i);
+  constexpr int kBytes = N * int(sizeof(T));
+  constexpr int kPW = Io<T>::kPerWord;
+  if constexpr (VEC && kBytes % 16 == 0) {
+    char *q = reinterpret_cast<char *>(static_cast<T *>(p) + i);
 #pragma unroll
-    for (int c = 0; c < N / Io<T>::kPer16; ++c) q[c] = Io<T>::pack(f + c * Io<T>::kPer16);
+    for (int c = 0; c < kBytes / 16; ++c)
+      st16<NT>(q + 16 * c, u32x4{Io<T>::floats_to_word(f + (4 * c + 0) * kPW),
+                                 Io<T>::floats_to_word(f + (4 * c + 1) * kPW),
+                                 Io<T>::floats_to_word(f + (4 * c + 2) * kPW),
+                                 Io<T>::floats_to_word(f + (4 * c + 3) * kPW)});
+  } else if constexpr (VEC && kBytes == 8) {
+    st8<NT>(static_cast<T *>(p) + i,
+            u32x2{Io<T>::floats_to_word(f), Io<T>::floats_to_word(f + kPW)});
   } else {
 #pragma unroll
     for (int e = 0; e < N; ++e) Io<T>::store1(p, i + e, f[e]);
@@ -152,16 +221,16 @@ __device__ inline void store_n(void *p, int64_t i, const float *f) {
 // Raw copy of N elements (pass-through data is moved as bits, never converted).
 template <typename T, int N, bool VEC>
 struct RawN {
-  uint4 v[VEC ? (N * int(sizeof(T)) + 15) / 16 : 1];
+  u32x4 v[VEC ? (N * int(sizeof(T)) + 15) / 16 : 1];
   typename Io<T>::raw e[VEC ? 1 : N];
 };
 
-template <typename T, int N, bool VEC>
+template <typename T, int N, bool VEC, bool NT>
 __device__ inline void load_raw(const void *p, int64_t i, RawN<T, N, VEC> &r) {
   if constexpr (VEC) {
-    const uint4 *q = reinterpret_cast<const uint4 *>(static_cast<const T *>(p) + i);
+    const char *q = reinterpret_cast<const char *>(static_cast<const T *>(p) + i);
 #pragma unroll
-    for (int c = 0; c < (N * int(sizeof(T))) / 16; ++c) r.v[c] = q[c];
+    for (int c = 0; c < (N * int(sizeof(T))) / 16; ++c) r.v[c] = ld16<NT>(q + 16 * c);
   } else {
     const typename Io<T>::raw *q = static_cast<const typename Io<T>::raw *>(p) + i;
 #pragma unroll
@@ -169,12 +238,12 @@ __device__ inline void load_raw(const void *p, int64_t i, RawN<T, N, VEC> &r) {
   }
 }
 
-template <typename T, int N, bool VEC>
+template <typename T, int N, bool VEC, bool NT>
 __device__ inline void store_raw(void *p, int64_t i, const RawN<T, N, VEC> &r) {
   if constexpr (VEC) {
-    uint4 *q = reinterpret_cast<uint4 *>(static_cast<T *>(p) + i);
+    char *q = reinterpret_cast<char *>(static_cast<T *>(p) + i);
 #pragma unroll
-    for (int c = 0; c < (N * int(sizeof(T))) / 16; ++c) q[c] = r.v[c];
+    for (int c = 0; c < (N * int(sizeof(T))) / 16; ++c) st16<NT>(q + 16 * c, r.v[c]);
   } else {
     typename Io<T>::raw *q = static_cast<typename Io<T>::raw *>(p) + i;
 #pragma unroll
@@ -186,10 +255,42 @@ template <typename T, int N, bool VEC>
 __device__ inline void raw_to_float(const RawN<T, N, VEC> &r, float *f) {
   if constexpr (VEC) {
 #pragma unroll
-    for (int c = 0; c < (N * int(sizeof(T))) / 16; ++c) Io<T>::unpack(r.v[c], f + c * Io<T>::kPer16);
+    for (int c = 0; c < (N * int(sizeof(T))) / 16; ++c)
+      Io<T>::unpack(to_uint4(r.v[c]), f + c * Io<T>::kPer16);
   } else {
 #pragma unroll
     for (int e = 0; e < N; ++e) f[e] = Io<T>::from_raw(r.e[e]);
+  }
+}
+
+// Word q (kPerWord elements) of a raw vector, as float32; and its inverse (one rounding).
+template <typename T, int N, bool VEC>
+__device__ inline void raw_word_to_float(const RawN<T, N, VEC> &r, int q, float *f) {
+  if constexpr (VEC) {
+    const u32x4 v = r.v[q / 4];
+    const int j = q % 4;
+    Io<T>::word_to_floats(j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w, f);
+  } else {
+#pragma unroll
+    for (int e = 0; e < Io<T>::kPerWord; ++e) f[e] = Io<T>::from_raw(r.e[q * Io<T>::kPerWord + e]);
+  }
+}
+
+template <typename T, int N, bool VEC>
+__device__ inline void float_to_raw_word(const float *f, int q, RawN<T, N, VEC> &r) {
+  if constexpr (VEC) {
+    const uint32_t w = Io<T>::floats_to_word(f);
+    const int j = q % 4;
+    if (j == 0) r.v[q / 4].x = w;
+    else if (j == 1) r.v[q / 4].y = w;
+    else if (j == 2) r.v[q / 4].z = w;
+    else r.v[q / 4].w = w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < Io<T>::kPerWord; ++e) {
+      float one = f[e];
+      Io<T>::store1(&r.e[q * Io<T>::kPerWord + e], 0, one);
+    }
   }
 }
 
@@ -211,12 +312,14 @@ __device__ inline void rotate_pair(float a, float b, float c0, float c1, float s
 // A lane owns K chunks of V slice elements (V/2 pairs); chunks of one row are adjacent lanes,
 // so a wavefront reads and writes whole 16-byte-aligned runs of each row's slice.  Elements
 // outside [start, end) are never touched.  cos/sin rows are addressed with zero strides on
-// broadcast dims (BSND, BS1D, B1ND, B11D, 111D and mixed forms).
+// broadcast dims (BSND, BS1D, B1ND, B11D, 111D and mixed forms).  x is streamed
+// (non-temporal); cos/sin are streamed too unless a row is shared by several x rows
+// (broadcast), where the caches serve the repeats.
 // ============================================================================================
-template <typename XT, typename CT, bool VEC>
+template <typename XT, typename CT, bool VEC, int K, bool CNT>
 __global__ __launch_bounds__(kBlock) void inplace_interleave_kernel(InplacePlan p) {
-  constexpr int V = VEC ? Io<XT>::kPer16 : 2;
-  constexpr int K = kItemsPerLane;
+  // one 16-byte access per lane for the wider of x and cos/sin, 8 bytes for the narrower
+  constexpr int V = VEC ? 16 / (sizeof(XT) > sizeof(CT) ? int(sizeof(XT)) : int(sizeof(CT))) : 2;
   const uint64_t items = uint64_t(p.items);
   const uint64_t per_block = uint64_t(kBlock) * K;
   for (uint64_t base = uint64_t(blockIdx.x) * per_block; base < items;
@@ -250,9 +353,9 @@ __global__ __launch_bounds__(kBlock) void inplace_interleave_kernel(InplacePlan 
       const int64_t crow = int64_t(b) * p.cb + int64_t(s) * p.cs + int64_t(n) * p.cn;
       const int64_t coff = crow * p.L + int64_t(chunk) * V;
       xoff[k] = int64_t(row) * p.D + p.start + int64_t(chunk) * V;
-      load_n<XT, V, VEC>(p.x, xoff[k], xv[k]);
-      load_n<CT, V, VEC>(p.cos, coff, cv[k]);
-      load_n<CT, V, VEC>(p.sin, coff, sv[k]);
+      load_n<XT, V, VEC, true>(p.x, xoff[k], xv[k]);
+      load_n<CT, V, VEC, CNT>(p.cos, coff, cv[k]);
+      load_n<CT, V, VEC, CNT>(p.sin, coff, sv[k]);
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -262,7 +365,7 @@ __global__ __launch_bounds__(kBlock) void inplace_interleave_kernel(InplacePlan 
       for (int e = 0; e < V; e += 2)
         rotate_pair(xv[k][e], xv[k][e + 1], cv[k][e], cv[k][e + 1], sv[k][e], sv[k][e + 1], y[e],
                     y[e + 1]);
-      store_n<XT, V, VEC>(p.x, xoff[k], y);
+      store_n<XT, V, VEC, true>(p.x, xoff[k], y);
     }
   }
 }
@@ -272,117 +375,230 @@ __global__ __launch_bounds__(kBlock) void inplace_interleave_kernel(InplacePlan 
 // A workgroup owns a tile of tokens.  Stage: its lanes gather each token's cos|sin row from
 // the cache (mrope: element i from the position row whose section holds i), raise it to
 // float32 and keep it in LDS, so it is read from HBM once per token and reused by every q/k
-// head.  Then lanes walk (token, head, unit) items; a unit is two V-element vectors of one
-// head: rotated units take vector u and vector u + rd/(2V) of the rotated part (NeoX pairs
-// lie across the two halves; GPT-J pairs lie inside each vector), pass units copy the same
-// two-vector shape of [rd, H) as raw bits.  Lanes u = 0..units-1 of one head touch the head
-// as two contiguous runs, so each wavefront load/store covers whole 128-byte lines.
+// head.  Then lanes walk (token, head, unit) items.  NeoX: a unit is two V-element vectors,
+// u and u + rd/(2V) of the rotated part (its pairs lie across the halves), or the same
+// two-vector shape over [rd, H) copied as raw bits.  GPT-J: a unit is one vector (its pairs
+// lie inside it), rotated below rd and copied above.  The units of one head are adjacent
+// lanes, so each wavefront load/store covers whole runs of 128-byte lines.  q/k are
+// streamed (non-temporal loads and stores); the first pass's loads are issued before the LDS
+// staging so that their latency overlaps the position -> cache gather.
 // ============================================================================================
-template <typename T, bool NEOX, bool VEC>
+// mrope: the position row whose section holds element i of cos/sin
+// ([RSCC §mrope 模式：多模态位置编码]).
+__device__ inline int mrope_section_of(const CachePlan &p, int64_t i) {
+  int sec = int(i >= p.sec_end[0]) + int(i >= p.sec_end[1]);
+  if (p.nsec == 4) sec += int(i >= p.sec_end[2]);
+  return sec;
+}
+
+// Positions outside [0, maxSeqLen) break the contract; clamping keeps every read inside the
+// cache.
+__device__ inline int64_t clamp_position(const CachePlan &p, int64_t pos) {
+  return pos < 0 ? 0 : (pos >= p.max_seq ? p.max_seq - 1 : pos);
+}
+
+// N floats from LDS: N a multiple of 4 at a 16-byte aligned address, or N == 2 at an 8-byte
+// aligned address.
+template <int N>
+__device__ inline void lds_read(const float *src, float *dst) {
+  static_assert(N % 4 == 0 || N == 2, "lds_read takes 2 or a multiple of 4 floats");
+  if constexpr (N == 2) {
+    const float2 v = *reinterpret_cast<const float2 *>(src);
+    dst[0] = v.x;
+    dst[1] = v.y;
+  } else {
+    const float4 *q = reinterpret_cast<const float4 *>(src);
+#pragma unroll
+    for (int c = 0; c < N / 4; ++c) {
+      const float4 v = q[c];
+      dst[4 * c] = v.x;
+      dst[4 * c + 1] = v.y;
+      dst[4 * c + 2] = v.z;
+      dst[4 * c + 3] = v.w;
+    }
+  }
+}
+
+// Where one item of a tile lives: token, q or k, head, unit, and the element offsets of its
+// vectors inside the head (off_b is used by NeoX units only).
+struct CacheItem {
+  int64_t in_row, out_row, off_a, off_b;
+  uint32_t tl, u;
+  bool is_q;
+};
+
+template <bool NEOX>
+__device__ inline CacheItem cache_item(const CachePlan &p, int64_t t0, uint32_t it) {
+  CacheItem c;
+  c.tl = fdiv(p.div_ipt, it);
+  const uint32_t r = it - c.tl * p.items_per_token;
+  const uint32_t h = fdiv(p.div_units, r);
+  c.u = r - h * p.units;
+  const int64_t t = t0 + c.tl;
+  c.is_q = h < uint32_t(p.nq);
+  const int64_t hh = c.is_q ? int64_t(h) : int64_t(h) - p.nq;
+  c.in_row = t * (c.is_q ? p.q_stride : p.k_stride) + hh * p.H;
+  c.out_row = t * ((c.is_q ? p.nq : p.nk) * p.H) + hh * p.H;
+  const int64_t V = p.vec;
+  if constexpr (NEOX) {
+    if (c.u < p.rot_units) {
+      c.off_a = int64_t(c.u) * V;
+      c.off_b = p.rd / 2 + int64_t(c.u) * V;
+    } else {
+      const int64_t v = int64_t(c.u - p.rot_units) * V;
+      c.off_a = p.rd + v;
+      c.off_b = p.rd + (p.H - p.rd) / 2 + v;
+    }
+  } else {
+    c.off_a = int64_t(c.u) * V;
+    c.off_b = 0;
+  }
+  return c;
+}
+
+// A lane's in-flight items: only the raw vectors and the item index are kept across the
+// load -> store distance (addresses are recomputed), which keeps register use low and the
+// number of resident waves high.
+template <typename T, int V, bool VEC, int K, int NV>
+struct CacheItems {
+  RawN<T, V, VEC> v[K][NV];
+  uint32_t it[K];
+};
+
+constexpr uint32_t kNoItem = 0xffffffffu;
+
+template <typename T, bool NEOX, int V, bool VEC, int K, int NV>
+__device__ inline void cache_load_pass(const CachePlan &p, int64_t t0, uint32_t tile_items,
+                                       uint32_t pbase, CacheItems<T, V, VEC, K, NV> &w) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const uint32_t it = pbase + uint32_t(k) * kBlock + threadIdx.x;
+    w.it[k] = it < tile_items ? it : kNoItem;
+    if (it >= tile_items) continue;
+    const CacheItem c = cache_item<NEOX>(p, t0, it);
+    const void *in = c.is_q ? p.q_in : p.k_in;
+    load_raw<T, V, VEC, true>(in, c.in_row + c.off_a, w.v[k][0]);
+    if constexpr (NV == 2) load_raw<T, V, VEC, true>(in, c.in_row + c.off_b, w.v[k][NV - 1]);
+  }
+}
+
+template <typename T, bool NEOX, int V, bool VEC, int K, int NV>
+__device__ inline void cache_store_pass(const CachePlan &p, int64_t t0, const float *cs_tile,
+                                        const CacheItems<T, V, VEC, K, NV> &w) {
+  const int64_t rd = p.rd, half = rd / 2;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (w.it[k] == kNoItem) continue;
+    const CacheItem c = cache_item<NEOX>(p, t0, w.it[k]);
+    void *out = c.is_q ? p.q_out : p.k_out;
+    if (c.u >= p.rot_units) {  // pass-through: raw bits
+      store_raw<T, V, VEC, true>(out, c.out_row + c.off_a, w.v[k][0]);
+      if constexpr (NV == 2) store_raw<T, V, VEC, true>(out, c.out_row + c.off_b, w.v[k][NV - 1]);
+      continue;
+    }
+    const float *cs = cs_tile + int64_t(c.tl) * rd;
+    if constexpr (NEOX) {
+      // [RSCC §rotate_half（GPT-NeoX style）旋转模式]: x1 = a (first half), x2 = b.  Worked one
+      // 32-bit word (1 or 2 elements) of each vector at a time to keep few values live.
+      constexpr int PW = Io<T>::kPerWord;
+      const float *cc = cs + int64_t(c.u) * V;
+      RawN<T, V, VEC> oa, ob;
+#pragma unroll
+      for (int q = 0; q < V / PW; ++q) {
+        float a[PW], b[PW], ya[PW], yb[PW];
+        raw_word_to_float<T, V, VEC>(w.v[k][0], q, a);
+        raw_word_to_float<T, V, VEC>(w.v[k][NV - 1], q, b);
+#pragma unroll
+        for (int e = 0; e < PW; ++e) {
+          const float cv = cc[q * PW + e], sv = cc[half + q * PW + e];
+          ya[e] = a[e] * cv - b[e] * sv;
+          yb[e] = b[e] * cv + a[e] * sv;
+        }
+        float_to_raw_word<T, V, VEC>(ya, q, oa);
+        float_to_raw_word<T, V, VEC>(yb, q, ob);
+      }
+      store_raw<T, V, VEC, true>(out, c.out_row + c.off_a, oa);
+      store_raw<T, V, VEC, true>(out, c.out_row + c.off_b, ob);
+    } else {
+      // [RSCC §rotate_interleaved（GPT-J style）旋转模式]: pairs (x[2m], x[2m+1]) inside the
+      // vector; vector u holds pair indices u*V/2 .. u*V/2 + V/2 - 1
+      float a[V], ya[V], cv[V / 2], sv[V / 2];
+      raw_to_float<T, V, VEC>(w.v[k][0], a);
+      const int64_t ca = int64_t(c.u) * (V / 2);
+      lds_read<V / 2>(cs + ca, cv);
+      lds_read<V / 2>(cs + half + ca, sv);
+#pragma unroll
+      for (int m = 0; m < V / 2; ++m) {
+        ya[2 * m] = a[2 * m] * cv[m] - a[2 * m + 1] * sv[m];
+        ya[2 * m + 1] = a[2 * m + 1] * cv[m] + a[2 * m] * sv[m];
+      }
+      store_n<T, V, VEC, true>(out, c.out_row + c.off_a, ya);
+    }
+  }
+}
+
+template <typename T, bool NEOX, bool VEC, int K>
 __global__ __launch_bounds__(kBlock) void cos_sin_cache_kernel(CachePlan p) {
   extern __shared__ float cs_tile[];  // [tile_tokens][rd]: cos (rd/2) then sin (rd/2)
   constexpr int V = Io<T>::kPer16;
-  constexpr int K = kItemsPerLane;
+  constexpr int NV = NEOX ? 2 : 1;  // vectors per unit
   const int64_t rd = p.rd, half = rd / 2;
-  const int64_t pass_half = (p.H - rd) / 2;
-  const uint32_t ipt = p.items_per_token;
+  const uint32_t pass = uint32_t(kBlock) * K;
   for (int64_t tile = blockIdx.x; tile < p.tiles; tile += gridDim.x) {
     const int64_t t0 = tile * int64_t(p.tile_tokens);
     const int64_t ntok = (p.T - t0) < int64_t(p.tile_tokens) ? (p.T - t0) : int64_t(p.tile_tokens);
-    const uint32_t tile_items = uint32_t(ntok) * ipt;
+    const uint32_t tile_items = uint32_t(ntok) * p.items_per_token;
+
+    CacheItems<T, V, VEC, K, NV> w;
+    cache_load_pass<T, NEOX, V, VEC, K, NV>(p, t0, tile_items, 0, w);
 
     // ---- stage the tile's cos|sin rows in LDS (steps 1-2: gather, split, stitch) ----
-    for (int64_t idx = threadIdx.x; idx < ntok * half; idx += kBlock) {
-      const int64_t tl = idx / half;
-      const int64_t i = idx - tl * half;
-      int sec = 0;
-      if (p.mrope) {
-        sec = int(i >= p.sec_end[0]) + int(i >= p.sec_end[1]);
-        if (p.nsec == 4) sec += int(i >= p.sec_end[2]);
+    // One lane per V-element chunk of a token's cos half (and the matching sin chunk).  A
+    // chunk inside one mrope section (always, in rope mode) comes from one cache row with
+    // 16-byte loads; a chunk split by a section boundary is gathered element by element.
+    const uint32_t stage_items = uint32_t(ntok) * p.stage_chunks;
+    for (uint32_t idx = threadIdx.x; idx < stage_items; idx += kBlock) {
+      const uint32_t tl = fdiv(p.div_stage, idx);
+      const int64_t i0 = int64_t(idx - tl * p.stage_chunks) * V;
+      const int64_t tok = (t0 + tl) * p.pos_stride_tok;
+      const int s_lo = p.mrope ? mrope_section_of(p, i0) : 0;
+      const int s_hi = p.mrope ? mrope_section_of(p, i0 + V - 1) : 0;
+      float *dst = cs_tile + int64_t(tl) * rd + i0;
+      if (s_lo == s_hi) {
+        const int64_t row = clamp_position(p, p.positions[s_lo * p.pos_stride_row + tok]) *
+                            p.cache_stride;
+        float c[V], sn[V];
+        if (p.cache_vec) {
+          load_n<T, V, true, false>(p.cache, row + i0, c);
+          load_n<T, V, true, false>(p.cache, row + half + i0, sn);
+        } else {
+          load_n<T, V, false, false>(p.cache, row + i0, c);
+          load_n<T, V, false, false>(p.cache, row + half + i0, sn);
+        }
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          dst[j] = c[j];
+          dst[half + j] = sn[j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const int sec = mrope_section_of(p, i0 + j);
+          const int64_t row = clamp_position(p, p.positions[sec * p.pos_stride_row + tok]) *
+                              p.cache_stride;
+          dst[j] = Io<T>::load1(p.cache, row + i0 + j);
+          dst[half + j] = Io<T>::load1(p.cache, row + half + i0 + j);
+        }
       }
-      int64_t pos = p.positions[sec * p.pos_stride_row + (t0 + tl) * p.pos_stride_tok];
-      pos = pos < 0 ? 0 : (pos >= p.max_seq ? p.max_seq - 1 : pos);  // never read outside
-      const int64_t row = pos * p.cache_stride;
-      cs_tile[tl * rd + i] = Io<T>::load1(p.cache, row + i);
-      cs_tile[tl * rd + half + i] = Io<T>::load1(p.cache, row + half + i);
     }
     __syncthreads();
 
     // ---- step 3: rotate the first rd of every q head then k head, copy the rest ----
-    for (uint32_t pbase = 0; pbase < tile_items; pbase += uint32_t(kBlock) * K) {
-      RawN<T, V, VEC> va[K], vb[K];
-      int64_t out_row[K], off_a[K], off_b[K];
-      int32_t unit[K], tlk[K];
-      bool isq[K];
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const uint32_t it = pbase + uint32_t(k) * kBlock + threadIdx.x;
-        unit[k] = -1;
-        if (it >= tile_items) continue;
-        const uint32_t tl = fdiv(p.div_ipt, it);
-        const uint32_t r = it - tl * ipt;
-        const uint32_t h = fdiv(p.div_units, r);
-        const uint32_t u = r - h * p.units;
-        const int64_t t = t0 + tl;
-        const bool is_q = h < uint32_t(p.nq);
-        const int64_t hh = is_q ? int64_t(h) : int64_t(h) - p.nq;
-        const void *in = is_q ? p.q_in : p.k_in;
-        const int64_t in_row = t * (is_q ? p.q_stride : p.k_stride) + hh * p.H;
-        out_row[k] = t * ((is_q ? p.nq : p.nk) * p.H) + hh * p.H;
-        if (u < p.rot_units) {
-          off_a[k] = int64_t(u) * V;
-          off_b[k] = half + int64_t(u) * V;
-        } else {
-          const int64_t w = int64_t(u - p.rot_units) * V;
-          off_a[k] = rd + w;
-          off_b[k] = rd + pass_half + w;
-        }
-        unit[k] = int32_t(u);
-        tlk[k] = int32_t(tl);
-        isq[k] = is_q;
-        load_raw<T, V, VEC>(in, in_row + off_a[k], va[k]);
-        load_raw<T, V, VEC>(in, in_row + off_b[k], vb[k]);
-      }
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        if (unit[k] < 0) continue;
-        void *out = isq[k] ? p.q_out : p.k_out;
-        const int64_t orow = out_row[k];
-        if (uint32_t(unit[k]) >= p.rot_units) {  // pass-through: raw bits
-          store_raw<T, V, VEC>(out, orow + off_a[k], va[k]);
-          store_raw<T, V, VEC>(out, orow + off_b[k], vb[k]);
-          continue;
-        }
-        float a[V], b[V], ya[V], yb[V];
-        raw_to_float<T, V, VEC>(va[k], a);
-        raw_to_float<T, V, VEC>(vb[k], b);
-        const float *cs = cs_tile + int64_t(tlk[k]) * rd;
-        if constexpr (NEOX) {
-          // [RSCC §rotate_half（GPT-NeoX style）旋转模式]: x1 = a (first half), x2 = b
-          const int64_t ci = int64_t(unit[k]) * V;
-#pragma unroll
-          for (int j = 0; j < V; ++j) {
-            const float c = cs[ci + j], s = cs[half + ci + j];
-            ya[j] = a[j] * c - b[j] * s;
-            yb[j] = b[j] * c + a[j] * s;
-          }
-        } else {
-          // [RSCC §rotate_interleaved（GPT-J style）旋转模式]: pairs (x[2m], x[2m+1]) inside
-          // each vector; vector a holds pair indices u*V/2.., vector b holds rd/4 + u*V/2..
-          const int64_t ca = int64_t(unit[k]) * (V / 2), cb = half / 2 + ca;
-#pragma unroll
-          for (int m = 0; m < V / 2; ++m) {
-            const float c = cs[ca + m], s = cs[half + ca + m];
-            ya[2 * m] = a[2 * m] * c - a[2 * m + 1] * s;
-            ya[2 * m + 1] = a[2 * m + 1] * c + a[2 * m] * s;
-            const float c2 = cs[cb + m], s2 = cs[half + cb + m];
-            yb[2 * m] = b[2 * m] * c2 - b[2 * m + 1] * s2;
-            yb[2 * m + 1] = b[2 * m + 1] * c2 + b[2 * m] * s2;
-          }
-        }
-        store_n<T, V, VEC>(out, orow + off_a[k], ya);
-        store_n<T, V, VEC>(out, orow + off_b[k], yb);
-      }
+    for (uint32_t pbase = 0;;) {
+      cache_store_pass<T, NEOX, V, VEC, K, NV>(p, t0, cs_tile, w);
+      pbase += pass;
+      if (pbase >= tile_items) break;
+      cache_load_pass<T, NEOX, V, VEC, K, NV>(p, t0, tile_items, pbase, w);
     }
     __syncthreads();  // the LDS tile is rewritten by the next tile
   }
@@ -407,18 +623,23 @@ int launch(const void *fn, int64_t blocks, size_t lds, void *stream, void *plan)
 }
 
 template <typename XT, typename CT>
-const void *pick_inplace(bool vec) {
-  return vec ? reinterpret_cast<const void *>(&inplace_interleave_kernel<XT, CT, true>)
-             : reinterpret_cast<const void *>(&inplace_interleave_kernel<XT, CT, false>);
+const void *pick_inplace(bool vec, bool cos_stream) {
+  constexpr int K = kInplaceItemsPerLane;
+  if (vec)
+    return cos_stream
+               ? reinterpret_cast<const void *>(&inplace_interleave_kernel<XT, CT, true, K, true>)
+               : reinterpret_cast<const void *>(&inplace_interleave_kernel<XT, CT, true, K, false>);
+  return reinterpret_cast<const void *>(&inplace_interleave_kernel<XT, CT, false, K, false>);
 }
 
 template <typename T>
 const void *pick_cache(bool neox, bool vec) {
+  constexpr int KN = kNeoxItemsPerLane, KJ = kGptjItemsPerLane;
   if (neox)
-    return vec ? reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, true, true>)
-               : reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, true, false>);
-  return vec ? reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, false, true>)
-             : reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, false, false>);
+    return vec ? reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, true, true, KN>)
+               : reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, true, false, KN>);
+  return vec ? reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, false, true, KJ>)
+             : reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, false, false, KJ>);
 }
 
 }  // namespace
@@ -443,14 +664,14 @@ ROPE_API int rope_partial_inplace(const rope_tensor *x, const rope_tensor *cos,
   g_last_error.clear();
   if (plan.noop) return ROPE_OK;
   const void *fn = nullptr;
-  if (plan.xdt == ROPE_F32) fn = pick_inplace<float, float>(plan.vector_io);
+  if (plan.xdt == ROPE_F32) fn = pick_inplace<float, float>(plan.vector_io, plan.cos_stream);
   else if (plan.xdt == ROPE_F16)
-    fn = plan.cdt == ROPE_F32 ? pick_inplace<_Float16, float>(plan.vector_io)
-                              : pick_inplace<_Float16, _Float16>(plan.vector_io);
+    fn = plan.cdt == ROPE_F32 ? pick_inplace<_Float16, float>(plan.vector_io, plan.cos_stream)
+                              : pick_inplace<_Float16, _Float16>(plan.vector_io, plan.cos_stream);
   else
-    fn = plan.cdt == ROPE_F32 ? pick_inplace<__bf16, float>(plan.vector_io)
-                              : pick_inplace<__bf16, __bf16>(plan.vector_io);
-  const int64_t per_block = int64_t(kBlock) * kItemsPerLane;
+    fn = plan.cdt == ROPE_F32 ? pick_inplace<__bf16, float>(plan.vector_io, plan.cos_stream)
+                              : pick_inplace<__bf16, __bf16>(plan.vector_io, plan.cos_stream);
+  const int64_t per_block = int64_t(kBlock) * kInplaceItemsPerLane;
   return launch(fn, (plan.items + per_block - 1) / per_block, 0, stream, &plan);
 }
 

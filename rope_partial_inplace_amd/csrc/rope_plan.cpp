@@ -163,15 +163,19 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
   p.cn = cos->shape[2] == 1 ? 0 : 1;
   p.cs = cos->shape[1] == 1 ? 0 : Nc;
   p.cb = cos->shape[0] == 1 ? 0 : Sc * Nc;
+  p.cos_stream = (cos->shape[0] == p.B || p.B == 1) && (cos->shape[1] == p.S || p.S == 1) &&
+                 (cos->shape[2] == p.N || p.N == 1);
 
-  // 16-byte vectors of x when every chunk start is 16-byte aligned; else element access.
+  // Lane chunks of V elements: a 16-byte access for the wider of x and cos/sin (8 bytes for
+  // the narrower) when every chunk start is aligned to its access size; else element access.
   const int xs = bytes_of(p.xdt), cs = bytes_of(p.cdt);
-  const int64_t v16 = 16 / xs;
-  const bool ok16 = L % v16 == 0 && (D * xs) % 16 == 0 && (start * xs) % 16 == 0 &&
-                    aligned16(p.x) && aligned16(p.cos) && aligned16(p.sin) &&
-                    (L * cs) % 16 == 0;
-  p.vector_io = ok16;
-  p.vec = ok16 ? uint32_t(v16) : 2u;
+  const int64_t v = 16 / std::max(xs, cs);
+  const bool aligned = L % v == 0 && (D * xs) % (v * xs) == 0 && (start * xs) % (v * xs) == 0 &&
+                       (reinterpret_cast<uintptr_t>(p.x) % uintptr_t(v * xs)) == 0 &&
+                       (reinterpret_cast<uintptr_t>(p.cos) % uintptr_t(v * cs)) == 0 &&
+                       (reinterpret_cast<uintptr_t>(p.sin) % uintptr_t(v * cs)) == 0;
+  p.vector_io = aligned;
+  p.vec = aligned ? uint32_t(v) : 2u;
   p.chunks_per_row = uint32_t(L / p.vec);
   p.items = p.rows * p.chunks_per_row;
   p.idx32 = p.items < (int64_t(1) << 32);
@@ -329,16 +333,34 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
                     (p.k_stride * es) % 16 == 0;
   p.vector_io = ok16;
   p.vec = uint32_t(16 / es);  // headSize and rotaryDim are 64-byte multiples: always divides
-  p.units = uint32_t(head_size / (2 * p.vec));
-  p.rot_units = uint32_t(rd / (2 * p.vec));
+  // NeoX pairs lie rd/2 apart, so a NeoX unit is two vectors (u and u + rd/(2 vec)); GPT-J
+  // pairs lie inside one vector, so a GPT-J unit is one vector and a head's units run
+  // contiguously.  Each access instruction then covers whole lines of the head.
+  const int64_t per_unit = p.neox ? 2 * p.vec : p.vec;
+  p.units = uint32_t(head_size / per_unit);
+  p.rot_units = uint32_t(rd / per_unit);
   const int64_t ipt = (p.nq + p.nk) * int64_t(p.units);
   if (ipt > 0x7fffffffLL)
     return reject(err, ROPE_ERR_PARAM_INVALID, "too many heads per token for this library");
   p.items_per_token = uint32_t(ipt);
-  // Tokens per workgroup: fill about one pass (kBlock * kItemsPerLane items); the LDS tile of
-  // cos|sin (tile_tokens * rd floats) stays within 32 KiB.
-  int64_t tt = std::max<int64_t>(1, int64_t(kBlock) * kItemsPerLane / ipt);
-  tt = std::min<int64_t>(tt, std::max<int64_t>(1, (32 * 1024) / (rd * 4)));
+  // Tokens per workgroup: the tile's items are processed in passes of kBlock*K; pick the
+  // smallest tile that fills its passes to >= 90% (at most 8 passes), else the best filled
+  // one; the LDS tile of cos|sin (tile_tokens * rd floats) stays within 32 KiB.
+  const int64_t pass = int64_t(kBlock) * (p.neox ? kNeoxItemsPerLane : kGptjItemsPerLane);
+  const int64_t tt_lds = std::max<int64_t>(1, (32 * 1024) / (rd * 4));
+  int64_t tt = 1;
+  double best = -1.0;
+  for (int64_t cand = 1; cand <= std::min<int64_t>(tt_lds, 64); ++cand) {
+    const int64_t items = cand * ipt;
+    const int64_t passes = (items + pass - 1) / pass;
+    if (passes > 8 && cand > 1) break;
+    const double fill = double(items) / double(passes * pass);
+    if (fill > best + 1e-9) {
+      best = fill;
+      tt = cand;
+    }
+    if (fill >= 0.9) break;
+  }
   tt = std::min<int64_t>(tt, T);
   if (rd * 4 * tt > 64 * 1024)
     return reject(err, ROPE_ERR_PARAM_INVALID, "rotaryDim too large for the LDS tile (max 16384)");
@@ -346,6 +368,9 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
   p.tiles = (T + tt - 1) / tt;
   p.div_units = make_fastdiv(p.units);
   p.div_ipt = make_fastdiv(p.items_per_token);
+  p.cache_vec = aligned16(p.cache) && (p.cache_stride * es) % 16 == 0;
+  p.stage_chunks = uint32_t((rd / 2) / p.vec);  // rd/2 is a 32-byte multiple
+  p.div_stage = make_fastdiv(p.stage_chunks);
   return ROPE_OK;
 }
 

@@ -52,6 +52,7 @@ struct InplacePlan {
   uint32_t chunks_per_row = 0;  // L / vec
   // cos/sin row of x-row (b, s, n) = b*cb + s*cs + n*cn (in rows of L elements)
   int64_t cb = 0, cs = 0, cn = 0;
+  bool cos_stream = false;  // every cos/sin row is read by exactly one x row (no broadcast)
   bool idx32 = true;  // rows and items fit in 32 bits: use FastDiv below
   FastDiv div_cpr, div_n, div_s;
 };
@@ -59,8 +60,9 @@ struct InplacePlan {
 // ---- cos/sin cache --------------------------------------------------------------------------
 // A workgroup owns a tile of `tile_tokens` tokens.  It first stages the tile's cos|sin rows
 // (gathered, mrope-stitched, raised to float32) in LDS, then its lanes walk the tile's
-// (token, head, unit) items; a unit is two vectors of `vec` elements of one head: either a
-// rotated unit (vector u and vector u + rd/(2 vec) of the rotated part) or a pass-through unit.
+// (token, head, unit) items.  NeoX: a unit is two vectors of `vec` elements (vector u and
+// vector u + rd/(2 vec) of the rotated part, or the same shape over the pass-through part).
+// GPT-J: a unit is one vector.
 struct CachePlan {
   rope_dtype dt = ROPE_F32;
   bool neox = true;
@@ -75,12 +77,14 @@ struct CachePlan {
   int32_t sec_end[4] = {0, 0, 0, 0};  // cumulative mrope section ends (in cos/sin index)
   int32_t nsec = 0;
   uint32_t vec = 1;          // elements per vector
-  uint32_t units = 0;        // units per head (H / (2 vec))
-  uint32_t rot_units = 0;    // rotated units per head (rd / (2 vec))
+  uint32_t units = 0;        // units per head (NeoX H / (2 vec), GPT-J H / vec)
+  uint32_t rot_units = 0;    // rotated units per head (NeoX rd / (2 vec), GPT-J rd / vec)
   uint32_t items_per_token = 0;
   uint32_t tile_tokens = 1;
   int64_t tiles = 0;
-  FastDiv div_units, div_ipt;
+  bool cache_vec = false;       // cache rows can be read with 16-byte loads
+  uint32_t stage_chunks = 0;    // (rd/2) / vec: vector chunks of one cos (or sin) half-row
+  FastDiv div_units, div_ipt, div_stage;
 };
 
 int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor *sin,
@@ -93,8 +97,12 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
                int is_neox_style, const rope_tensor *query_out, const rope_tensor *key_out,
                CachePlan *plan, std::string *err);
 
-// Items (lanes' work units) a workgroup processes per pass; the kernels use this too.
+// Workgroup size and the work units (16-byte chunks / two-vector units) a lane carries per
+// pass.  Few units per lane and many waves keep more independent HBM requests in flight on
+// gfx950 than deep per-lane unrolling.
 constexpr int kBlock = 256;
-constexpr int kItemsPerLane = 4;
+constexpr int kInplaceItemsPerLane = 1;
+constexpr int kNeoxItemsPerLane = 2;  // NeoX units are two vectors
+constexpr int kGptjItemsPerLane = 2;  // GPT-J units are one vector
 
 }  // namespace ropeamd
