@@ -472,7 +472,7 @@ __device__ inline void cache_load_pass(const CachePlan &p, int64_t t0, uint32_t 
                                        uint32_t pbase, CacheItems<T, V, VEC, K, NV> &w) {
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    const uint32_t it = pbase + uint32_t(k) * kBlock + threadIdx.x;
+    const uint32_t it = pbase + uint32_t(k) * kCacheBlock + threadIdx.x;
     w.it[k] = it < tile_items ? it : kNoItem;
     if (it >= tile_items) continue;
     const CacheItem c = cache_item<NEOX>(p, t0, it);
@@ -538,12 +538,12 @@ __device__ inline void cache_store_pass(const CachePlan &p, int64_t t0, const fl
 }
 
 template <typename T, bool NEOX, bool VEC, int K>
-__global__ __launch_bounds__(kBlock) void cos_sin_cache_kernel(CachePlan p) {
+__global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p) {
   extern __shared__ float cs_tile[];  // [tile_tokens][rd]: cos (rd/2) then sin (rd/2)
   constexpr int V = Io<T>::kPer16;
   constexpr int NV = NEOX ? 2 : 1;  // vectors per unit
   const int64_t rd = p.rd, half = rd / 2;
-  const uint32_t pass = uint32_t(kBlock) * K;
+  const uint32_t pass = uint32_t(kCacheBlock) * K;
   for (int64_t tile = blockIdx.x; tile < p.tiles; tile += gridDim.x) {
     const int64_t t0 = tile * int64_t(p.tile_tokens);
     const int64_t ntok = (p.T - t0) < int64_t(p.tile_tokens) ? (p.T - t0) : int64_t(p.tile_tokens);
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(kBlock) void cos_sin_cache_kernel(CachePlan p) {
     // chunk inside one mrope section (always, in rope mode) comes from one cache row with
     // 16-byte loads; a chunk split by a section boundary is gathered element by element.
     const uint32_t stage_items = uint32_t(ntok) * p.stage_chunks;
-    for (uint32_t idx = threadIdx.x; idx < stage_items; idx += kBlock) {
+    for (uint32_t idx = threadIdx.x; idx < stage_items; idx += kCacheBlock) {
       const uint32_t tl = fdiv(p.div_stage, idx);
       const int64_t i0 = int64_t(idx - tl * p.stage_chunks) * V;
       const int64_t tok = (t0 + tl) * p.pos_stride_tok;
@@ -610,10 +610,10 @@ constexpr int64_t kMaxGrid = int64_t(1) << 20;
 
 thread_local std::string g_last_error;
 
-int launch(const void *fn, int64_t blocks, size_t lds, void *stream, void *plan) {
+int launch(const void *fn, int64_t blocks, int threads, size_t lds, void *stream, void *plan) {
   if (blocks > kMaxGrid) blocks = kMaxGrid;
   void *args[] = {plan};
-  hipError_t e = hipLaunchKernel(fn, dim3(uint32_t(blocks)), dim3(kBlock), args, lds,
+  hipError_t e = hipLaunchKernel(fn, dim3(uint32_t(blocks)), dim3(uint32_t(threads)), args, lds,
                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_error = std::string("kernel launch failed: ") + hipGetErrorString(e);
@@ -672,7 +672,7 @@ ROPE_API int rope_partial_inplace(const rope_tensor *x, const rope_tensor *cos,
     fn = plan.cdt == ROPE_F32 ? pick_inplace<__bf16, float>(plan.vector_io, plan.cos_stream)
                               : pick_inplace<__bf16, __bf16>(plan.vector_io, plan.cos_stream);
   const int64_t per_block = int64_t(kBlock) * kInplaceItemsPerLane;
-  return launch(fn, (plan.items + per_block - 1) / per_block, 0, stream, &plan);
+  return launch(fn, (plan.items + per_block - 1) / per_block, kBlock, 0, stream, &plan);
 }
 
 ROPE_API int rope_with_cos_sin_cache(const rope_tensor *positions, const rope_tensor *query_in,
@@ -695,7 +695,7 @@ ROPE_API int rope_with_cos_sin_cache(const rope_tensor *positions, const rope_te
                    : plan.dt == ROPE_F16 ? pick_cache<_Float16>(plan.neox, plan.vector_io)
                                          : pick_cache<__bf16>(plan.neox, plan.vector_io);
   const size_t lds = size_t(plan.tile_tokens) * size_t(plan.rd) * sizeof(float);
-  return launch(fn, plan.tiles, lds, stream, &plan);
+  return launch(fn, plan.tiles, kCacheBlock, lds, stream, &plan);
 }
 
 ROPE_API const char *rope_last_error(void) { return g_last_error.c_str(); }

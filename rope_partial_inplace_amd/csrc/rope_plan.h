@@ -100,7 +100,9 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
 // Workgroup size and the work units (16-byte chunks / two-vector units) a lane carries per
 // pass.  Few units per lane and many waves keep more independent HBM requests in flight on
 // gfx950 than deep per-lane unrolling.
-constexpr int kBlock = 256;
+constexpr int kBlock = 1024;      // in-place kernel workgroup (few, large workgroups: the
+                                  // headline launch is short and dispatch-bound)
+constexpr int kCacheBlock = 256;  // cache kernel workgroup (one token tile)
 constexpr int kInplaceItemsPerLane = 1;
 constexpr int kNeoxItemsPerLane = 2;  // NeoX units are two vectors
 constexpr int kGptjItemsPerLane = 2;  // GPT-J units are one vector
