@@ -10,7 +10,9 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "rope_oracle.c")
-LIB_PATH = os.path.join(HERE, "librope_oracle.so")
+# ROPE_ORACLE_LIB points the tests at another build of this file (the mutation tests load
+# deliberately broken copies to show that the pins catch them).
+LIB_PATH = os.environ.get("ROPE_ORACLE_LIB") or os.path.join(HERE, "librope_oracle.so")
 CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
           "-Wall", "-Wextra", "-Werror"]
 

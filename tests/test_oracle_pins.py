@@ -107,6 +107,32 @@ def test_rounding_against_numpy_f16_sample():
     assert (oracle.round_f16_bits(f)[ok] == np16[ok]).all()
 
 
+def _ties(dropped_bits: int) -> np.ndarray:
+    """binary32 patterns whose dropped low bits are exactly half a unit, with the kept part
+    even and odd, for every exponent and both signs, plus their neighbours one ulp away."""
+    e = np.arange(256, dtype=np.uint32) << 23
+    half = np.uint32(1 << (dropped_bits - 1))
+    kept_lsb = np.uint32(1 << dropped_bits)
+    base = np.concatenate([e | half, e | half | kept_lsb, e | half | np.uint32(0x2AAAAA & ~((1 << dropped_bits) - 1))])
+    base = np.concatenate([base, base + 1, base - 1])
+    return np.concatenate([base, base | np.uint32(0x80000000)])
+
+
+def test_rounding_ties_and_boundaries():
+    """Round-half-to-even at every exponent: bfloat16 drops 16 bits; binary16 drops 13 bits
+    for normal results and more in the subnormal range (every shift up to 24 is covered)."""
+    with np.errstate(over="ignore"):
+        f = _ties(16).view(np.float32)
+        ok = ~np.isnan(f)
+        tb = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert (oracle.round_bf16_bits(f)[ok] == tb[ok]).all()
+        for k in range(13, 25):
+            f = _ties(k).view(np.float32)
+            ok = ~np.isnan(f)
+            tf = torch.from_numpy(f).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+            assert (oracle.round_f16_bits(f)[ok] == tf[ok]).all(), k
+
+
 def test_decoding_all_f16_and_bf16_patterns():
     bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     mine = oracle.f16_bits_to_f32(bits)
