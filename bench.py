@@ -115,7 +115,8 @@ def inplace_calls(ra, case, n_sets):
         x = case.x if i == 0 else case.x.clone()
         c = case.cos if i == 0 else case.cos.clone()
         s = case.sin if i == 0 else case.sin.clone()
-        calls.append(ra.prepare_partial_inplace(x, c, s, 1, case.partial_slice))
+        calls.append(ra.prepare_partial_inplace(x, c, s, 1, case.partial_slice,
+                                                backward=case.backward))
     return calls
 
 
@@ -133,7 +134,9 @@ def cache_calls(ra, torch, case, n_sets):
 
 def describe_case(name, case):
     if hasattr(case, "x"):
-        return (f"InplacePartialRotaryMul interleave x {str(case.x.dtype)[6:]} "
+        what = "InplacePartialRotaryMul backward (gradient)" if case.backward else \
+            "InplacePartialRotaryMul"
+        return (f"{what} interleave x {str(case.x.dtype)[6:]} "
                 f"{list(case.x.shape)} slice {case.partial_slice} cos/sin "
                 f"{str(case.cos.dtype)[6:]} {list(case.cos.shape)}")
     mode = f"mrope {case.mrope_section}" if case.mrope_section else "rope"
@@ -200,7 +203,8 @@ def main() -> int:
     ap.add_argument("--workloads", default=",".join(
                         ["inplace_bf16_8x4096x1x576_s512", "inplace_f32_1x16x2x64",
                          "cache_rope_neox_bf16_t8192", "cache_rope_gptj_f16_t32768_rd64",
-                         "cache_mrope_neox_bf16_t16384"]),
+                         "cache_mrope_neox_bf16_t16384",
+                         "inplace_backward_bf16_8x4096x1x576_s512"]),
                     help="first is the headline; the rest are reported under `kernels`")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)

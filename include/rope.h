@@ -1,12 +1,13 @@
 /*
  * rope.h -- C ABI of the MI355X (gfx950) RoPE apply library, librope_amd.so.
  *
- * Two operations, each one call that validates its arguments on the host and then enqueues
+ * Each operation is one call that validates its arguments on the host and then enqueues
  * hand-written HIP kernels on the caller's stream:
  *
- *   rope_partial_inplace      in-place partial RoPE, interleave mode, on a BSND tensor
- *   rope_with_cos_sin_cache   RoPE of query/key rows with cos/sin gathered from a cache by
- *                             position; rope or mrope mode; GPT-NeoX or GPT-J style
+ *   rope_partial_inplace           in-place partial RoPE, interleave mode, on a BSND tensor
+ *   rope_partial_inplace_backward  its gradient with respect to x, in place on the gradient
+ *   rope_with_cos_sin_cache        RoPE of query/key rows with cos/sin gathered from a cache by
+ *                                  position; rope or mrope mode; GPT-NeoX or GPT-J style
  *
  * Pages defining the operations:
  *   [IPRM] "CANN ops-transformer 的 aclnnInplacePartialRotaryMul 算子：Inplace 部分旋转位置编码
@@ -98,6 +99,25 @@ typedef struct {
 int rope_partial_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor *sin,
                          int64_t rotary_mode, const int64_t *partial_slice,
                          int64_t partial_slice_len, void *stream);
+
+/*
+ * rope_partial_inplace_backward -- gradient of rope_partial_inplace with respect to x, in place
+ * on the incoming gradient g.
+ *
+ * [IPRM §Python 接口与自动微分]: the training path computes the gradient of x with a backward
+ * op; cos and sin get no gradient; empty tensors and empty slices are no-ops.  The pages give
+ * no formula: on each slice pair the forward map is y = [[c0, -s0], [s1, c1]] x, so its
+ * gradient is the transpose,
+ *     g[2i]   = g[2i]*cos[2i]     + g[2i+1]*sin[2i+1]
+ *     g[2i+1] = g[2i+1]*cos[2i+1] - g[2i]*sin[2i]
+ * and elements outside [start, end) pass the gradient through unchanged (never touched).
+ * Arguments, layouts, validation, error codes and the no-op rules are those of
+ * rope_partial_inplace, with g in the place of x.
+ */
+int rope_partial_inplace_backward(const rope_tensor *g, const rope_tensor *cos,
+                                  const rope_tensor *sin, int64_t rotary_mode,
+                                  const int64_t *partial_slice, int64_t partial_slice_len,
+                                  void *stream);
 
 /*
  * rope_with_cos_sin_cache -- RoPE with a cos/sin cache ([RSCC §设计动机]).

@@ -46,6 +46,8 @@ def _load():
         P(OroTensor), P(OroTensor), P(OroTensor), ctypes.c_int64,
         P(ctypes.c_int64), ctypes.c_int64, P(ctypes.c_double)]
     lib.oro_rope_partial_inplace.restype = ctypes.c_int
+    lib.oro_rope_partial_inplace_backward.argtypes = lib.oro_rope_partial_inplace.argtypes
+    lib.oro_rope_partial_inplace_backward.restype = ctypes.c_int
     lib.oro_rope_with_cos_sin_cache.argtypes = [
         P(OroTensor), P(OroTensor), P(OroTensor), P(OroTensor),
         P(ctypes.c_int64), ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
@@ -127,6 +129,25 @@ def rope_partial_inplace(x, cos, sin, rotary_mode=1, partial_slice=None, *, twin
         dx, dc, ds = _desc(x), _desc(cos), _desc(sin)
     st = _lib.oro_rope_partial_inplace(dx, dc, ds, int(rotary_mode), sl, sl_len, x64p)
     return st, x64
+
+
+def rope_partial_inplace_backward(g, cos, sin, rotary_mode=1, partial_slice=None, *,
+                                  twin=False, raw_desc=None):
+    """Gradient of operation A, in place on the incoming gradient ``g``: on each slice pair
+    dx = (c0*g0 + s1*g1, c1*g1 - s0*g0), the transpose of the forward pair map
+    ([IPRM §Python 接口与自动微分]).  Returns ``(status, g64)``."""
+    g64 = None
+    g64p = None
+    if twin:
+        g64 = np.zeros(tuple(g.shape), dtype=np.float64)
+        g64p = g64.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    sl, sl_len = _ints(partial_slice)
+    if raw_desc is not None:
+        dg, dc, ds = raw_desc["x"], raw_desc["cos"], raw_desc["sin"]
+    else:
+        dg, dc, ds = _desc(g), _desc(cos), _desc(sin)
+    st = _lib.oro_rope_partial_inplace_backward(dg, dc, ds, int(rotary_mode), sl, sl_len, g64p)
+    return st, g64
 
 
 def rope_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,

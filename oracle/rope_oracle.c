@@ -247,9 +247,9 @@ static int is_float_dtype(int dt) { return dt == ORO_F32 || dt == ORO_F16 || dt 
  *                              length, cos/sin broadcast to BSND, contiguous tensors only;
  *   [IPRM §返回值与错误码]     161001 for null tensors, 161002 for every other invalid input.
  * ========================================================================================== */
-int oro_rope_partial_inplace(const oro_tensor *x, const oro_tensor *cos_t, const oro_tensor *sin_t,
-                             int64_t rotary_mode, const int64_t *partial_slice,
-                             int64_t partial_slice_len, double *x64) {
+static int partial_inplace(const oro_tensor *x, const oro_tensor *cos_t, const oro_tensor *sin_t,
+                           int64_t rotary_mode, const int64_t *partial_slice,
+                           int64_t partial_slice_len, double *x64, int backward) {
   /* null checks */
   if (!x || !cos_t || !sin_t) return fail(ORO_ERR_PARAM_NULLPTR, "xRef, cos or sin is null");
   if (!partial_slice && partial_slice_len > 0)
@@ -324,22 +324,56 @@ int oro_rope_partial_inplace(const oro_tensor *x, const oro_tensor *cos_t, const
           float bb = load_f32(x, j1);
           float c0 = load_f32(cos_t, crow + 2 * i), c1 = load_f32(cos_t, crow + 2 * i + 1);
           float s0 = load_f32(sin_t, crow + 2 * i), s1 = load_f32(sin_t, crow + 2 * i + 1);
-          /* y = x*cos + x_rotate*sin with x_rotate = (-b, a) on the pair */
-          float p0 = a * c0;
-          float q0 = (-bb) * s0;
-          float y0 = p0 + q0;
-          float p1 = bb * c1;
-          float q1 = a * s1;
-          float y1 = p1 + q1;
-          if (x64) {
-            x64[j0] = (double)a * (double)c0 + (-(double)bb) * (double)s0;
-            x64[j1] = (double)bb * (double)c1 + (double)a * (double)s1;
+          float y0, y1;
+          if (!backward) {
+            /* y = x*cos + x_rotate*sin with x_rotate = (-b, a) on the pair */
+            float p0 = a * c0;
+            float q0 = (-bb) * s0;
+            y0 = p0 + q0;
+            float p1 = bb * c1;
+            float q1 = a * s1;
+            y1 = p1 + q1;
+            if (x64) {
+              x64[j0] = (double)a * (double)c0 + (-(double)bb) * (double)s0;
+              x64[j1] = (double)bb * (double)c1 + (double)a * (double)s1;
+            }
+          } else {
+            /* gradient: the pair map is y = M x with M = [[c0, -s0], [s1, c1]], so
+             * dx = M^T g = (c0*g0 + s1*g1, c1*g1 - s0*g0); here (a, bb) = (g0, g1) */
+            float p0 = a * c0;
+            float q0 = bb * s1;
+            y0 = p0 + q0;
+            float p1 = bb * c1;
+            float q1 = a * s0;
+            y1 = p1 - q1;
+            if (x64) {
+              x64[j0] = (double)a * (double)c0 + (double)bb * (double)s1;
+              x64[j1] = (double)bb * (double)c1 - (double)a * (double)s0;
+            }
           }
           store_rounded(x, j0, y0);
           store_rounded(x, j1, y1);
         }
       }
   return ORO_OK;
+}
+
+int oro_rope_partial_inplace(const oro_tensor *x, const oro_tensor *cos_t, const oro_tensor *sin_t,
+                             int64_t rotary_mode, const int64_t *partial_slice,
+                             int64_t partial_slice_len, double *x64) {
+  return partial_inplace(x, cos_t, sin_t, rotary_mode, partial_slice, partial_slice_len, x64, 0);
+}
+
+/* Backward of operation A, in place on the incoming gradient g (same shapes, validation and
+ * no-op rules as the forward).  [IPRM §Python 接口与自动微分]: the training path computes the
+ * gradient of x with a backward op, cos/sin get no gradient, and empty tensors and empty
+ * slices are no-ops.  The pages give no formula; the gradient of the linear pair map above
+ * is its transpose.  Elements outside the slice pass the gradient through unchanged. */
+int oro_rope_partial_inplace_backward(const oro_tensor *g, const oro_tensor *cos_t,
+                                      const oro_tensor *sin_t, int64_t rotary_mode,
+                                      const int64_t *partial_slice, int64_t partial_slice_len,
+                                      double *g64) {
+  return partial_inplace(g, cos_t, sin_t, rotary_mode, partial_slice, partial_slice_len, g64, 1);
 }
 
 /* ==========================================================================================

@@ -6,6 +6,8 @@ of both operations runs in the library's HIP kernels.  PyTorch provides device m
 streams.  There is no fallback: if the library is not built this import fails.
 
   rope_partial_inplace(x, cos, sin, rotary_mode=1, partial_slice=None, stream=None)
+  rope_partial_inplace_backward(g, cos, sin, rotary_mode=1, partial_slice=None, stream=None)
+  InplacePartialRotaryMul.apply(x, cos, sin, partial_slice)   (autograd; x must not be a leaf)
   rope_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,
                           head_size, is_neox_style, query_out=None, key_out=None, stream=None)
 
@@ -56,6 +58,8 @@ def _load() -> ctypes.CDLL:
                                          ctypes.c_int64, P(ctypes.c_int64), ctypes.c_int64,
                                          ctypes.c_void_p]
     lib.rope_partial_inplace.restype = ctypes.c_int
+    lib.rope_partial_inplace_backward.argtypes = lib.rope_partial_inplace.argtypes
+    lib.rope_partial_inplace_backward.restype = ctypes.c_int
     lib.rope_with_cos_sin_cache.argtypes = [P(RopeTensor), P(RopeTensor), P(RopeTensor),
                                             P(RopeTensor), P(ctypes.c_int64), ctypes.c_int64,
                                             ctypes.c_int64, ctypes.c_int, P(RopeTensor),
@@ -138,6 +142,52 @@ def rope_partial_inplace(x, cos, sin, rotary_mode: int = 1, partial_slice=None, 
                                     int(rotary_mode), sl, sl_len, _stream_handle(stream, dev)))
 
 
+def rope_partial_inplace_backward(g, cos, sin, rotary_mode: int = 1, partial_slice=None,
+                                  stream=None):
+    """Gradient of rope_partial_inplace with respect to x, in place on the incoming gradient
+    ``g`` ([IPRM §Python 接口与自动微分]; the transpose of the forward pair map)."""
+    dev = _device_of([g, cos, sin])
+    dg, dc, ds = describe(g), describe(cos), describe(sin)
+    sl, sl_len = _int_array(partial_slice)
+    _check(LIB.rope_partial_inplace_backward(ctypes.byref(dg), ctypes.byref(dc),
+                                             ctypes.byref(ds), int(rotary_mode), sl, sl_len,
+                                             _stream_handle(stream, dev)))
+
+
+def _autograd_function():
+    import torch
+
+    class InplacePartialRotaryMul(torch.autograd.Function):
+        """Autograd wrapper ([IPRM §Python 接口与自动微分]): forward rotates x in place and marks
+        it dirty; backward runs the backward kernel on a contiguous copy of the incoming
+        gradient; cos and sin get no gradient."""
+
+        @staticmethod
+        def forward(ctx, x, cos, sin, partial_slice=None):
+            rope_partial_inplace(x, cos, sin, 1, partial_slice)
+            ctx.mark_dirty(x)
+            ctx.save_for_backward(cos, sin)
+            ctx.partial_slice = partial_slice
+            return x
+
+        @staticmethod
+        def backward(ctx, grad):
+            cos, sin = ctx.saved_tensors
+            g = grad.contiguous().clone()
+            rope_partial_inplace_backward(g, cos, sin, 1, ctx.partial_slice)
+            return g, None, None, None
+
+    return InplacePartialRotaryMul
+
+
+def __getattr__(name):
+    if name == "InplacePartialRotaryMul":
+        fn = _autograd_function()
+        globals()[name] = fn
+        return fn
+    raise AttributeError(name)
+
+
 def rope_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section=None,
                             head_size: int | None = None, is_neox_style: bool = True,
                             query_out=None, key_out=None, stream=None):
@@ -177,13 +227,14 @@ class PreparedCall:
 
 
 def prepare_partial_inplace(x, cos, sin, rotary_mode: int = 1, partial_slice=None,
-                            stream=None) -> PreparedCall:
+                            stream=None, backward: bool = False) -> PreparedCall:
     dev = _device_of([x, cos, sin])
     dx, dc, ds = describe(x), describe(cos), describe(sin)
     sl, sl_len = _int_array(partial_slice)
     args = (ctypes.byref(dx), ctypes.byref(dc), ctypes.byref(ds), int(rotary_mode), sl, sl_len,
             _stream_handle(stream, dev))
-    return PreparedCall(LIB.rope_partial_inplace, args, (x, cos, sin, dx, dc, ds, sl))
+    fn = LIB.rope_partial_inplace_backward if backward else LIB.rope_partial_inplace
+    return PreparedCall(fn, args, (x, cos, sin, dx, dc, ds, sl))
 
 
 def prepare_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,

@@ -300,11 +300,19 @@ __device__ inline uint32_t fdiv(const FastDiv &f, uint32_t n) {
 }
 
 // One interleave pair of [IPRM §计算原理与公式] (reading: x_rotate = (-x[2i+1], x[2i]) per pair):
-//   y0 = x0*c0 + (-x1)*s0,  y1 = x1*c1 + x0*s1.
+//   forward  y0 = x0*c0 + (-x1)*s0,  y1 = x1*c1 + x0*s1;
+//   backward (transpose of the pair map, [IPRM §Python 接口与自动微分]):
+//            g0' = g0*c0 + g1*s1,    g1' = g1*c1 - g0*s0.
+template <bool BWD>
 __device__ inline void rotate_pair(float a, float b, float c0, float c1, float s0, float s1,
                                    float &y0, float &y1) {
-  y0 = a * c0 - b * s0;
-  y1 = b * c1 + a * s1;
+  if constexpr (!BWD) {
+    y0 = a * c0 - b * s0;
+    y1 = b * c1 + a * s1;
+  } else {
+    y0 = a * c0 + b * s1;
+    y1 = b * c1 - a * s0;
+  }
 }
 
 // ============================================================================================
@@ -312,11 +320,12 @@ __device__ inline void rotate_pair(float a, float b, float c0, float c1, float s
 // A lane owns K chunks of V slice elements (V/2 pairs); chunks of one row are adjacent lanes,
 // so a wavefront reads and writes whole 16-byte-aligned runs of each row's slice.  Elements
 // outside [start, end) are never touched.  cos/sin rows are addressed with zero strides on
-// broadcast dims (BSND, BS1D, B1ND, B11D, 111D and mixed forms).  x is streamed
+// broadcast dims (BSND, BS1D, B1ND, B11D, 111D and mixed forms).  BWD runs the transpose
+// of the pair map on an incoming gradient (same access pattern).  x is streamed
 // (non-temporal); cos/sin are streamed too unless a row is shared by several x rows
 // (broadcast), where the caches serve the repeats.
 // ============================================================================================
-template <typename XT, typename CT, bool VEC, int K, bool CNT>
+template <typename XT, typename CT, bool VEC, int K, bool CNT, bool BWD>
 __global__ __launch_bounds__(kBlock) void inplace_interleave_kernel(InplacePlan p) {
   // one 16-byte access per lane for the wider of x and cos/sin, 8 bytes for the narrower
   constexpr int V = VEC ? 16 / (sizeof(XT) > sizeof(CT) ? int(sizeof(XT)) : int(sizeof(CT))) : 2;
@@ -363,8 +372,8 @@ __global__ __launch_bounds__(kBlock) void inplace_interleave_kernel(InplacePlan 
       float y[V];
 #pragma unroll
       for (int e = 0; e < V; e += 2)
-        rotate_pair(xv[k][e], xv[k][e + 1], cv[k][e], cv[k][e + 1], sv[k][e], sv[k][e + 1], y[e],
-                    y[e + 1]);
+        rotate_pair<BWD>(xv[k][e], xv[k][e + 1], cv[k][e], cv[k][e + 1], sv[k][e], sv[k][e + 1],
+                         y[e], y[e + 1]);
       store_n<XT, V, VEC, true>(p.x, xoff[k], y);
     }
   }
@@ -622,14 +631,25 @@ int launch(const void *fn, int64_t blocks, int threads, size_t lds, void *stream
   return ROPE_OK;
 }
 
-template <typename XT, typename CT>
+template <typename XT, typename CT, bool BWD>
 const void *pick_inplace(bool vec, bool cos_stream) {
   constexpr int K = kInplaceItemsPerLane;
   if (vec)
-    return cos_stream
-               ? reinterpret_cast<const void *>(&inplace_interleave_kernel<XT, CT, true, K, true>)
-               : reinterpret_cast<const void *>(&inplace_interleave_kernel<XT, CT, true, K, false>);
-  return reinterpret_cast<const void *>(&inplace_interleave_kernel<XT, CT, false, K, false>);
+    return cos_stream ? reinterpret_cast<const void *>(
+                            &inplace_interleave_kernel<XT, CT, true, K, true, BWD>)
+                      : reinterpret_cast<const void *>(
+                            &inplace_interleave_kernel<XT, CT, true, K, false, BWD>);
+  return reinterpret_cast<const void *>(&inplace_interleave_kernel<XT, CT, false, K, false, BWD>);
+}
+
+template <bool BWD>
+const void *pick_inplace_dtype(const InplacePlan &p) {
+  if (p.xdt == ROPE_F32) return pick_inplace<float, float, BWD>(p.vector_io, p.cos_stream);
+  if (p.xdt == ROPE_F16)
+    return p.cdt == ROPE_F32 ? pick_inplace<_Float16, float, BWD>(p.vector_io, p.cos_stream)
+                             : pick_inplace<_Float16, _Float16, BWD>(p.vector_io, p.cos_stream);
+  return p.cdt == ROPE_F32 ? pick_inplace<__bf16, float, BWD>(p.vector_io, p.cos_stream)
+                           : pick_inplace<__bf16, __bf16, BWD>(p.vector_io, p.cos_stream);
 }
 
 template <typename T>
@@ -649,10 +669,12 @@ using namespace ropeamd;
 
 #define ROPE_API extern "C" __attribute__((visibility("default")))
 
-ROPE_API int rope_partial_inplace(const rope_tensor *x, const rope_tensor *cos,
-                                  const rope_tensor *sin, int64_t rotary_mode,
-                                  const int64_t *partial_slice, int64_t partial_slice_len,
-                                  void *stream) {
+namespace ropeamd {
+namespace {
+
+int run_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor *sin,
+                int64_t rotary_mode, const int64_t *partial_slice, int64_t partial_slice_len,
+                void *stream, bool backward) {
   InplacePlan plan;
   std::string err;
   const int st = plan_inplace(x, cos, sin, rotary_mode, partial_slice, partial_slice_len, &plan,
@@ -663,16 +685,26 @@ ROPE_API int rope_partial_inplace(const rope_tensor *x, const rope_tensor *cos,
   }
   g_last_error.clear();
   if (plan.noop) return ROPE_OK;
-  const void *fn = nullptr;
-  if (plan.xdt == ROPE_F32) fn = pick_inplace<float, float>(plan.vector_io, plan.cos_stream);
-  else if (plan.xdt == ROPE_F16)
-    fn = plan.cdt == ROPE_F32 ? pick_inplace<_Float16, float>(plan.vector_io, plan.cos_stream)
-                              : pick_inplace<_Float16, _Float16>(plan.vector_io, plan.cos_stream);
-  else
-    fn = plan.cdt == ROPE_F32 ? pick_inplace<__bf16, float>(plan.vector_io, plan.cos_stream)
-                              : pick_inplace<__bf16, __bf16>(plan.vector_io, plan.cos_stream);
+  const void *fn = backward ? pick_inplace_dtype<true>(plan) : pick_inplace_dtype<false>(plan);
   const int64_t per_block = int64_t(kBlock) * kInplaceItemsPerLane;
   return launch(fn, (plan.items + per_block - 1) / per_block, kBlock, 0, stream, &plan);
+}
+
+}  // namespace
+}  // namespace ropeamd
+
+ROPE_API int rope_partial_inplace(const rope_tensor *x, const rope_tensor *cos,
+                                  const rope_tensor *sin, int64_t rotary_mode,
+                                  const int64_t *partial_slice, int64_t partial_slice_len,
+                                  void *stream) {
+  return run_inplace(x, cos, sin, rotary_mode, partial_slice, partial_slice_len, stream, false);
+}
+
+ROPE_API int rope_partial_inplace_backward(const rope_tensor *g, const rope_tensor *cos,
+                                           const rope_tensor *sin, int64_t rotary_mode,
+                                           const int64_t *partial_slice,
+                                           int64_t partial_slice_len, void *stream) {
+  return run_inplace(g, cos, sin, rotary_mode, partial_slice, partial_slice_len, stream, true);
 }
 
 ROPE_API int rope_with_cos_sin_cache(const rope_tensor *positions, const rope_tensor *query_in,

@@ -70,6 +70,7 @@ class InplaceCase:
     partial_slice: list | None
     tokens: int           # B*S
     algo_bytes: int       # bytes the op must move (slice read+write, cos, sin)
+    backward: bool = False  # run the gradient op (x is then the incoming gradient)
 
 
 def inplace_case(name, B, S, N, D, xdtype, cdtype, partial_slice, cos_shape=None, seed=0,
@@ -187,6 +188,14 @@ def cache_mrope(device="cpu"):
                       positions=pos, device=device)
 
 
+def inplace_bf16_slice_backward(device="cpu"):
+    """The gradient op on the headline shape: incoming gradient bf16 [8,4096,1,576]."""
+    case = inplace_bf16_slice(device)
+    case.name = "inplace_backward_bf16_8x4096x1x576_s512"
+    case.backward = True
+    return case
+
+
 CONFIGS = {
     "inplace_f32_1x16x2x64": inplace_f32_small,
     "inplace_bf16_8x4096x1x576_s512": inplace_bf16_slice,
@@ -194,5 +203,6 @@ CONFIGS = {
     "cache_rope_gptj_f16_t32768_rd64": cache_rope_gptj_partial,
     "cache_mrope_neox_bf16_t16384": cache_mrope,
 }
+CONFIGS["inplace_backward_bf16_8x4096x1x576_s512"] = inplace_bf16_slice_backward
 HEADLINE = "inplace_bf16_8x4096x1x576_s512"
 

@@ -90,14 +90,15 @@ def ints(v):
     return (ctypes.c_int64 * max(len(v), 1))(*v), len(v)
 
 
-def call_inplace(x, c, s, mode, sl, sl_len=None):
+def call_inplace(x, c, s, mode, sl, sl_len=None, backward=False):
     arr, n = ints(sl)
     if sl_len is not None:
         n = sl_len
-    lib_st = ra.LIB.rope_partial_inplace(lib_desc(x), lib_desc(c), lib_desc(s), mode, arr, n,
-                                         None)
-    ora_st = oracle._lib.oro_rope_partial_inplace(oro_desc(x), oro_desc(c), oro_desc(s), mode,
-                                                  arr, n, None)
+    lib_fn = ra.LIB.rope_partial_inplace_backward if backward else ra.LIB.rope_partial_inplace
+    ora_fn = (oracle._lib.oro_rope_partial_inplace_backward if backward
+              else oracle._lib.oro_rope_partial_inplace)
+    lib_st = lib_fn(lib_desc(x), lib_desc(c), lib_desc(s), mode, arr, n, None)
+    ora_st = ora_fn(oro_desc(x), oro_desc(c), oro_desc(s), mode, arr, n, None)
     return lib_st, ora_st
 
 
@@ -155,10 +156,11 @@ INPLACE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("backward", [False, True], ids=["forward", "backward"])
 @pytest.mark.parametrize("name,build,expected", INPLACE_CASES, ids=[c[0] for c in INPLACE_CASES])
-def test_inplace_validation(name, build, expected):
+def test_inplace_validation(name, build, expected, backward):
     args = build(inplace_base())
-    lib_st, ora_st = call_inplace(*args)
+    lib_st, ora_st = call_inplace(*args, backward=backward)
     assert lib_st == expected, ra.last_error()
     assert ora_st == expected, oracle.last_error()
 

@@ -355,3 +355,71 @@ def test_binding_errors_touch_nothing():
     assert e.value.code == ra.ROPE_ERR_PARAM_INVALID
     torch.cuda.synchronize()
     assert not qo.any() and not ko.any()
+
+
+# ------------------------------------------------------------------------------------------
+# backward of the in-place op ([IPRM §Python 接口与自动微分]; transpose of the pair map)
+# ------------------------------------------------------------------------------------------
+
+def check_backward(g_before, g_after_gpu, cos, sin, sl, what):
+    ref = g_before.clone()
+    st, g64 = oracle.rope_partial_inplace_backward(ref, cos.cpu(), sin.cpu(), 1, sl, twin=True)
+    assert st == 0, oracle.last_error()
+    D = g_before.shape[-1]
+    start, end = (0, D) if sl is None else sl
+    got = g_after_gpu.cpu()
+    check_bits_equal(got[..., :start], g_before[..., :start], what + " [0,start)")
+    check_bits_equal(got[..., end:], g_before[..., end:], what + " [end,D)")
+    if g_before.dtype in HALF:
+        return check_half(got[..., start:end], ref[..., start:end], what)
+    # scale of the transposed products: |g0 c0| + |g1 s1| and |g1 c1| + |g0 s0|
+    gs = as_f64(g_before)[..., start:end]
+    L = end - start
+    c = np.broadcast_to(as_f64(cos), gs.shape[:-1] + (L,))
+    s = np.broadcast_to(as_f64(sin), gs.shape[:-1] + (L,))
+    a, b = gs[..., 0::2], gs[..., 1::2]
+    scale = np.empty_like(gs)
+    scale[..., 0::2] = np.abs(a * c[..., 0::2]) + np.abs(b * s[..., 1::2])
+    scale[..., 1::2] = np.abs(b * c[..., 1::2]) + np.abs(a * s[..., 0::2])
+    return check_f32(got[..., start:end], g64[..., start:end], scale, what)
+
+
+@pytest.mark.parametrize("cfg", ["inplace_f32_1x16x2x64", "inplace_bf16_8x4096x1x576_s512"])
+def test_backward_configs_full(cfg):
+    case = W.CONFIGS[cfg](DEV)
+    g = case.x  # the same seeded N(0,1) tensor serves as the incoming gradient
+    before = g.cpu()
+    ra.rope_partial_inplace_backward(g, case.cos, case.sin, 1, case.partial_slice)
+    torch.cuda.synchronize()
+    check_backward(before, g, case.cos, case.sin, case.partial_slice, "backward " + case.name)
+
+
+@pytest.mark.parametrize("xdt,cdt", DTYPE_PAIRS, ids=lambda d: str(d).split(".")[-1])
+@pytest.mark.parametrize("layout", ["BSND", "BS1D", "B11D", "111D"])
+@pytest.mark.parametrize("shape,sl", [((3, 37, 5, 96), [16, 80]), ((1, 300, 2, 40), [1, 37])])
+def test_backward_sweep(xdt, cdt, layout, shape, sl):
+    B, S, N, D = shape
+    L = sl[1] - sl[0]
+    cshape = LAYOUTS[layout](B, S, N) + (L,)
+    case = W.inplace_case("bwd", B, S, N, D, xdt, cdt, sl, cos_shape=cshape, seed=S + 5,
+                          table="randn", device=DEV)
+    before = case.x.cpu()
+    ra.rope_partial_inplace_backward(case.x, case.cos, case.sin, 1, sl)
+    torch.cuda.synchronize()
+    check_backward(before, case.x, case.cos, case.sin, sl, f"backward {layout} {shape} {xdt}/{cdt}")
+
+
+def test_autograd_wrapper_gradient():
+    """InplacePartialRotaryMul (forward kernel, mark_dirty, backward kernel) gives the same
+    gradient as the oracle's backward applied to the incoming gradient."""
+    B, S, N, D, sl = 2, 32, 8, 128, [0, 64]
+    g = W.generator(31, DEV)
+    x = W.randn((B, S, N, D), torch.float32, g).requires_grad_(True)
+    c = W.randn((B, S, 1, 64), torch.float32, g)
+    s = W.randn((B, S, 1, 64), torch.float32, g)
+    y = x * 1.0
+    y = ra.InplacePartialRotaryMul.apply(y, c, s, sl)
+    w = W.randn((B, S, N, D), torch.float32, g)
+    (y * w).sum().backward()
+    torch.cuda.synchronize()
+    check_backward(w.cpu(), x.grad, c, s, sl, "autograd")

@@ -17,8 +17,10 @@ SRC = os.path.join(ROOT, "oracle", "rope_oracle.c")
 
 # (name, text to replace, replacement, pin tests to run (-k expression))
 MUTANTS = [
-    ("interleave y0 sign", "float y0 = p0 + q0;", "float y0 = p0 - q0;", "golden_inplace or matrices"),
-    ("interleave dropped term", "float y1 = p1 + q1;", "float y1 = p1;", "golden_inplace or matrices"),
+    ("interleave y0 sign", "float q0 = (-bb) * s0;", "float q0 = bb * s0;",
+     "golden_inplace or matrices"),
+    ("interleave dropped term", "float q1 = a * s1;\n            y1 = p1 + q1;",
+     "float q1 = a * s1;\n            y1 = p1;", "golden_inplace or matrices"),
     ("cos and sin swapped", "float c0 = load_f32(cos_t, crow + 2 * i), c1 = load_f32(cos_t, crow + 2 * i + 1);",
      "float c0 = load_f32(sin_t, crow + 2 * i), c1 = load_f32(sin_t, crow + 2 * i + 1);",
      "golden_inplace or matrices or exact_angles"),
@@ -46,6 +48,9 @@ MUTANTS = [
      "if (rem >= half) q += 1;", "rounding_ties"),
     ("f16 subnormal quantum", "int Ec = E < -14 ? -14 : E;", "int Ec = E < -15 ? -15 : E;",
      "rounding_ties"),
+    ("backward sign", "y1 = p1 - q1;", "y1 = p1 + q1;", "backward or twin"),
+    ("backward uses forward's sin index", "float q0 = bb * s1;", "float q0 = bb * s0;",
+     "backward or twin"),
     ("f16 subnormal decode", "v = ldexpf((float)m, -24);", "v = ldexpf((float)m, -23);",
      "decoding"),
 ]

@@ -478,3 +478,106 @@ def test_oracle_refuses_out_of_range_positions_without_writing():
                                               None, 32, True, qo, ko)
     assert st == oracle.ERR_OUTSIDE_CONTRACT
     assert (raw_bits(qo) == 0).all()
+
+
+# ------------------------------------------------------------------------------------------
+# Backward of the in-place op ([IPRM §Python 接口与自动微分]; the transpose of the pair map)
+# ------------------------------------------------------------------------------------------
+
+def run_backward(g, cos, sin, sl, twin=False):
+    g = g.clone()
+    st, g64 = oracle.rope_partial_inplace_backward(g, cos, sin, 1, sl, twin=twin)
+    assert st == oracle.OK, oracle.last_error()
+    return g, g64
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+def test_golden_backward(dt):
+    gj = golden("t7_backward_pairs.json")
+    g = torch.tensor(gj["grad"], dtype=DT[dt]).reshape(gj["x_shape"])
+    c = torch.tensor(gj["cos"], dtype=DT[dt]).reshape(1, 1, 1, 4)
+    s = torch.tensor(gj["sin"], dtype=DT[dt]).reshape(1, 1, 1, 4)
+    dx, _ = run_backward(g, c, s, gj["partial_slice"])
+    assert f64(dx).ravel().tolist() == gj["expected"]
+
+
+@pytest.mark.parametrize("cos_layout", ["BSND", "BS1D", "B11D", "1S1D"])
+def test_backward_is_adjoint_of_forward(cos_layout):
+    """<F(x), v> = <x, B(v)> for random x, v and per-element cos/sin (float64 twins)."""
+    B_, S, N, D, sl = 2, 5, 3, 24, [4, 20]
+    L = sl[1] - sl[0]
+    shape = {"BSND": (B_, S, N, L), "BS1D": (B_, S, 1, L), "B11D": (B_, 1, 1, L),
+             "1S1D": (1, S, 1, L)}[cos_layout]
+    gen = torch.Generator().manual_seed(21)
+    x = torch.randn(B_, S, N, D, generator=gen)
+    v = torch.randn(B_, S, N, D, generator=gen)
+    c = torch.randn(shape, generator=gen)
+    s = torch.randn(shape, generator=gen)
+    _, fx = run_inplace(x, c, s, sl, twin=True)
+    _, bv = run_backward(v, c, s, sl, twin=True)
+    lhs = float((fx * f64(v)).sum())
+    rhs = float((f64(x) * bv).sum())
+    assert abs(lhs - rhs) <= 1e-12 * (abs(lhs) + abs(rhs) + 1)
+
+
+def test_backward_matches_torch_autograd():
+    """PyTorch autograd of the forward written with tensor ops in float64 (x2 = odd
+    elements, x1 = even ones, the pairwise rotation assembled with torch.stack)."""
+    B_, S, N, D, sl = 2, 4, 2, 16, [2, 14]
+    gen = torch.Generator().manual_seed(22)
+    x = torch.randn(B_, S, N, D, generator=gen, dtype=torch.float64, requires_grad=True)
+    c = torch.randn(B_, S, 1, sl[1] - sl[0], generator=gen, dtype=torch.float64)
+    s = torch.randn(B_, S, 1, sl[1] - sl[0], generator=gen, dtype=torch.float64)
+    g = torch.randn(B_, S, N, D, generator=gen, dtype=torch.float64)
+    part = x[..., sl[0]:sl[1]]
+    x1, x2 = part[..., 0::2], part[..., 1::2]
+    rot = torch.stack((-x2, x1), dim=-1).flatten(-2)
+    y = torch.cat([x[..., :sl[0]], part * c + rot * s, x[..., sl[1]:]], dim=-1)
+    (grad,) = torch.autograd.grad(y, x, g)
+    _, g64 = run_backward(g.float(), c.float(), s.float(), sl, twin=True)
+    # the oracle reads float32 copies of c, s and g: compare at float32 input precision
+    np.testing.assert_allclose(g64, grad.numpy(), rtol=2e-6, atol=2e-6)
+
+
+def test_backward_inverts_rotation():
+    case = W.inplace_case("inv", 2, 64, 2, 96, torch.float32, torch.float32, [32, 96], seed=23)
+    y, _ = run_inplace(case.x, case.cos, case.sin, case.partial_slice)
+    back, _ = run_backward(y, case.cos, case.sin, case.partial_slice)
+    np.testing.assert_allclose(f64(back), f64(case.x), rtol=0, atol=1e-5)
+
+
+def test_backward_untouched_and_noop():
+    g = torch.randn(2, 3, 2, 20, generator=torch.Generator().manual_seed(24)).to(torch.bfloat16)
+    c = torch.randn(2, 3, 1, 8).to(torch.bfloat16)
+    out, _ = run_backward(g, c, c.clone(), [6, 14])
+    assert (raw_bits(out)[..., :6] == raw_bits(g)[..., :6]).all()
+    assert (raw_bits(out)[..., 14:] == raw_bits(g)[..., 14:]).all()
+    same, _ = run_backward(g, c, c.clone(), [6, 6])
+    assert (raw_bits(same) == raw_bits(g)).all()
+
+
+@pytest.mark.parametrize("direction", ["forward", "backward"])
+def test_inplace_fp32_within_bound_of_twin(direction):
+    """The float32 results equal the float64 twin within 2^-23 (|p| + |q|) per element, with
+    per-element (not pair-repeated) cos/sin: ties the float32 path to the twin that the
+    adjoint, matrix and autograd pins check."""
+    gen = torch.Generator().manual_seed(25)
+    x = torch.randn(3, 7, 2, 40, generator=gen) * torch.exp(torch.randn(3, 7, 2, 40, generator=gen))
+    c = torch.randn(3, 7, 1, 32, generator=gen)
+    s = torch.randn(3, 7, 1, 32, generator=gen)
+    sl = [4, 36]
+    run = run_inplace if direction == "forward" else run_backward
+    y, y64 = run(x, c, s, sl, twin=True)
+    a, b = f64(x)[..., 4:36:2], f64(x)[..., 5:36:2]
+    cb = np.broadcast_to(f64(c), (3, 7, 2, 32))
+    sb = np.broadcast_to(f64(s), (3, 7, 2, 32))
+    c0, c1, s0, s1 = cb[..., 0::2], cb[..., 1::2], sb[..., 0::2], sb[..., 1::2]
+    scale = np.empty((3, 7, 2, 32))
+    if direction == "forward":
+        scale[..., 0::2] = np.abs(a * c0) + np.abs(b * s0)
+        scale[..., 1::2] = np.abs(b * c1) + np.abs(a * s1)
+    else:
+        scale[..., 0::2] = np.abs(a * c0) + np.abs(b * s1)
+        scale[..., 1::2] = np.abs(b * c1) + np.abs(a * s0)
+    err = np.abs(f64(y)[..., 4:36] - y64[..., 4:36])
+    assert (err <= 2.0 ** -23 * scale * (1 + 1e-6)).all()
