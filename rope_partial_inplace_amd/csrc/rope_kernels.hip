@@ -406,6 +406,11 @@ __device__ inline int64_t clamp_position(const CachePlan &p, int64_t pos) {
   return pos < 0 ? 0 : (pos >= p.max_seq ? p.max_seq - 1 : pos);
 }
 
+// Word j of a 16-byte raw vector.
+__device__ inline uint32_t word_of(const u32x4 &v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
 // N floats from LDS: N a multiple of 4 at a 16-byte aligned address, or N == 2 at an 8-byte
 // aligned address.
 template <int N>
@@ -492,7 +497,7 @@ __device__ inline void cache_load_pass(const CachePlan &p, int64_t t0, uint32_t 
 }
 
 template <typename T, bool NEOX, int V, bool VEC, int K, int NV>
-__device__ inline void cache_store_pass(const CachePlan &p, int64_t t0, const float *cs_tile,
+__device__ inline void cache_store_pass(const CachePlan &p, int64_t t0, const T *cs_tile,
                                         const CacheItems<T, V, VEC, K, NV> &w) {
   const int64_t rd = p.rd, half = rd / 2;
 #pragma unroll
@@ -505,23 +510,27 @@ __device__ inline void cache_store_pass(const CachePlan &p, int64_t t0, const fl
       if constexpr (NV == 2) store_raw<T, V, VEC, true>(out, c.out_row + c.off_b, w.v[k][NV - 1]);
       continue;
     }
-    const float *cs = cs_tile + int64_t(c.tl) * rd;
+    // the token's cos|sin row, kept in LDS in the cache's own element type
+    const T *cs = cs_tile + int64_t(c.tl) * rd;
+    constexpr int PW = Io<T>::kPerWord;
     if constexpr (NEOX) {
       // [RSCC §rotate_half（GPT-NeoX style）旋转模式]: x1 = a (first half), x2 = b.  Worked one
       // 32-bit word (1 or 2 elements) of each vector at a time to keep few values live.
-      constexpr int PW = Io<T>::kPerWord;
-      const float *cc = cs + int64_t(c.u) * V;
+      const int64_t ci = int64_t(c.u) * V;
+      const u32x4 cw = *reinterpret_cast<const u32x4 *>(cs + ci);
+      const u32x4 sw = *reinterpret_cast<const u32x4 *>(cs + half + ci);
       RawN<T, V, VEC> oa, ob;
 #pragma unroll
       for (int q = 0; q < V / PW; ++q) {
-        float a[PW], b[PW], ya[PW], yb[PW];
+        float a[PW], b[PW], ya[PW], yb[PW], cv[PW], sv[PW];
         raw_word_to_float<T, V, VEC>(w.v[k][0], q, a);
         raw_word_to_float<T, V, VEC>(w.v[k][NV - 1], q, b);
+        Io<T>::word_to_floats(word_of(cw, q), cv);
+        Io<T>::word_to_floats(word_of(sw, q), sv);
 #pragma unroll
         for (int e = 0; e < PW; ++e) {
-          const float cv = cc[q * PW + e], sv = cc[half + q * PW + e];
-          ya[e] = a[e] * cv - b[e] * sv;
-          yb[e] = b[e] * cv + a[e] * sv;
+          ya[e] = a[e] * cv[e] - b[e] * sv[e];
+          yb[e] = b[e] * cv[e] + a[e] * sv[e];
         }
         float_to_raw_word<T, V, VEC>(ya, q, oa);
         float_to_raw_word<T, V, VEC>(yb, q, ob);
@@ -530,12 +539,16 @@ __device__ inline void cache_store_pass(const CachePlan &p, int64_t t0, const fl
       store_raw<T, V, VEC, true>(out, c.out_row + c.off_b, ob);
     } else {
       // [RSCC §rotate_interleaved（GPT-J style）旋转模式]: pairs (x[2m], x[2m+1]) inside the
-      // vector; vector u holds pair indices u*V/2 .. u*V/2 + V/2 - 1
+      // vector; vector u holds pair indices u*V/2 .. u*V/2 + V/2 - 1 (V/2 elements = 8 bytes)
       float a[V], ya[V], cv[V / 2], sv[V / 2];
       raw_to_float<T, V, VEC>(w.v[k][0], a);
       const int64_t ca = int64_t(c.u) * (V / 2);
-      lds_read<V / 2>(cs + ca, cv);
-      lds_read<V / 2>(cs + half + ca, sv);
+      const u32x2 cw = *reinterpret_cast<const u32x2 *>(cs + ca);
+      const u32x2 sw = *reinterpret_cast<const u32x2 *>(cs + half + ca);
+      Io<T>::word_to_floats(cw.x, cv);
+      Io<T>::word_to_floats(cw.y, cv + PW);
+      Io<T>::word_to_floats(sw.x, sv);
+      Io<T>::word_to_floats(sw.y, sv + PW);
 #pragma unroll
       for (int m = 0; m < V / 2; ++m) {
         ya[2 * m] = a[2 * m] * cv[m] - a[2 * m + 1] * sv[m];
@@ -548,7 +561,9 @@ __device__ inline void cache_store_pass(const CachePlan &p, int64_t t0, const fl
 
 template <typename T, bool NEOX, bool VEC, int K>
 __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p) {
-  extern __shared__ float cs_tile[];  // [tile_tokens][rd]: cos (rd/2) then sin (rd/2)
+  // [tile_tokens][rd] elements of T: the gathered cos (rd/2) then sin (rd/2) of each token
+  extern __shared__ u32x4 cs_lds[];
+  T *cs_tile = reinterpret_cast<T *>(cs_lds);
   constexpr int V = Io<T>::kPer16;
   constexpr int NV = NEOX ? 2 : 1;  // vectors per unit
   const int64_t rd = p.rd, half = rd / 2;
@@ -558,45 +573,58 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
     const int64_t ntok = (p.T - t0) < int64_t(p.tile_tokens) ? (p.T - t0) : int64_t(p.tile_tokens);
     const uint32_t tile_items = uint32_t(ntok) * p.items_per_token;
 
+    // The position of this lane's first staging chunk is loaded before the first pass's q/k
+    // loads: waiting for it does not then wait for them, and the position -> cache-row
+    // chain runs while the q/k data is in flight.
+    const uint32_t stage_items = uint32_t(ntok) * p.stage_chunks;
+    int64_t first_pos = 0;
+    if (threadIdx.x < stage_items) {
+      const uint32_t tl = fdiv(p.div_stage, threadIdx.x);
+      const int64_t i0 = int64_t(threadIdx.x - tl * p.stage_chunks) * V;
+      const int sec = p.mrope ? mrope_section_of(p, i0) : 0;
+      first_pos = p.positions[sec * p.pos_stride_row + (t0 + tl) * p.pos_stride_tok];
+    }
+
     CacheItems<T, V, VEC, K, NV> w;
     cache_load_pass<T, NEOX, V, VEC, K, NV>(p, t0, tile_items, 0, w);
 
     // ---- stage the tile's cos|sin rows in LDS (steps 1-2: gather, split, stitch) ----
     // One lane per V-element chunk of a token's cos half (and the matching sin chunk).  A
-    // chunk inside one mrope section (always, in rope mode) comes from one cache row with
-    // 16-byte loads; a chunk split by a section boundary is gathered element by element.
-    const uint32_t stage_items = uint32_t(ntok) * p.stage_chunks;
+    // chunk inside one mrope section (always, in rope mode) is copied from one cache row as
+    // 16-byte vectors; a chunk split by a section boundary is gathered element by element.
+    // Values stay in the cache's element type (bits copied, raised to float32 at use).
     for (uint32_t idx = threadIdx.x; idx < stage_items; idx += kCacheBlock) {
       const uint32_t tl = fdiv(p.div_stage, idx);
       const int64_t i0 = int64_t(idx - tl * p.stage_chunks) * V;
       const int64_t tok = (t0 + tl) * p.pos_stride_tok;
       const int s_lo = p.mrope ? mrope_section_of(p, i0) : 0;
       const int s_hi = p.mrope ? mrope_section_of(p, i0 + V - 1) : 0;
-      float *dst = cs_tile + int64_t(tl) * rd + i0;
+      T *dst = cs_tile + int64_t(tl) * rd + i0;
+      using R = typename Io<T>::raw;
       if (s_lo == s_hi) {
-        const int64_t row = clamp_position(p, p.positions[s_lo * p.pos_stride_row + tok]) *
-                            p.cache_stride;
-        float c[V], sn[V];
+        const int64_t pos =
+            idx == threadIdx.x ? first_pos : p.positions[s_lo * p.pos_stride_row + tok];
+        const int64_t row = clamp_position(p, pos) * p.cache_stride;
+        const T *src = static_cast<const T *>(p.cache) + row + i0;
         if (p.cache_vec) {
-          load_n<T, V, true, false>(p.cache, row + i0, c);
-          load_n<T, V, true, false>(p.cache, row + half + i0, sn);
+          *reinterpret_cast<u32x4 *>(dst) = ld16<false>(src);
+          *reinterpret_cast<u32x4 *>(dst + half) = ld16<false>(src + half);
         } else {
-          load_n<T, V, false, false>(p.cache, row + i0, c);
-          load_n<T, V, false, false>(p.cache, row + half + i0, sn);
+#pragma unroll 1
+          for (int j = 0; j < V; ++j) {
+            reinterpret_cast<R *>(dst)[j] = reinterpret_cast<const R *>(src)[j];
+            reinterpret_cast<R *>(dst + half)[j] = reinterpret_cast<const R *>(src + half)[j];
+          }
         }
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          dst[j] = c[j];
-          dst[half + j] = sn[j];
-        }
-      } else {
-#pragma unroll
+      } else {  // rare: kept rolled so it does not raise the kernel's register count
+#pragma unroll 1
         for (int j = 0; j < V; ++j) {
           const int sec = mrope_section_of(p, i0 + j);
           const int64_t row = clamp_position(p, p.positions[sec * p.pos_stride_row + tok]) *
                               p.cache_stride;
-          dst[j] = Io<T>::load1(p.cache, row + i0 + j);
-          dst[half + j] = Io<T>::load1(p.cache, row + half + i0 + j);
+          const R *src = static_cast<const R *>(p.cache) + row + i0 + j;
+          reinterpret_cast<R *>(dst)[j] = src[0];
+          reinterpret_cast<R *>(dst + half)[j] = src[half];
         }
       }
     }
@@ -726,7 +754,8 @@ ROPE_API int rope_with_cos_sin_cache(const rope_tensor *positions, const rope_te
   const void *fn = plan.dt == ROPE_F32   ? pick_cache<float>(plan.neox, plan.vector_io)
                    : plan.dt == ROPE_F16 ? pick_cache<_Float16>(plan.neox, plan.vector_io)
                                          : pick_cache<__bf16>(plan.neox, plan.vector_io);
-  const size_t lds = size_t(plan.tile_tokens) * size_t(plan.rd) * sizeof(float);
+  const size_t esize = plan.dt == ROPE_F32 ? 4 : 2;
+  const size_t lds = size_t(plan.tile_tokens) * size_t(plan.rd) * esize;
   return launch(fn, plan.tiles, kCacheBlock, lds, stream, &plan);
 }
 
