@@ -8,6 +8,8 @@
  *   rope_partial_inplace_backward  its gradient with respect to x, in place on the gradient
  *   rope_with_cos_sin_cache        RoPE of query/key rows with cos/sin gathered from a cache by
  *                                  position; rope or mrope mode; GPT-NeoX or GPT-J style
+ *   rope_with_cos_sin_cache_v2     the same with the cacheMode argument (sectioned or
+ *                                  interleaved mrope stitching)
  *
  * Pages defining the operations:
  *   [IPRM] "CANN ops-transformer 的 aclnnInplacePartialRotaryMul 算子：Inplace 部分旋转位置编码
@@ -160,6 +162,27 @@ int rope_with_cos_sin_cache(const rope_tensor *positions, const rope_tensor *que
                             int64_t head_size, int is_neox_style,
                             const rope_tensor *query_out, const rope_tensor *key_out,
                             void *stream);
+
+/*
+ * rope_with_cos_sin_cache_v2 -- rope_with_cos_sin_cache with the cacheMode argument
+ * ([RSCC §V2 接口：cacheMode 扩展]), which picks how mrope stitches cos/sin from the position
+ * rows:
+ *   cache_mode 0  sectioned: element i comes from the row whose section holds i (exactly
+ *                 rope_with_cos_sin_cache, which is this call with cache_mode 0);
+ *   cache_mode 1  interleaved, 3-section lists only: every element starts from row 0; then
+ *                 the elements i < 3*mropeSection[1] with i % 3 == 1 come from row 1 and
+ *                 those with i % 3 == 2 from row 2 (index i in [0, rotaryDim/2), the same
+ *                 for the cos and the sin half).
+ * cache_mode must be 0 or 1, and 0 with the list {16,16,16,16}; anything else gives
+ * ROPE_ERR_PARAM_INVALID (checked in rope mode too, where the value changes nothing).
+ * Every other argument, layout and rule is that of rope_with_cos_sin_cache.
+ */
+int rope_with_cos_sin_cache_v2(const rope_tensor *positions, const rope_tensor *query_in,
+                               const rope_tensor *key_in, const rope_tensor *cos_sin_cache,
+                               const int64_t *mrope_section, int64_t mrope_section_len,
+                               int64_t head_size, int is_neox_style, int64_t cache_mode,
+                               const rope_tensor *query_out, const rope_tensor *key_out,
+                               void *stream);
 
 /* Text describing the last failing call on the calling thread ("" if none).  The pointer
  * stays valid until the next call on this thread. */

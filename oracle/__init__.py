@@ -53,6 +53,11 @@ def _load():
         P(ctypes.c_int64), ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
         P(OroTensor), P(OroTensor), P(ctypes.c_double), P(ctypes.c_double)]
     lib.oro_rope_with_cos_sin_cache.restype = ctypes.c_int
+    lib.oro_rope_with_cos_sin_cache_v2.argtypes = [
+        P(OroTensor), P(OroTensor), P(OroTensor), P(OroTensor),
+        P(ctypes.c_int64), ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
+        P(OroTensor), P(OroTensor), P(ctypes.c_double), P(ctypes.c_double)]
+    lib.oro_rope_with_cos_sin_cache_v2.restype = ctypes.c_int
     lib.oro_last_error.restype = ctypes.c_char_p
     for name in ("oro_round_bf16_array", "oro_round_f16_array"):
         getattr(lib, name).argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
@@ -152,8 +157,9 @@ def rope_partial_inplace_backward(g, cos, sin, rotary_mode=1, partial_slice=None
 
 def rope_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,
                             head_size, is_neox_style, query_out, key_out, *, twin=False,
-                            raw_desc=None):
+                            raw_desc=None, cache_mode=None):
     """Operation B on host tensors, writing ``query_out``/``key_out`` ([RSCC §设计动机]).
+    ``cache_mode`` (not None) calls the V2 form ([RSCC §V2 接口：cacheMode 扩展]).
 
     Returns ``(status, q64, k64)`` where the float64 twins have the output shapes.
     """
@@ -171,9 +177,15 @@ def rope_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_se
     else:
         descs = [_desc(t) for t in (positions, query_in, key_in, cos_sin_cache,
                                     query_out, key_out)]
-    st = _lib.oro_rope_with_cos_sin_cache(descs[0], descs[1], descs[2], descs[3], ms, ms_len,
-                                          int(head_size), int(bool(is_neox_style)),
-                                          descs[4], descs[5], q64p, k64p)
+    if cache_mode is None:
+        st = _lib.oro_rope_with_cos_sin_cache(descs[0], descs[1], descs[2], descs[3], ms, ms_len,
+                                              int(head_size), int(bool(is_neox_style)),
+                                              descs[4], descs[5], q64p, k64p)
+    else:
+        st = _lib.oro_rope_with_cos_sin_cache_v2(descs[0], descs[1], descs[2], descs[3], ms,
+                                                 ms_len, int(head_size),
+                                                 int(bool(is_neox_style)), int(cache_mode),
+                                                 descs[4], descs[5], q64p, k64p)
     return st, q64, k64
 
 

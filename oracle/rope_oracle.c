@@ -418,12 +418,12 @@ static int same_layout(const oro_tensor *a, const oro_tensor *b) {
   return 1;
 }
 
-int oro_rope_with_cos_sin_cache(const oro_tensor *positions, const oro_tensor *query_in,
-                                const oro_tensor *key_in, const oro_tensor *cache,
-                                const int64_t *mrope_section, int64_t mrope_section_len,
-                                int64_t head_size, int is_neox_style,
-                                const oro_tensor *query_out, const oro_tensor *key_out,
-                                double *q64, double *k64) {
+static int cos_sin_cache(const oro_tensor *positions, const oro_tensor *query_in,
+                         const oro_tensor *key_in, const oro_tensor *cache,
+                         const int64_t *mrope_section, int64_t mrope_section_len,
+                         int64_t head_size, int is_neox_style, int64_t cache_mode,
+                         const oro_tensor *query_out, const oro_tensor *key_out, double *q64,
+                         double *k64) {
   const oro_tensor *all[6] = {positions, query_in, key_in, cache, query_out, key_out};
   for (int i = 0; i < 6; ++i)
     if (!all[i]) return fail(ORO_ERR_PARAM_NULLPTR, "a tensor argument is null");
@@ -486,6 +486,13 @@ int oro_rope_with_cos_sin_cache(const oro_tensor *positions, const oro_tensor *q
     }
   }
 
+  /* cacheMode ([RSCC §V2 接口：cacheMode 扩展]): 0 sectioned, 1 interleaved; the 4-section list
+   * allows 0 only.  In rope mode the value has no effect. */
+  if (cache_mode != 0 && cache_mode != 1)
+    return fail(ORO_ERR_PARAM_INVALID, "cacheMode must be 0 or 1");
+  if (mrope && cache_mode == 1 && nsec == 4)
+    return fail(ORO_ERR_PARAM_INVALID, "cacheMode 1 needs a 3-section mropeSection");
+
   /* headSize and rotaryDim: 64-byte multiples, rotaryDim <= headSize */
   const int es = elem_size(query_in->dtype);
   const int64_t align = 64 / es;
@@ -546,12 +553,20 @@ int oro_rope_with_cos_sin_cache(const oro_tensor *positions, const oro_tensor *q
      * sections: element i of cos/sin comes from the position row whose section holds i */
     for (int64_t i = 0; i < half; ++i) {
       int64_t row_sel = 0;
-      if (mrope) {
+      if (mrope && cache_mode == 0) {
+        /* sectioned: element i takes the row of the section that holds it */
         int64_t acc = 0;
         for (int64_t k = 0; k < nsec; ++k) {
           acc += sec[k];
           if (i < acc) { row_sel = k; break; }
         }
+      } else if (mrope) {
+        /* interleaved ([RSCC §V2 接口：cacheMode 扩展]): start from row 0, then the elements
+         * 1, 4, 7, ... below 3*mropeSection[1] come from row 1 and 2, 5, 8, ... below the same
+         * bound from row 2 (the bound printed for both; for every accepted list it selects the
+         * same elements as 3*mropeSection[2] would, the slices ending at rotaryDim/2) */
+        if (i % 3 == 1 && i < 3 * sec[1]) row_sel = 1;
+        else if (i % 3 == 2 && i < 3 * sec[1]) row_sel = 2;
       }
       int64_t p = mrope ? load_i64(positions, row_sel * positions->stride[0] + t * positions->stride[1])
                         : load_i64(positions, t * positions->stride[0]);
@@ -594,4 +609,26 @@ int oro_rope_with_cos_sin_cache(const oro_tensor *positions, const oro_tensor *q
     }
   }
   return ORO_OK;
+}
+
+int oro_rope_with_cos_sin_cache(const oro_tensor *positions, const oro_tensor *query_in,
+                                const oro_tensor *key_in, const oro_tensor *cache,
+                                const int64_t *mrope_section, int64_t mrope_section_len,
+                                int64_t head_size, int is_neox_style,
+                                const oro_tensor *query_out, const oro_tensor *key_out,
+                                double *q64, double *k64) {
+  return cos_sin_cache(positions, query_in, key_in, cache, mrope_section, mrope_section_len,
+                       head_size, is_neox_style, 0, query_out, key_out, q64, k64);
+}
+
+/* The V2 form with the cacheMode argument ([RSCC §V2 接口：cacheMode 扩展]); cacheMode 0 is the
+ * call above. */
+int oro_rope_with_cos_sin_cache_v2(const oro_tensor *positions, const oro_tensor *query_in,
+                                   const oro_tensor *key_in, const oro_tensor *cache,
+                                   const int64_t *mrope_section, int64_t mrope_section_len,
+                                   int64_t head_size, int is_neox_style, int64_t cache_mode,
+                                   const oro_tensor *query_out, const oro_tensor *key_out,
+                                   double *q64, double *k64) {
+  return cos_sin_cache(positions, query_in, key_in, cache, mrope_section, mrope_section_len,
+                       head_size, is_neox_style, cache_mode, query_out, key_out, q64, k64);
 }

@@ -10,6 +10,7 @@ streams.  There is no fallback: if the library is not built this import fails.
   InplacePartialRotaryMul.apply(x, cos, sin, partial_slice)   (autograd; x must not be a leaf)
   rope_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,
                           head_size, is_neox_style, query_out=None, key_out=None, stream=None)
+  rope_with_cos_sin_cache_v2(..., is_neox_style, cache_mode, query_out=None, ...)
 
 Pages defining the operations:
   [IPRM] "CANN ops-transformer 的 aclnnInplacePartialRotaryMul 算子：Inplace 部分旋转位置编码接口详解与实现剖析"
@@ -65,6 +66,11 @@ def _load() -> ctypes.CDLL:
                                             ctypes.c_int64, ctypes.c_int, P(RopeTensor),
                                             P(RopeTensor), ctypes.c_void_p]
     lib.rope_with_cos_sin_cache.restype = ctypes.c_int
+    lib.rope_with_cos_sin_cache_v2.argtypes = [P(RopeTensor), P(RopeTensor), P(RopeTensor),
+                                               P(RopeTensor), P(ctypes.c_int64), ctypes.c_int64,
+                                               ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
+                                               P(RopeTensor), P(RopeTensor), ctypes.c_void_p]
+    lib.rope_with_cos_sin_cache_v2.restype = ctypes.c_int
     lib.rope_last_error.argtypes = []
     lib.rope_last_error.restype = ctypes.c_char_p
     return lib
@@ -188,13 +194,24 @@ def __getattr__(name):
     raise AttributeError(name)
 
 
-def rope_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section=None,
-                            head_size: int | None = None, is_neox_style: bool = True,
-                            query_out=None, key_out=None, stream=None):
-    """RoPE with a cos/sin cache ([RSCC §设计动机]); returns (query_out, key_out).
+def _cache_args(positions, query_in, key_in, cos_sin_cache, mrope_section, head_size,
+                is_neox_style, cache_mode, query_out, key_out, stream):
+    """(C function, its arguments, objects to keep alive) of one cos/sin-cache call: the V1
+    entry point when cache_mode is None, else the V2 one."""
+    tensors = (positions, query_in, key_in, cos_sin_cache, query_out, key_out)
+    dev = _device_of(list(tensors))
+    descs = [describe(t) for t in tensors]
+    ms, ms_len = _int_array(mrope_section)
+    head = (ctypes.byref(descs[0]), ctypes.byref(descs[1]), ctypes.byref(descs[2]),
+            ctypes.byref(descs[3]), ms, ms_len, int(head_size), int(bool(is_neox_style)))
+    tail = (ctypes.byref(descs[4]), ctypes.byref(descs[5]), _stream_handle(stream, dev))
+    if cache_mode is None:
+        return LIB.rope_with_cos_sin_cache, head + tail, (tensors, descs, ms)
+    return LIB.rope_with_cos_sin_cache_v2, head + (int(cache_mode),) + tail, (tensors, descs, ms)
 
-    Outputs are allocated (contiguous) when not given; ``head_size`` defaults to the cache's
-    rotaryDim."""
+
+def _with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section, head_size,
+                        is_neox_style, cache_mode, query_out, key_out, stream):
     import torch
     if head_size is None:
         head_size = cos_sin_cache.shape[-1]
@@ -202,16 +219,32 @@ def rope_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_se
         query_out = torch.empty(query_in.shape, dtype=query_in.dtype, device=query_in.device)
     if key_out is None:
         key_out = torch.empty(key_in.shape, dtype=key_in.dtype, device=key_in.device)
-    dev = _device_of([positions, query_in, key_in, cos_sin_cache, query_out, key_out])
-    descs = [describe(t) for t in (positions, query_in, key_in, cos_sin_cache, query_out,
-                                   key_out)]
-    ms, ms_len = _int_array(mrope_section)
-    _check(LIB.rope_with_cos_sin_cache(ctypes.byref(descs[0]), ctypes.byref(descs[1]),
-                                       ctypes.byref(descs[2]), ctypes.byref(descs[3]), ms,
-                                       ms_len, int(head_size), int(bool(is_neox_style)),
-                                       ctypes.byref(descs[4]), ctypes.byref(descs[5]),
-                                       _stream_handle(stream, dev)))
+    fn, args, _keep = _cache_args(positions, query_in, key_in, cos_sin_cache, mrope_section,
+                                  head_size, is_neox_style, cache_mode, query_out, key_out,
+                                  stream)
+    _check(fn(*args))
     return query_out, key_out
+
+
+def rope_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section=None,
+                            head_size: int | None = None, is_neox_style: bool = True,
+                            query_out=None, key_out=None, stream=None):
+    """RoPE with a cos/sin cache ([RSCC §设计动机]); returns (query_out, key_out).
+
+    Outputs are allocated (contiguous) when not given; ``head_size`` defaults to the cache's
+    rotaryDim."""
+    return _with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,
+                               head_size, is_neox_style, None, query_out, key_out, stream)
+
+
+def rope_with_cos_sin_cache_v2(positions, query_in, key_in, cos_sin_cache, mrope_section=None,
+                               head_size: int | None = None, is_neox_style: bool = True,
+                               cache_mode: int = 0, query_out=None, key_out=None, stream=None):
+    """The V2 form with ``cache_mode`` ([RSCC §V2 接口：cacheMode 扩展]): 0 sectioned,
+    1 interleaved mrope stitching.  Other arguments as rope_with_cos_sin_cache."""
+    return _with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,
+                               head_size, is_neox_style, int(cache_mode), query_out, key_out,
+                               stream)
 
 
 class PreparedCall:
@@ -238,13 +271,10 @@ def prepare_partial_inplace(x, cos, sin, rotary_mode: int = 1, partial_slice=Non
 
 
 def prepare_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,
-                               head_size, is_neox_style, query_out, key_out,
-                               stream=None) -> PreparedCall:
-    tensors = (positions, query_in, key_in, cos_sin_cache, query_out, key_out)
-    dev = _device_of(list(tensors))
-    descs = [describe(t) for t in tensors]
-    ms, ms_len = _int_array(mrope_section)
-    args = (ctypes.byref(descs[0]), ctypes.byref(descs[1]), ctypes.byref(descs[2]),
-            ctypes.byref(descs[3]), ms, ms_len, int(head_size), int(bool(is_neox_style)),
-            ctypes.byref(descs[4]), ctypes.byref(descs[5]), _stream_handle(stream, dev))
-    return PreparedCall(LIB.rope_with_cos_sin_cache, args, (tensors, descs, ms))
+                               head_size, is_neox_style, query_out, key_out, stream=None,
+                               cache_mode: int | None = None) -> PreparedCall:
+    """cache_mode None: the V1 entry point; else the V2 one with that cacheMode."""
+    fn, args, keep = _cache_args(positions, query_in, key_in, cos_sin_cache, mrope_section,
+                                 head_size, is_neox_style, cache_mode, query_out, key_out,
+                                 stream)
+    return PreparedCall(fn, args, keep)

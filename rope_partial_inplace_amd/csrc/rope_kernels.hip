@@ -152,7 +152,6 @@ __device__ inline void st16(void *p, u32x4 v) {
 }
 
 __device__ inline uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
-__device__ inline u32x4 from_uint4(uint4 v) { return u32x4{v.x, v.y, v.z, v.w}; }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -400,6 +399,18 @@ __device__ inline int mrope_section_of(const CachePlan &p, int64_t i) {
   return sec;
 }
 
+// The position row that element i (< rotaryDim/2) of the stitched cos/sin takes.  Sectioned
+// (cacheMode 0): the section holding i.  Interleaved (cacheMode 1, three sections,
+// [RSCC §V2 接口：cacheMode 扩展]): below 3 * mropeSection[1], elements with i % 3 == 1 come
+// from row 1 and those with i % 3 == 2 from row 2; every other element from row 0.
+__device__ inline int cs_row_of(const CachePlan &p, uint32_t i) {
+  if (p.interleaved) {
+    const uint32_t r = i % 3u;
+    return (int32_t(i) < p.interleave_end && r != 0) ? int(r) : 0;
+  }
+  return mrope_section_of(p, i);
+}
+
 // Positions outside [0, maxSeqLen) break the contract; clamping keeps every read inside the
 // cache.
 __device__ inline int64_t clamp_position(const CachePlan &p, int64_t pos) {
@@ -559,7 +570,53 @@ __device__ inline void cache_store_pass(const CachePlan &p, int64_t t0, const T 
   }
 }
 
-template <typename T, bool NEOX, bool VEC, int K>
+// Stages one V-element chunk (elements i0 .. i0+V-1 of the cos half, and the same of the sin
+// half) of a token whose stitched cos/sin draws on several position rows (interleaved
+// stitching, or a section boundary inside the chunk; three rows at most).  The chunk of every
+// row it needs is loaded as whole 16-byte vectors, then each element is taken from its row.
+template <typename T, int V>
+__device__ inline void stage_multi_row(const CachePlan &p, int64_t tok, uint32_t i0, int64_t half,
+                                       T *dst) {
+  using R = typename Io<T>::raw;
+  union Chunk {
+    u32x4 v;
+    R e[V];
+  };
+  int row[V];
+  bool need[3] = {false, false, false};
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    row[j] = cs_row_of(p, i0 + uint32_t(j));
+    need[0] |= row[j] == 0;
+    need[1] |= row[j] == 1;
+    need[2] |= row[j] == 2;
+  }
+  int64_t pos[3] = {0, 0, 0};
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+    if (need[r]) pos[r] = p.positions[r * p.pos_stride_row + tok];
+  Chunk c[3], s[3];
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    if (!need[r]) continue;
+    const T *src = static_cast<const T *>(p.cache) + clamp_position(p, pos[r]) * p.cache_stride + i0;
+    c[r].v = ld16<false>(src);
+    s[r].v = ld16<false>(src + half);
+  }
+  Chunk co, so;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int r = row[j];
+    co.e[j] = r == 0 ? c[0].e[j] : r == 1 ? c[1].e[j] : c[2].e[j];
+    so.e[j] = r == 0 ? s[0].e[j] : r == 1 ? s[1].e[j] : s[2].e[j];
+  }
+  *reinterpret_cast<u32x4 *>(dst) = co.v;
+  *reinterpret_cast<u32x4 *>(dst + half) = so.v;
+}
+
+// MULTI: the plan's stitched cos/sin has chunks drawing on several position rows
+// (CachePlan::multi_row); otherwise every staging chunk comes from one row.
+template <typename T, bool NEOX, bool VEC, int K, bool MULTI>
 __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p) {
   // [tile_tokens][rd] elements of T: the gathered cos (rd/2) then sin (rd/2) of each token
   extern __shared__ u32x4 cs_lds[];
@@ -578,7 +635,7 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
     // chain runs while the q/k data is in flight.
     const uint32_t stage_items = uint32_t(ntok) * p.stage_chunks;
     int64_t first_pos = 0;
-    if (threadIdx.x < stage_items) {
+    if (!MULTI && threadIdx.x < stage_items) {
       const uint32_t tl = fdiv(p.div_stage, threadIdx.x);
       const int64_t i0 = int64_t(threadIdx.x - tl * p.stage_chunks) * V;
       const int sec = p.mrope ? mrope_section_of(p, i0) : 0;
@@ -590,42 +647,36 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
 
     // ---- stage the tile's cos|sin rows in LDS (steps 1-2: gather, split, stitch) ----
     // One lane per V-element chunk of a token's cos half (and the matching sin chunk).  A
-    // chunk inside one mrope section (always, in rope mode) is copied from one cache row as
-    // 16-byte vectors; a chunk split by a section boundary is gathered element by element.
-    // Values stay in the cache's element type (bits copied, raised to float32 at use).
+    // chunk drawn from one position row (always, in rope mode) is copied as 16-byte vectors;
+    // chunks of a multi-row plan go through stage_multi_row.  An unaligned cache is gathered
+    // element by element.  Values stay in the cache's element type (bits copied, raised to
+    // float32 at use).
     for (uint32_t idx = threadIdx.x; idx < stage_items; idx += kCacheBlock) {
       const uint32_t tl = fdiv(p.div_stage, idx);
-      const int64_t i0 = int64_t(idx - tl * p.stage_chunks) * V;
+      const uint32_t i0 = (idx - tl * p.stage_chunks) * uint32_t(V);
       const int64_t tok = (t0 + tl) * p.pos_stride_tok;
-      const int s_lo = p.mrope ? mrope_section_of(p, i0) : 0;
-      const int s_hi = p.mrope ? mrope_section_of(p, i0 + V - 1) : 0;
       T *dst = cs_tile + int64_t(tl) * rd + i0;
       using R = typename Io<T>::raw;
-      if (s_lo == s_hi) {
-        const int64_t pos =
-            idx == threadIdx.x ? first_pos : p.positions[s_lo * p.pos_stride_row + tok];
-        const int64_t row = clamp_position(p, pos) * p.cache_stride;
-        const T *src = static_cast<const T *>(p.cache) + row + i0;
-        if (p.cache_vec) {
-          *reinterpret_cast<u32x4 *>(dst) = ld16<false>(src);
-          *reinterpret_cast<u32x4 *>(dst + half) = ld16<false>(src + half);
-        } else {
-#pragma unroll 1
-          for (int j = 0; j < V; ++j) {
-            reinterpret_cast<R *>(dst)[j] = reinterpret_cast<const R *>(src)[j];
-            reinterpret_cast<R *>(dst + half)[j] = reinterpret_cast<const R *>(src + half)[j];
-          }
-        }
-      } else {  // rare: kept rolled so it does not raise the kernel's register count
+      if (!p.cache_vec) {  // rare: kept rolled so it does not raise the register count
 #pragma unroll 1
         for (int j = 0; j < V; ++j) {
-          const int sec = mrope_section_of(p, i0 + j);
-          const int64_t row = clamp_position(p, p.positions[sec * p.pos_stride_row + tok]) *
+          const int r = p.mrope ? cs_row_of(p, i0 + uint32_t(j)) : 0;
+          const int64_t row = clamp_position(p, p.positions[r * p.pos_stride_row + tok]) *
                               p.cache_stride;
           const R *src = static_cast<const R *>(p.cache) + row + i0 + j;
           reinterpret_cast<R *>(dst)[j] = src[0];
           reinterpret_cast<R *>(dst + half)[j] = src[half];
         }
+      } else if constexpr (MULTI) {
+        stage_multi_row<T, V>(p, tok, i0, half, dst);
+      } else {
+        const int sec = p.mrope ? mrope_section_of(p, i0) : 0;
+        const int64_t pos =
+            idx == threadIdx.x ? first_pos : p.positions[sec * p.pos_stride_row + tok];
+        const T *src =
+            static_cast<const T *>(p.cache) + clamp_position(p, pos) * p.cache_stride + i0;
+        *reinterpret_cast<u32x4 *>(dst) = ld16<false>(src);
+        *reinterpret_cast<u32x4 *>(dst + half) = ld16<false>(src + half);
       }
     }
     __syncthreads();
@@ -680,14 +731,20 @@ const void *pick_inplace_dtype(const InplacePlan &p) {
                            : pick_inplace<__bf16, __bf16, BWD>(p.vector_io, p.cos_stream);
 }
 
-template <typename T>
-const void *pick_cache(bool neox, bool vec) {
+template <typename T, bool MULTI>
+const void *pick_cache_rows(bool neox, bool vec) {
   constexpr int KN = kNeoxItemsPerLane, KJ = kGptjItemsPerLane;
   if (neox)
-    return vec ? reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, true, true, KN>)
-               : reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, true, false, KN>);
-  return vec ? reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, false, true, KJ>)
-             : reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, false, false, KJ>);
+    return vec ? reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, true, true, KN, MULTI>)
+               : reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, true, false, KN, MULTI>);
+  return vec ? reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, false, true, KJ, MULTI>)
+             : reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, false, false, KJ, MULTI>);
+}
+
+template <typename T>
+const void *pick_cache(const CachePlan &p) {
+  return p.multi_row ? pick_cache_rows<T, true>(p.neox, p.vector_io)
+                     : pick_cache_rows<T, false>(p.neox, p.vector_io);
 }
 
 }  // namespace
@@ -735,28 +792,40 @@ ROPE_API int rope_partial_inplace_backward(const rope_tensor *g, const rope_tens
   return run_inplace(g, cos, sin, rotary_mode, partial_slice, partial_slice_len, stream, true);
 }
 
+ROPE_API int rope_with_cos_sin_cache_v2(const rope_tensor *positions, const rope_tensor *query_in,
+                                        const rope_tensor *key_in,
+                                        const rope_tensor *cos_sin_cache,
+                                        const int64_t *mrope_section, int64_t mrope_section_len,
+                                        int64_t head_size, int is_neox_style, int64_t cache_mode,
+                                        const rope_tensor *query_out, const rope_tensor *key_out,
+                                        void *stream) {
+  CachePlan plan;
+  std::string err;
+  const int st = plan_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,
+                            mrope_section_len, head_size, is_neox_style, cache_mode, query_out,
+                            key_out, &plan, &err);
+  if (st != ROPE_OK) {
+    g_last_error = err;
+    return st;
+  }
+  g_last_error.clear();
+  const void *fn = plan.dt == ROPE_F32   ? pick_cache<float>(plan)
+                   : plan.dt == ROPE_F16 ? pick_cache<_Float16>(plan)
+                                         : pick_cache<__bf16>(plan);
+  const size_t esize = plan.dt == ROPE_F32 ? 4 : 2;
+  const size_t lds = size_t(plan.tile_tokens) * size_t(plan.rd) * esize;
+  return launch(fn, plan.tiles, kCacheBlock, lds, stream, &plan);
+}
+
 ROPE_API int rope_with_cos_sin_cache(const rope_tensor *positions, const rope_tensor *query_in,
                                      const rope_tensor *key_in, const rope_tensor *cos_sin_cache,
                                      const int64_t *mrope_section, int64_t mrope_section_len,
                                      int64_t head_size, int is_neox_style,
                                      const rope_tensor *query_out, const rope_tensor *key_out,
                                      void *stream) {
-  CachePlan plan;
-  std::string err;
-  const int st = plan_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,
-                            mrope_section_len, head_size, is_neox_style, query_out, key_out,
-                            &plan, &err);
-  if (st != ROPE_OK) {
-    g_last_error = err;
-    return st;
-  }
-  g_last_error.clear();
-  const void *fn = plan.dt == ROPE_F32   ? pick_cache<float>(plan.neox, plan.vector_io)
-                   : plan.dt == ROPE_F16 ? pick_cache<_Float16>(plan.neox, plan.vector_io)
-                                         : pick_cache<__bf16>(plan.neox, plan.vector_io);
-  const size_t esize = plan.dt == ROPE_F32 ? 4 : 2;
-  const size_t lds = size_t(plan.tile_tokens) * size_t(plan.rd) * esize;
-  return launch(fn, plan.tiles, kCacheBlock, lds, stream, &plan);
+  return rope_with_cos_sin_cache_v2(positions, query_in, key_in, cos_sin_cache, mrope_section,
+                                    mrope_section_len, head_size, is_neox_style, 0, query_out,
+                                    key_out, stream);
 }
 
 ROPE_API const char *rope_last_error(void) { return g_last_error.c_str(); }

@@ -191,8 +191,8 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
 int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
                const rope_tensor *key_in, const rope_tensor *cache,
                const int64_t *mrope_section, int64_t mrope_section_len, int64_t head_size,
-               int is_neox_style, const rope_tensor *query_out, const rope_tensor *key_out,
-               CachePlan *plan, std::string *err) {
+               int is_neox_style, int64_t cache_mode, const rope_tensor *query_out,
+               const rope_tensor *key_out, CachePlan *plan, std::string *err) {
   *plan = CachePlan();
   const rope_tensor *all[6] = {positions, query_in, key_in, cache, query_out, key_out};
   for (const rope_tensor *t : all)
@@ -255,6 +255,13 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
       for (int i = 0; i < nsec; ++i) sec[i] = mrope_section[i];
     }
   }
+
+  // cacheMode ([RSCC §V2 接口：cacheMode 扩展]): 0 sectioned, 1 interleaved; the 4-section
+  // list allows 0 only; in rope mode the value has no effect.
+  if (cache_mode != 0 && cache_mode != 1)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "cacheMode must be 0 or 1");
+  if (mrope && cache_mode == 1 && nsec == 4)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "cacheMode 1 needs a 3-section mropeSection");
 
   const int es = bytes_of(dt);
   const int64_t align_elems = 64 / es;
@@ -371,6 +378,18 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
   p.cache_vec = aligned16(p.cache) && (p.cache_stride * es) % 16 == 0;
   p.stage_chunks = uint32_t((rd / 2) / p.vec);  // rd/2 is a 32-byte multiple
   p.div_stage = make_fastdiv(p.stage_chunks);
+  // Interleaved stitching: element i of cos/sin takes row 1 if i % 3 == 1 and row 2 if
+  // i % 3 == 2, below 3 * mropeSection[1] (the bound printed for both rows; for every accepted
+  // list it selects the same elements as 3 * mropeSection[2], the slices ending at rd/2).
+  p.interleaved = mrope && cache_mode == 1;
+  p.interleave_end = p.interleaved ? int32_t(3 * sec[1]) : 0;
+  bool split = false;
+  for (int i = 0; i + 1 < nsec; ++i) split |= (p.sec_end[i] % int32_t(p.vec)) != 0;
+  p.multi_row = p.interleaved || (mrope && split);
+  // The multi-row staging reads rows 0..2; only the 3-section lists get there (the 4-section
+  // list has its boundaries on vector edges and allows cacheMode 0 only).
+  if (p.multi_row && nsec != 3)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "mropeSection layout not supported");
   return ROPE_OK;
 }
 

@@ -67,6 +67,9 @@ struct CachePlan {
   rope_dtype dt = ROPE_F32;
   bool neox = true;
   bool mrope = false;
+  bool interleaved = false;  // cacheMode 1: rows 1 and 2 take the elements 1, 4, ... / 2, 5, ...
+  bool multi_row = false;    // some staging chunk draws on more than one position row
+  int32_t interleave_end = 0;  // 3 * mropeSection[1]: end of the interleaved elements
   bool vector_io = false;
   const int64_t *positions = nullptr;
   const void *q_in = nullptr, *k_in = nullptr, *cache = nullptr;
@@ -94,8 +97,8 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
 int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
                const rope_tensor *key_in, const rope_tensor *cos_sin_cache,
                const int64_t *mrope_section, int64_t mrope_section_len, int64_t head_size,
-               int is_neox_style, const rope_tensor *query_out, const rope_tensor *key_out,
-               CachePlan *plan, std::string *err);
+               int is_neox_style, int64_t cache_mode, const rope_tensor *query_out,
+               const rope_tensor *key_out, CachePlan *plan, std::string *err);
 
 // Workgroup size and the work units (16-byte chunks / two-vector units) a lane carries per
 // pass.  Few units per lane and many waves keep more independent HBM requests in flight on

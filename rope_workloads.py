@@ -129,6 +129,7 @@ class CacheCase:
     is_neox: bool
     tokens: int
     algo_bytes: int
+    cache_mode: int | None = None  # None: the V1 call; 0/1: the V2 call with that cacheMode
 
 
 def cache_algo_bytes(T, nq, nk, H, rd, es, npos_rows):
@@ -137,7 +138,7 @@ def cache_algo_bytes(T, nq, nk, H, rd, es, npos_rows):
 
 
 def cache_case(name, T, nq, nk, H, rd, dtype, is_neox, max_seq, seed, mrope_section=None,
-               positions=None, device="cpu"):
+               positions=None, device="cpu", cache_mode=None):
     g = generator(seed, device)
     q = randn((T, nq * H), dtype, g)
     k = randn((T, nk * H), dtype, g)
@@ -150,7 +151,7 @@ def cache_case(name, T, nq, nk, H, rd, dtype, is_neox, max_seq, seed, mrope_sect
     nrows = 1 if positions.dim() == 1 else positions.shape[0]
     es = q.element_size()
     return CacheCase(name, positions, q, k, cache, mrope_section, H, is_neox, T,
-                     cache_algo_bytes(T, nq, nk, H, rd, es, nrows))
+                     cache_algo_bytes(T, nq, nk, H, rd, es, nrows), cache_mode)
 
 
 def mrope_positions(T_text: int, frames: int, grid_h: int, grid_w: int, m: int = 3):

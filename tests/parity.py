@@ -109,15 +109,20 @@ def cache_scale(x: torch.Tensor, cos_t: np.ndarray, sin_t: np.ndarray, H: int, r
     return out.reshape(x.shape[0], -1)
 
 
-def gathered_tables(cache: torch.Tensor, positions: torch.Tensor, mrope_section):
+def gathered_tables(cache: torch.Tensor, positions: torch.Tensor, mrope_section,
+                    cache_mode: int = 0):
     """Per-token cos/sin tables in float64 (for the f32 scale only)."""
     C = as_f64(cache)
     P = positions.detach().cpu().numpy()
     rd = C.shape[1]
     if not mrope_section or mrope_section[0] <= 0:
         return C[P, : rd // 2], C[P, rd // 2:]
-    edges = np.cumsum(mrope_section)
-    sec = np.searchsorted(edges, np.arange(rd // 2), side="right")
+    if cache_mode == 1:
+        i = np.arange(rd // 2)
+        sec = np.where(i < 3 * mrope_section[1], i % 3, 0)
+    else:
+        edges = np.cumsum(mrope_section)
+        sec = np.searchsorted(edges, np.arange(rd // 2), side="right")
     rows = P[sec, :].T                                        # [T, rd/2]
     idx = np.arange(rd // 2)[None, :]
     return C[rows, idx], C[rows, rd // 2 + idx]

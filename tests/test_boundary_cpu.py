@@ -175,16 +175,23 @@ def cache_base(T=4, nq=2, nk=1, H=64, rd=32, dt=torch.bfloat16, m=0):
             "msec": None, "H": H, "neox": 1}
 
 
-def call_cache(a, msec_len=None):
+def call_cache(a, msec_len=None, cache_mode=None):
+    """Statuses of the library and of the oracle on the same arguments: the V1 entry points,
+    or the V2 ones when cache_mode is given."""
     arr, n = ints(a["msec"])
     if msec_len is not None:
         n = msec_len
     order = ["pos", "q", "k", "cache"]
-    lib_st = ra.LIB.rope_with_cos_sin_cache(*[lib_desc(a[k]) for k in order], arr, n, a["H"],
-                                            a["neox"], lib_desc(a["qo"]), lib_desc(a["ko"]), None)
-    ora_st = oracle._lib.oro_rope_with_cos_sin_cache(*[oro_desc(a[k]) for k in order], arr, n,
-                                                     a["H"], a["neox"], oro_desc(a["qo"]),
-                                                     oro_desc(a["ko"]), None, None)
+    lib_in = [lib_desc(a[k]) for k in order] + [arr, n, a["H"], a["neox"]]
+    lib_out = [lib_desc(a["qo"]), lib_desc(a["ko"]), None]
+    ora_in = [oro_desc(a[k]) for k in order] + [arr, n, a["H"], a["neox"]]
+    ora_out = [oro_desc(a["qo"]), oro_desc(a["ko"]), None, None]
+    if cache_mode is None:
+        lib_st = ra.LIB.rope_with_cos_sin_cache(*lib_in, *lib_out)
+        ora_st = oracle._lib.oro_rope_with_cos_sin_cache(*ora_in, *ora_out)
+    else:
+        lib_st = ra.LIB.rope_with_cos_sin_cache_v2(*lib_in, cache_mode, *lib_out)
+        ora_st = oracle._lib.oro_rope_with_cos_sin_cache_v2(*ora_in, cache_mode, *ora_out)
     return lib_st, ora_st
 
 
@@ -256,16 +263,59 @@ CACHE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("cache_mode", [None, 0, 1], ids=["v1", "v2_mode0", "v2_mode1"])
 @pytest.mark.parametrize("name,build,expected", CACHE_CASES, ids=[c[0] for c in CACHE_CASES])
-def test_cache_validation(name, build, expected):
+def test_cache_validation(name, build, expected, cache_mode):
     built = build(cache_base())
     if isinstance(built, tuple):
-        lib_st, ora_st = call_cache(built[0], msec_len=built[1])
+        lib_st, ora_st = call_cache(built[0], msec_len=built[1], cache_mode=cache_mode)
     else:
-        lib_st, ora_st = call_cache(built)
+        lib_st, ora_st = call_cache(built, cache_mode=cache_mode)
     assert lib_st == expected, ra.last_error()
     assert ora_st == expected, oracle.last_error()
     assert ra.last_error() != ""
+
+
+def mrope_base(msec, rd):
+    a = cache_base(H=rd, rd=rd, m=len(msec))
+    return upd(a, msec=msec)
+
+
+# cacheMode rules of [RSCC §V2 接口：cacheMode 扩展]: 0 or 1 only, and 0 only with the
+# 4-section list; the check applies in rope mode too.
+V2_REFUSED = [
+    ("rope mode, cacheMode 2", lambda: cache_base(), 2),
+    ("rope mode, cacheMode -1", lambda: cache_base(), -1),
+    ("mrope [16,24,24], cacheMode 2", lambda: mrope_base([16, 24, 24], 128), 2),
+    ("mrope [16,16,16,16], cacheMode 1", lambda: mrope_base([16, 16, 16, 16], 128), 1),
+    ("mrope [11,11,10], cacheMode 3", lambda: mrope_base([11, 11, 10], 64), 3),
+]
+
+
+@pytest.mark.parametrize("name,build,mode", V2_REFUSED, ids=[c[0] for c in V2_REFUSED])
+def test_cache_mode_refused(name, build, mode):
+    assert call_cache(build(), cache_mode=mode) == (INVALID, INVALID), ra.last_error()
+    assert ra.last_error() != ""
+
+
+V2_ACCEPTED = [
+    ("rope mode, cacheMode 1", lambda: cache_base(), 1),
+    ("mrope [16,16,16,16], cacheMode 0", lambda: mrope_base([16, 16, 16, 16], 128), 0),
+    ("mrope [16,24,24], cacheMode 1", lambda: mrope_base([16, 24, 24], 128), 1),
+    ("mrope [8,12,12], cacheMode 1", lambda: mrope_base([8, 12, 12], 64), 1),
+    ("mrope [24,20,20], cacheMode 1", lambda: mrope_base([24, 20, 20], 128), 1),
+    ("mrope [11,11,10], cacheMode 1", lambda: mrope_base([11, 11, 10], 64), 1),
+]
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU error path")
+@pytest.mark.parametrize("name,build,mode", V2_ACCEPTED, ids=[c[0] for c in V2_ACCEPTED])
+def test_cache_mode_accepted(name, build, mode):
+    """Accepted by both: the oracle computes, the library gets past validation to the launch
+    (which fails without a GPU, so no host pointer reaches a kernel)."""
+    lib_st, ora_st = call_cache(build(), cache_mode=mode)
+    assert ora_st == 0, oracle.last_error()
+    assert lib_st == ra.ROPE_ERR_RUNTIME and "launch" in ra.last_error()
 
 
 def test_mrope_bad_positions_shape():

@@ -154,20 +154,20 @@ def test_inplace_deterministic_and_stream():
 # cache op
 # ------------------------------------------------------------------------------------------
 
-def oracle_cache(pos, q, k, cache, msec, H, neox):
+def oracle_cache(pos, q, k, cache, msec, H, neox, cache_mode=None):
     qo = torch.empty(q.shape, dtype=q.dtype)
     ko = torch.empty(k.shape, dtype=k.dtype)
     st, q64, k64 = oracle.rope_with_cos_sin_cache(pos, q, k, cache, msec, H, neox, qo, ko,
-                                                  twin=True)
+                                                  twin=True, cache_mode=cache_mode)
     assert st == 0, oracle.last_error()
     return qo, ko, q64, k64
 
 
-def compare_cache(pos, q_in, k_in, cache, msec, H, neox, q_gpu, k_gpu, what):
+def compare_cache(pos, q_in, k_in, cache, msec, H, neox, q_gpu, k_gpu, what, cache_mode=None):
     """All arguments on the host; q_gpu/k_gpu are host copies of the GPU outputs."""
     rd = cache.shape[1]
-    qo, ko, q64, k64 = oracle_cache(pos, q_in, k_in, cache, msec, H, neox)
-    cos_t, sin_t = gathered_tables(cache, pos, msec)
+    qo, ko, q64, k64 = oracle_cache(pos, q_in, k_in, cache, msec, H, neox, cache_mode)
+    cos_t, sin_t = gathered_tables(cache, pos, msec, cache_mode or 0)
     exact = 0
     for name, inp, got, ref, ref64 in (("q", q_in, q_gpu, qo, q64), ("k", k_in, k_gpu, ko, k64)):
         T = inp.shape[0]
@@ -184,10 +184,22 @@ def compare_cache(pos, q_in, k_in, cache, msec, H, neox, q_gpu, k_gpu, what):
 
 
 def run_cache_case(case, **kw):
-    qo, ko = ra.rope_with_cos_sin_cache(case.positions, case.query, case.key, case.cache,
-                                        case.mrope_section, case.head_size, case.is_neox, **kw)
+    if case.cache_mode is None:
+        qo, ko = ra.rope_with_cos_sin_cache(case.positions, case.query, case.key, case.cache,
+                                            case.mrope_section, case.head_size, case.is_neox,
+                                            **kw)
+    else:
+        qo, ko = ra.rope_with_cos_sin_cache_v2(case.positions, case.query, case.key, case.cache,
+                                               case.mrope_section, case.head_size, case.is_neox,
+                                               case.cache_mode, **kw)
     torch.cuda.synchronize()
     return qo, ko
+
+
+def compare_cache_case(case, qo, ko, what=None):
+    compare_cache(case.positions.cpu(), case.query.cpu(), case.key.cpu(), case.cache.cpu(),
+                  case.mrope_section, case.head_size, case.is_neox, qo.cpu(), ko.cpu(),
+                  what or case.name, case.cache_mode)
 
 
 @pytest.mark.parametrize("cfg", ["cache_rope_neox_bf16_t8192", "cache_mrope_neox_bf16_t16384"])
@@ -247,6 +259,65 @@ def test_cache_mrope(sec, neox, dt):
     qo, ko = run_cache_case(case)
     compare_cache(case.positions.cpu(), case.query.cpu(), case.key.cpu(), case.cache.cpu(),
                   sec, H, neox, qo.cpu(), ko.cpu(), f"mrope {sec} {dt} neox={neox}")
+
+
+@pytest.mark.parametrize("neox", [True, False], ids=["neox", "gptj"])
+@pytest.mark.parametrize("sec", [[16, 24, 24], [8, 12, 12], [24, 20, 20], [11, 11, 10]])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("cache_mode", [0, 1], ids=["sectioned", "interleaved"])
+def test_cache_mrope_v2(sec, neox, dt, cache_mode):
+    """The V2 entry point: both stitchings of every 3-section list, on text + image
+    positions whose three rows differ (so each element's source row shows in the result)."""
+    rd = 2 * sum(sec)
+    H = 128 if rd <= 128 else 256
+    if dt == torch.float32 and rd % 16:
+        pytest.skip("rotaryDim must be a 64-byte multiple")
+    pos = W.mrope_positions(200, 3, 12, 10, m=3)
+    T = pos.shape[1]
+    case = W.cache_case("mrope_v2", T, 5, 3, H, rd, dt, neox, 400, seed=rd + 7,
+                        mrope_section=sec, positions=pos, device=DEV, cache_mode=cache_mode)
+    qo, ko = run_cache_case(case)
+    compare_cache_case(case, qo, ko, f"mrope v2 {sec} mode {cache_mode} {dt} neox={neox}")
+
+
+@pytest.mark.parametrize("sec,rd", [([16, 16, 16, 16], 128), (None, 64)])
+def test_cache_v2_mode0_equals_v1(sec, rd):
+    """cacheMode 0 is the V1 call: bit-identical outputs (4-section mrope, rope mode)."""
+    m = len(sec) if sec else 0
+    pos = W.mrope_positions(100, 2, 8, 8, m=m) if m else None
+    case = W.cache_case("v2_vs_v1", 228, 4, 2, 128, rd, torch.bfloat16, True, 300, seed=21,
+                        mrope_section=sec, positions=pos, device=DEV)
+    q1, k1 = run_cache_case(case)
+    q2, k2 = ra.rope_with_cos_sin_cache_v2(case.positions, case.query, case.key, case.cache, sec,
+                                           128, True, 0)
+    torch.cuda.synchronize()
+    check_bits_equal(q1.cpu(), q2.cpu(), "q v1 vs v2 mode 0")
+    check_bits_equal(k1.cpu(), k2.cpu(), "k v1 vs v2 mode 0")
+    if not m:  # rope mode: cacheMode 1 changes nothing
+        q3, k3 = ra.rope_with_cos_sin_cache_v2(case.positions, case.query, case.key, case.cache,
+                                               None, 128, True, 1)
+        torch.cuda.synchronize()
+        check_bits_equal(q1.cpu(), q3.cpu(), "q rope mode, cacheMode 1")
+        check_bits_equal(k1.cpu(), k3.cpu(), "k rope mode, cacheMode 1")
+
+
+def test_cache_v2_interleaved_misaligned_cache_rows():
+    """Interleaved stitching from a cache whose rows are not 16-byte aligned (element
+    staging path)."""
+    sec, rd, H = [8, 12, 12], 64, 128
+    g = W.generator(31, DEV)
+    full = torch.zeros(300, rd + 3, dtype=torch.bfloat16, device=DEV)
+    full[:, 1:1 + rd] = W.cos_sin_cache(300, rd, torch.bfloat16).to(DEV)
+    cache = full[:, 1:1 + rd]                # row stride rd + 3 elements, 2-byte offset
+    pos = W.mrope_positions(60, 2, 6, 5, m=3).to(DEV)
+    T = pos.shape[1]
+    q = W.randn((T, 3 * H), torch.bfloat16, g)
+    k = W.randn((T, H), torch.bfloat16, g)
+    for neox in (True, False):
+        qo, ko = ra.rope_with_cos_sin_cache_v2(pos, q, k, cache, sec, H, neox, 1)
+        torch.cuda.synchronize()
+        compare_cache(pos.cpu(), q.cpu(), k.cpu(), cache.cpu(), sec, H, neox, qo.cpu(), ko.cpu(),
+                      f"interleaved misaligned cache neox={neox}", 1)
 
 
 def test_cache_strided_inputs_and_positions():

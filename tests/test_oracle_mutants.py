@@ -51,6 +51,10 @@ MUTANTS = [
     ("backward sign", "y1 = p1 - q1;", "y1 = p1 + q1;", "backward or twin"),
     ("backward uses forward's sin index", "float q0 = bb * s1;", "float q0 = bb * s0;",
      "backward or twin"),
+    ("interleaved residue", "if (i % 3 == 1 && i < 3 * sec[1]) row_sel = 1;",
+     "if (i % 3 == 2 && i < 3 * sec[1]) row_sel = 1;", "interleaved"),
+    ("interleaved bound", "else if (i % 3 == 2 && i < 3 * sec[1]) row_sel = 2;",
+     "else if (i % 3 == 2 && i < 3 * sec[1] - 3) row_sel = 2;", "interleaved"),
     ("f16 subnormal decode", "v = ldexpf((float)m, -24);", "v = ldexpf((float)m, -23);",
      "decoding"),
 ]

@@ -581,3 +581,98 @@ def test_inplace_fp32_within_bound_of_twin(direction):
         scale[..., 1::2] = np.abs(b * c1) + np.abs(a * s0)
     err = np.abs(f64(y)[..., 4:36] - y64[..., 4:36])
     assert (err <= 2.0 ** -23 * scale * (1 + 1e-6)).all()
+
+
+# ------------------------------------------------------------------------------------------
+# V2 cacheMode = 1: interleaved mrope stitching ([RSCC §V2 接口：cacheMode 扩展])
+# ------------------------------------------------------------------------------------------
+
+def run_cache_v2(pos, q, k, cache, msec, H, neox, mode, twin=False):
+    qo = torch.empty_like(q, memory_format=torch.contiguous_format)
+    ko = torch.empty_like(k, memory_format=torch.contiguous_format)
+    st, q64, k64 = oracle.rope_with_cos_sin_cache(pos, q, k, cache, msec, H, neox, qo, ko,
+                                                  twin=twin, cache_mode=mode)
+    return st, qo, ko, q64, k64
+
+
+@pytest.mark.parametrize("case_i", [0, 1])
+def test_golden_mrope_interleaved(case_i):
+    g = golden("t8_mrope_interleaved.json")
+    cs = g["cases"][case_i]
+    rd = H = cs["rotary_dim"]
+    cache = torch.zeros(4, rd)
+    for p in range(4):
+        cache[p, : rd // 2] = p
+        cache[p, rd // 2:] = 10 * p
+    cache = cache.to(torch.bfloat16)
+    head = torch.zeros(H)
+    head[: rd // 2] = 1.0
+    q = head.reshape(1, H).to(torch.bfloat16)
+    st, qo, _, _, _ = run_cache_v2(torch.tensor(g["positions"]), q, q.clone(), cache,
+                                   cs["mrope_section"], H, True, 1)
+    assert st == 0, oracle.last_error()
+    out = f64(qo).ravel()
+    for i in range(rd // 2):
+        exp = cs["expected_cos_by_index_mod3"][i % 3]
+        if cs["tail_from"] is not None and i >= cs["tail_from"]:
+            exp = cs["expected_cos_by_index_mod3"][0]
+        assert out[i] == exp and out[rd // 2 + i] == 10 * exp, i
+
+
+@pytest.mark.parametrize("neox", [True, False])
+@pytest.mark.parametrize("sec", [[16, 24, 24], [8, 12, 12], [24, 20, 20], [11, 11, 10]])
+def test_interleaved_matches_complex_multiplication(neox, sec):
+    """NumPy: start from row 0's cos/sin, overwrite the slices 1::3 and 2::3 below
+    3*mropeSection[1] from rows 1 and 2, then complex multiplication per pair."""
+    T, H = 29, 128
+    rd = 2 * sum(sec)
+    gen = torch.Generator().manual_seed(26)
+    q = torch.randn(T, 3 * H, generator=gen)
+    k = torch.randn(T, H, generator=gen)
+    cache = torch.randn(40, rd, generator=gen)
+    pos = torch.randint(0, 40, (3, T), generator=gen)
+    st, _, _, q64, k64 = run_cache_v2(pos, q, k, cache, sec, H, neox, 1, twin=True)
+    assert st == 0, oracle.last_error()
+    C = f64(cache)
+    gathered = C[pos.numpy()]                      # [3, T, rd]
+    cos = gathered[0, :, : rd // 2].copy()
+    sin = gathered[0, :, rd // 2:].copy()
+    for r in (1, 2):
+        sl = slice(r, sec[1] * 3, 3)
+        cos[:, sl] = gathered[r, :, : rd // 2][:, sl]
+        sin[:, sl] = gathered[r, :, rd // 2:][:, sl]
+    w = cos + 1j * sin
+    for inp, got in ((q, q64), (k, k64)):
+        X = f64(inp).reshape(T, -1, H)
+        if neox:
+            z = X[..., : rd // 2] + 1j * X[..., rd // 2: rd]
+        else:
+            z = X[..., 0:rd:2] + 1j * X[..., 1:rd:2]
+        r_ = z * w[:, None, :]
+        exp = X.copy()
+        if neox:
+            exp[..., : rd // 2], exp[..., rd // 2: rd] = r_.real, r_.imag
+        else:
+            exp[..., 0:rd:2], exp[..., 1:rd:2] = r_.real, r_.imag
+        np.testing.assert_allclose(got.reshape(T, -1, H), exp, rtol=1e-13, atol=1e-13)
+
+
+def test_interleaved_equal_rows_and_rope_mode_and_validation():
+    T, H = 11, 128
+    gen = torch.Generator().manual_seed(27)
+    q = torch.randn(T, 2 * H, generator=gen).to(torch.bfloat16)
+    cache = torch.randn(30, 128, generator=gen).to(torch.bfloat16)
+    p = torch.randint(0, 30, (T,), generator=gen)
+    rope = run_cache(p, q, q[:, :H].clone(), cache, None, H, True)
+    st, qo, ko, _, _ = run_cache_v2(p.repeat(3, 1).contiguous(), q, q[:, :H].clone(), cache,
+                                    [16, 24, 24], H, True, 1)
+    assert st == 0 and (raw_bits(qo) == raw_bits(rope[0])).all()
+    # cacheMode has no effect in rope mode
+    st, qo, _, _, _ = run_cache_v2(p, q, q[:, :H].clone(), cache, None, H, True, 1)
+    assert st == 0 and (raw_bits(qo) == raw_bits(rope[0])).all()
+    # cacheMode outside {0, 1}, and 1 with the 4-section list, are refused
+    st, *_ = run_cache_v2(p, q, q[:, :H].clone(), cache, None, H, True, 2)
+    assert st == oracle.ERR_PARAM_INVALID
+    st, *_ = run_cache_v2(p.repeat(4, 1).contiguous(), q, q[:, :H].clone(), cache,
+                          [16, 16, 16, 16], H, True, 1)
+    assert st == oracle.ERR_PARAM_INVALID
