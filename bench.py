@@ -128,7 +128,8 @@ def cache_calls(ra, torch, case, n_sets):
         p = case.positions if i == 0 else case.positions.clone()
         qo, ko = torch.empty_like(q), torch.empty_like(k)
         calls.append(ra.prepare_with_cos_sin_cache(p, q, k, case.cache, case.mrope_section,
-                                                   case.head_size, case.is_neox, qo, ko))
+                                                   case.head_size, case.is_neox, qo, ko,
+                                                   cache_mode=case.cache_mode))
     return calls
 
 
@@ -140,6 +141,8 @@ def describe_case(name, case):
                 f"{list(case.x.shape)} slice {case.partial_slice} cos/sin "
                 f"{str(case.cos.dtype)[6:]} {list(case.cos.shape)}")
     mode = f"mrope {case.mrope_section}" if case.mrope_section else "rope"
+    if case.mrope_section and case.cache_mode == 1:
+        mode += " interleaved (cacheMode 1)"
     style = "NeoX" if case.is_neox else "GPT-J"
     return (f"RopeWithSinCosCache {mode} {style} {str(case.query.dtype)[6:]} T={case.tokens} "
             f"q {list(case.query.shape)} k {list(case.key.shape)} headSize {case.head_size} "
@@ -204,7 +207,8 @@ def main() -> int:
                         ["inplace_bf16_8x4096x1x576_s512", "inplace_f32_1x16x2x64",
                          "cache_rope_neox_bf16_t8192", "cache_rope_gptj_f16_t32768_rd64",
                          "cache_mrope_neox_bf16_t16384",
-                         "inplace_backward_bf16_8x4096x1x576_s512"]),
+                         "inplace_backward_bf16_8x4096x1x576_s512",
+                         "cache_mrope_interleaved_neox_bf16_t16384"]),
                     help="first is the headline; the rest are reported under `kernels`")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)

@@ -570,35 +570,61 @@ __device__ inline void cache_store_pass(const CachePlan &p, int64_t t0, const T 
   }
 }
 
+// The position row of each element of the chunk starting at i0 (a multiple of V) in a
+// 3-section plan, computed without branches.
+template <int V>
+__device__ inline void multi_rows(const CachePlan &p, uint32_t i0, int *row) {
+  const uint32_t base = i0 % 3u;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const uint32_t e = i0 + uint32_t(j);
+    uint32_t m = base + uint32_t(j % 3);
+    m = m >= 3u ? m - 3u : m;  // e % 3
+    const int ri = int32_t(e) < p.interleave_end ? int(m) : 0;
+    const int rs = int(int32_t(e) >= p.sec_end[0]) + int(int32_t(e) >= p.sec_end[1]);
+    row[j] = p.interleaved ? ri : rs;
+  }
+}
+
+// Positions of rows 0..2 for the chunk.  A row the chunk does not use reads the position of
+// the chunk's first element's row instead, so its cache loads below hit the lines that row
+// brings in rather than fetching another cache row.  Every load is unconditional: loads
+// under divergent branches make the compiler wait for all outstanding loads at each join.
+template <int V>
+__device__ inline void multi_positions(const CachePlan &p, int64_t tok, uint32_t i0,
+                                       int64_t *pos) {
+  int row[V];
+  multi_rows<V>(p, i0, row);
+  bool need[3] = {false, false, false};
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    need[0] |= row[j] == 0;
+    need[1] |= row[j] == 1;
+    need[2] |= row[j] == 2;
+  }
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+    pos[r] = p.positions[(need[r] ? r : row[0]) * p.pos_stride_row + tok];
+}
+
 // Stages one V-element chunk (elements i0 .. i0+V-1 of the cos half, and the same of the sin
 // half) of a token whose stitched cos/sin draws on several position rows (interleaved
-// stitching, or a section boundary inside the chunk; three rows at most).  The chunk of every
-// row it needs is loaded as whole 16-byte vectors, then each element is taken from its row.
+// stitching, or a section boundary inside the chunk; three rows at most): the chunk of each
+// row is loaded as whole 16-byte vectors, then each element is taken from its row.  `pos`
+// holds the positions from multi_positions for the same chunk.
 template <typename T, int V>
-__device__ inline void stage_multi_row(const CachePlan &p, int64_t tok, uint32_t i0, int64_t half,
-                                       T *dst) {
+__device__ inline void stage_multi_row(const CachePlan &p, const int64_t *pos, uint32_t i0,
+                                       int64_t half, T *dst) {
   using R = typename Io<T>::raw;
   union Chunk {
     u32x4 v;
     R e[V];
   };
   int row[V];
-  bool need[3] = {false, false, false};
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    row[j] = cs_row_of(p, i0 + uint32_t(j));
-    need[0] |= row[j] == 0;
-    need[1] |= row[j] == 1;
-    need[2] |= row[j] == 2;
-  }
-  int64_t pos[3] = {0, 0, 0};
-#pragma unroll
-  for (int r = 0; r < 3; ++r)
-    if (need[r]) pos[r] = p.positions[r * p.pos_stride_row + tok];
+  multi_rows<V>(p, i0, row);
   Chunk c[3], s[3];
 #pragma unroll
   for (int r = 0; r < 3; ++r) {
-    if (!need[r]) continue;
     const T *src = static_cast<const T *>(p.cache) + clamp_position(p, pos[r]) * p.cache_stride + i0;
     c[r].v = ld16<false>(src);
     s[r].v = ld16<false>(src + half);
@@ -634,10 +660,12 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
     // loads: waiting for it does not then wait for them, and the position -> cache-row
     // chain runs while the q/k data is in flight.
     const uint32_t stage_items = uint32_t(ntok) * p.stage_chunks;
+    // (Multi-row chunks load their positions at staging time: holding three positions
+    // across the q/k loads costs more registers than the early load saves.)
     int64_t first_pos = 0;
     if (!MULTI && threadIdx.x < stage_items) {
       const uint32_t tl = fdiv(p.div_stage, threadIdx.x);
-      const int64_t i0 = int64_t(threadIdx.x - tl * p.stage_chunks) * V;
+      const uint32_t i0 = (threadIdx.x - tl * p.stage_chunks) * uint32_t(V);
       const int sec = p.mrope ? mrope_section_of(p, i0) : 0;
       first_pos = p.positions[sec * p.pos_stride_row + (t0 + tl) * p.pos_stride_tok];
     }
@@ -668,7 +696,9 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
           reinterpret_cast<R *>(dst + half)[j] = src[half];
         }
       } else if constexpr (MULTI) {
-        stage_multi_row<T, V>(p, tok, i0, half, dst);
+        int64_t pos[3];
+        multi_positions<V>(p, tok, i0, pos);
+        stage_multi_row<T, V>(p, pos, i0, half, dst);
       } else {
         const int sec = p.mrope ? mrope_section_of(p, i0) : 0;
         const int64_t pos =

@@ -189,6 +189,15 @@ def cache_mrope(device="cpu"):
                       positions=pos, device=device)
 
 
+def cache_mrope_interleaved(device="cpu"):
+    """mrope [24,20,20] interleaved stitching (V2, cacheMode 1), NeoX bf16: the shapes of the
+    sectioned mrope workload, T=16384, q [T, 28*128], k [T, 4*128], cache [32768, 128]."""
+    pos = mrope_positions(8192, 2, 64, 64)
+    return cache_case("cache_mrope_interleaved_24_20_20_neox_bf16_T16384_q28_k4_H128", 16384,
+                      28, 4, 128, 128, torch.bfloat16, True, 32768, seed=1006,
+                      mrope_section=[24, 20, 20], positions=pos, device=device, cache_mode=1)
+
+
 def inplace_bf16_slice_backward(device="cpu"):
     """The gradient op on the headline shape: incoming gradient bf16 [8,4096,1,576]."""
     case = inplace_bf16_slice(device)
@@ -205,5 +214,6 @@ CONFIGS = {
     "cache_mrope_neox_bf16_t16384": cache_mrope,
 }
 CONFIGS["inplace_backward_bf16_8x4096x1x576_s512"] = inplace_bf16_slice_backward
+CONFIGS["cache_mrope_interleaved_neox_bf16_t16384"] = cache_mrope_interleaved
 HEADLINE = "inplace_bf16_8x4096x1x576_s512"
 

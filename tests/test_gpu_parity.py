@@ -202,13 +202,12 @@ def compare_cache_case(case, qo, ko, what=None):
                   what or case.name, case.cache_mode)
 
 
-@pytest.mark.parametrize("cfg", ["cache_rope_neox_bf16_t8192", "cache_mrope_neox_bf16_t16384"])
+@pytest.mark.parametrize("cfg", ["cache_rope_neox_bf16_t8192", "cache_mrope_neox_bf16_t16384",
+                                 "cache_mrope_interleaved_neox_bf16_t16384"])
 def test_cache_configs_full(cfg):
     case = W.CONFIGS[cfg](DEV)
     qo, ko = run_cache_case(case)
-    compare_cache(case.positions.cpu(), case.query.cpu(), case.key.cpu(), case.cache.cpu(),
-                  case.mrope_section, case.head_size, case.is_neox, qo.cpu(), ko.cpu(),
-                  case.name)
+    compare_cache_case(case, qo, ko)
 
 
 def test_cache_config_c4_sampled_tokens():
