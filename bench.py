@@ -115,7 +115,7 @@ def inplace_calls(ra, case, n_sets):
         x = case.x if i == 0 else case.x.clone()
         c = case.cos if i == 0 else case.cos.clone()
         s = case.sin if i == 0 else case.sin.clone()
-        calls.append(ra.prepare_partial_inplace(x, c, s, 1, case.partial_slice,
+        calls.append(ra.prepare_partial_inplace(x, c, s, case.rotary_mode, case.partial_slice,
                                                 backward=case.backward))
     return calls
 
@@ -137,7 +137,8 @@ def describe_case(name, case):
     if hasattr(case, "x"):
         what = "InplacePartialRotaryMul backward (gradient)" if case.backward else \
             "InplacePartialRotaryMul"
-        return (f"{what} interleave x {str(case.x.dtype)[6:]} "
+        mode = "interleave" if case.rotary_mode == 1 else "half mode"
+        return (f"{what} {mode} x {str(case.x.dtype)[6:]} "
                 f"{list(case.x.shape)} slice {case.partial_slice} cos/sin "
                 f"{str(case.cos.dtype)[6:]} {list(case.cos.shape)}")
     mode = f"mrope {case.mrope_section}" if case.mrope_section else "rope"
@@ -150,7 +151,7 @@ def describe_case(name, case):
 
 
 def kernel_name(case) -> str:
-    return "inplace_interleave_kernel" if hasattr(case, "x") else "cos_sin_cache_kernel"
+    return "inplace_rope_kernel" if hasattr(case, "x") else "cos_sin_cache_kernel"
 
 
 def traffic_for(workload: str):
@@ -208,7 +209,8 @@ def main() -> int:
                          "cache_rope_neox_bf16_t8192", "cache_rope_gptj_f16_t32768_rd64",
                          "cache_mrope_neox_bf16_t16384",
                          "inplace_backward_bf16_8x4096x1x576_s512",
-                         "cache_mrope_interleaved_neox_bf16_t16384"]),
+                         "cache_mrope_interleaved_neox_bf16_t16384",
+                         "inplace_half_bf16_8x4096x1x576_s512"]),
                     help="first is the headline; the rest are reported under `kernels`")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)

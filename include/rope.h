@@ -4,7 +4,7 @@
  * Each operation is one call that validates its arguments on the host and then enqueues
  * hand-written HIP kernels on the caller's stream:
  *
- *   rope_partial_inplace           in-place partial RoPE, interleave mode, on a BSND tensor
+ *   rope_partial_inplace           in-place partial RoPE (interleave or half mode) on a BSND tensor
  *   rope_partial_inplace_backward  its gradient with respect to x, in place on the gradient
  *   rope_with_cos_sin_cache        RoPE of query/key rows with cos/sin gathered from a cache by
  *                                  position; rope or mrope mode; GPT-NeoX or GPT-J style
@@ -75,21 +75,27 @@ typedef struct {
 } rope_tensor;
 
 /*
- * rope_partial_inplace -- in-place partial RoPE, interleave mode.
+ * rope_partial_inplace -- in-place partial RoPE.
  *
  * Defined in [IPRM §计算原理与公式] and [IPRM §partial_slice 局部旋转机制]: on the slice
- * x[..., start:end) of the last dim, pairs (x[2i], x[2i+1]) counted from `start` become
+ * x[..., start:end) of the last dim (indices below count from `start`), x = x*cos +
+ * x_rotate*sin.  Interleave mode (rotary_mode 1): x_rotate = (-x2, x1) interleaved per pair,
+ * so each pair (x[2i], x[2i+1]) becomes
  *     x[2i]   = x[2i]*cos[2i]     - x[2i+1]*sin[2i]
  *     x[2i+1] = x[2i+1]*cos[2i+1] + x[2i]*sin[2i+1]
- * (x*cos + x_rotate*sin with x_rotate = (-x2, x1) interleaved per pair).  Elements in
- * [0, start) and [end, D) are never read or written.
+ * Half mode (rotary_mode 0; [IPRM §参数说明] lists it as not yet enabled on its hardware,
+ * enabled here): x1, x2 are the two halves of the slice, x_rotate = cat(-x2, x1), so with
+ * h = L/2 each pair (x[i], x[i+h]) becomes
+ *     x[i]   = x[i]*cos[i]     - x[i+h]*sin[i]
+ *     x[i+h] = x[i+h]*cos[i+h] + x[i]*sin[i+h]
+ * Elements in [0, start) and [end, D) are never read or written.
  *
  * x      [B, S, N, D] (BSND), contiguous, F32 / F16 / BF16; read and written in place.
  * cos,   [Bc, Sc, Nc, L] with L = end - start, contiguous, both of one dtype: x's dtype or
  * sin    F32 (F32 with half-precision x is the mixed case of [IPRM §返回值与错误码]).
  *        Each of Bc, Sc, Nc is 1 (broadcast) or equal to x's B, S, N; this covers the BSND,
  *        BS1D, B1ND, B11D and 111D layouts of [IPRM §约束说明].
- * rotary_mode    must be 1 (interleave); half mode (0) is not supported ([IPRM §约束说明]).
+ * rotary_mode    1 (interleave) or 0 (half); any other value is ROPE_ERR_PARAM_INVALID.
  * partial_slice  host array {start, end}; NULL with partial_slice_len 0 means [0, D).
  *                0 <= start <= end <= D and end - start even; start == end returns
  *                ROPE_OK at once without launching anything (and without checking cos/sin's
@@ -108,10 +114,10 @@ int rope_partial_inplace(const rope_tensor *x, const rope_tensor *cos, const rop
  *
  * [IPRM §Python 接口与自动微分]: the training path computes the gradient of x with a backward
  * op; cos and sin get no gradient; empty tensors and empty slices are no-ops.  The pages give
- * no formula: on each slice pair the forward map is y = [[c0, -s0], [s1, c1]] x, so its
- * gradient is the transpose,
- *     g[2i]   = g[2i]*cos[2i]     + g[2i+1]*sin[2i+1]
- *     g[2i+1] = g[2i+1]*cos[2i+1] - g[2i]*sin[2i]
+ * no formula: on each slice pair (j, k) -- (2i, 2i+1) in interleave mode, (i, i+L/2) in half
+ * mode -- the forward map is y = [[c_j, -s_j], [s_k, c_k]] x, so its gradient is the transpose,
+ *     g[j] = g[j]*cos[j] + g[k]*sin[k]
+ *     g[k] = g[k]*cos[k] - g[j]*sin[j]
  * and elements outside [start, end) pass the gradient through unchanged (never touched).
  * Arguments, layouts, validation, error codes and the no-op rules are those of
  * rope_partial_inplace, with g in the place of x.

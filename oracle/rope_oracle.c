@@ -34,7 +34,13 @@
  *  R9 mropeSection[0] > 0 selects mrope; the whitelist is the five lists of [RSCC §入参校验逻辑];
  *  R11 a position outside [0, maxSeqLen) is outside the contract: the oracle refuses it;
  *  R12 an in-place call on an empty x is a successful no-op; the cache op requires non-empty
- *      inputs ([RSCC §入参校验逻辑]).
+ *      inputs ([RSCC §入参校验逻辑]);
+ *  R18 interleaved stitching (cacheMode 1) takes the printed bound 3*mropeSection[1] for rows
+ *      1 and 2;
+ *  R20 the in-place gradient is the transpose of the forward map (the page gives no formula);
+ *  R21 rotary_mode 0 (half mode, listed but not enabled on the pages) is enabled: x1 and x2
+ *      are the first and second halves of the slice, x_rotate = cat(-x2, x1), the same formula
+ *      x*cos + x_rotate*sin; 2 and 3 stay invalid.
  */
 #include <math.h>
 #include <stdint.h>
@@ -239,14 +245,48 @@ static int contiguous(const oro_tensor *t) {
 static int is_float_dtype(int dt) { return dt == ORO_F32 || dt == ORO_F16 || dt == ORO_BF16; }
 
 /* ==========================================================================================
- * Operation A: in-place partial interleave RoPE.
+ * Operation A: in-place partial RoPE, interleave mode (and half mode, reading R21).
  *   [IPRM §计算原理与公式]     x1 = x[..., ::2], x2 = x[..., 1::2], x_rotate from -x2 and x1,
  *                              x = x*cos + x_rotate*sin (reading R1: per-pair interleave);
+ *   [IPRM §参数说明]           rotary_mode 0 is half mode, 1 interleave;
  *   [IPRM §partial_slice 局部旋转机制] only x[..., start:end) is rotated, cos/sin cover that slice;
  *   [IPRM §约束说明]           D <= 1024, D even, slice length even, cos/sin last dim == slice
  *                              length, cos/sin broadcast to BSND, contiguous tensors only;
  *   [IPRM §返回值与错误码]     161001 for null tensors, 161002 for every other invalid input.
  * ========================================================================================== */
+/* Half mode on one row's slice (reading R21): with h = L/2, x1 = slice[0:h], x2 = slice[h:L],
+ *   x_rotate = cat(-x2, x1), i.e. x_rotate[i] = -slice[i+h] for i < h and slice[i-h] above;
+ *   forward   y = slice*cos + x_rotate*sin;
+ *   gradient  the map is y = C x + S R x (C, S diagonal, R the rotate-half matrix), so
+ *             dx = C g + R^T S g with (R^T v)[i] = v[i+h] for i < h and -v[i-h] above.
+ * The whole slice is read before any element is written (the op is in place). */
+static void half_mode_row(const oro_tensor *x, const oro_tensor *cos_t, const oro_tensor *sin_t,
+                          int64_t xs, int64_t crow, int64_t L, double *x64, int backward) {
+  float v[1024]; /* L <= D <= 1024 */
+  const int64_t h = L / 2;
+  for (int64_t i = 0; i < L; ++i) v[i] = load_f32(x, xs + i);
+  for (int64_t i = 0; i < L; ++i) {
+    const float c = load_f32(cos_t, crow + i), sn = load_f32(sin_t, crow + i);
+    float p = v[i] * c, q;
+    double q64;
+    if (!backward) {
+      const float rot = i < h ? -v[i + h] : v[i - h];
+      q = rot * sn;
+      q64 = (double)rot * (double)sn;
+    } else if (i < h) {
+      const float sp = load_f32(sin_t, crow + i + h);
+      q = v[i + h] * sp;
+      q64 = (double)v[i + h] * (double)sp;
+    } else {
+      const float sp = load_f32(sin_t, crow + i - h);
+      q = -(v[i - h] * sp);
+      q64 = -((double)v[i - h] * (double)sp);
+    }
+    store_rounded(x, xs + i, p + q);
+    if (x64) x64[xs + i] = (double)v[i] * (double)c + q64;
+  }
+}
+
 static int partial_inplace(const oro_tensor *x, const oro_tensor *cos_t, const oro_tensor *sin_t,
                            int64_t rotary_mode, const int64_t *partial_slice,
                            int64_t partial_slice_len, double *x64, int backward) {
@@ -265,7 +305,8 @@ static int partial_inplace(const oro_tensor *x, const oro_tensor *cos_t, const o
   if (!(cos_t->dtype == x->dtype || cos_t->dtype == ORO_F32))
     return fail(ORO_ERR_PARAM_INVALID, "cos/sin dtype must equal xRef's or be float32");
 
-  if (rotary_mode != 1) return fail(ORO_ERR_PARAM_INVALID, "only interleave mode (1) is supported");
+  if (rotary_mode != 0 && rotary_mode != 1)
+    return fail(ORO_ERR_PARAM_INVALID, "rotary_mode must be 1 (interleave) or 0 (half)");
 
   /* shapes */
   for (int i = 0; i < 3; ++i)
@@ -318,6 +359,10 @@ static int partial_inplace(const oro_tensor *x, const oro_tensor *cos_t, const o
         int64_t sc = cos_t->shape[1] == 1 ? 0 : s;
         int64_t nc = cos_t->shape[2] == 1 ? 0 : n;
         int64_t crow = ((bc * cos_t->shape[1] + sc) * cos_t->shape[2] + nc) * L;
+        if (rotary_mode == 0) {
+          half_mode_row(x, cos_t, sin_t, xrow + start, crow, L, x64, backward);
+          continue;
+        }
         for (int64_t i = 0; i < L / 2; ++i) {
           int64_t j0 = xrow + start + 2 * i, j1 = j0 + 1; /* pair counted from the slice start */
           float a = load_f32(x, j0);

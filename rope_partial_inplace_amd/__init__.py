@@ -7,7 +7,8 @@ streams.  There is no fallback: if the library is not built this import fails.
 
   rope_partial_inplace(x, cos, sin, rotary_mode=1, partial_slice=None, stream=None)
   rope_partial_inplace_backward(g, cos, sin, rotary_mode=1, partial_slice=None, stream=None)
-  InplacePartialRotaryMul.apply(x, cos, sin, partial_slice)   (autograd; x must not be a leaf)
+  InplacePartialRotaryMul.apply(x, cos, sin, partial_slice, rotary_mode)
+                                                  (autograd; x must not be a leaf)
   rope_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,
                           head_size, is_neox_style, query_out=None, key_out=None, stream=None)
   rope_with_cos_sin_cache_v2(..., is_neox_style, cache_mode, query_out=None, ...)
@@ -140,7 +141,8 @@ def _check(code: int):
 
 
 def rope_partial_inplace(x, cos, sin, rotary_mode: int = 1, partial_slice=None, stream=None):
-    """In-place partial interleave RoPE on x[..., start:end) ([IPRM §计算原理与公式])."""
+    """In-place partial RoPE on x[..., start:end) ([IPRM §计算原理与公式]): rotary_mode 1
+    interleave, 0 half mode (x1, x2 the two halves of the slice)."""
     dev = _device_of([x, cos, sin])
     dx, dc, ds = describe(x), describe(cos), describe(sin)
     sl, sl_len = _int_array(partial_slice)
@@ -169,19 +171,20 @@ def _autograd_function():
         gradient; cos and sin get no gradient."""
 
         @staticmethod
-        def forward(ctx, x, cos, sin, partial_slice=None):
-            rope_partial_inplace(x, cos, sin, 1, partial_slice)
+        def forward(ctx, x, cos, sin, partial_slice=None, rotary_mode=1):
+            rope_partial_inplace(x, cos, sin, rotary_mode, partial_slice)
             ctx.mark_dirty(x)
             ctx.save_for_backward(cos, sin)
             ctx.partial_slice = partial_slice
+            ctx.rotary_mode = rotary_mode
             return x
 
         @staticmethod
         def backward(ctx, grad):
             cos, sin = ctx.saved_tensors
             g = grad.contiguous().clone()
-            rope_partial_inplace_backward(g, cos, sin, 1, ctx.partial_slice)
-            return g, None, None, None
+            rope_partial_inplace_backward(g, cos, sin, ctx.rotary_mode, ctx.partial_slice)
+            return g, None, None, None, None
 
     return InplacePartialRotaryMul
 

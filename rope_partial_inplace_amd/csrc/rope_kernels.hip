@@ -298,7 +298,9 @@ __device__ inline uint32_t fdiv(const FastDiv &f, uint32_t n) {
   return (t + ((n - t) >> f.s1)) >> f.s2;
 }
 
-// One interleave pair of [IPRM §计算原理与公式] (reading: x_rotate = (-x[2i+1], x[2i]) per pair):
+// One pair (x0, x1) of [IPRM §计算原理与公式]: (x[2i], x[2i+1]) in interleave mode (reading:
+// x_rotate = (-x[2i+1], x[2i]) per pair), (x[i], x[i + L/2]) in half mode; c0, s0 are the
+// cos/sin entries of x0's position and c1, s1 those of x1's:
 //   forward  y0 = x0*c0 + (-x1)*s0,  y1 = x1*c1 + x0*s1;
 //   backward (transpose of the pair map, [IPRM §Python 接口与自动微分]):
 //            g0' = g0*c0 + g1*s1,    g1' = g1*c1 - g0*s0.
@@ -315,24 +317,31 @@ __device__ inline void rotate_pair(float a, float b, float c0, float c1, float s
 }
 
 // ============================================================================================
-// K1: in-place partial interleave ([IPRM §计算原理与公式], [IPRM §partial_slice 局部旋转机制]).
-// A lane owns K chunks of V slice elements (V/2 pairs); chunks of one row are adjacent lanes,
-// so a wavefront reads and writes whole 16-byte-aligned runs of each row's slice.  Elements
-// outside [start, end) are never touched.  cos/sin rows are addressed with zero strides on
-// broadcast dims (BSND, BS1D, B1ND, B11D, 111D and mixed forms).  BWD runs the transpose
-// of the pair map on an incoming gradient (same access pattern).  x is streamed
+// K1: in-place partial RoPE ([IPRM §计算原理与公式], [IPRM §partial_slice 局部旋转机制]).
+// Interleave mode: a lane owns K chunks of V slice elements (V/2 pairs); chunks of one row
+// are adjacent lanes, so a wavefront reads and writes whole 16-byte-aligned runs of each
+// row's slice.  HALF (rotary_mode 0, [IPRM §参数说明]; x1, x2 the two halves of the slice,
+// x_rotate = cat(-x2, x1)): a lane owns chunk u of the first half and chunk u of the second,
+// so every pair (i, i + L/2) is lane-local and both halves are read as contiguous runs.
+// Elements outside [start, end) are never touched.  cos/sin rows are addressed with zero
+// strides on broadcast dims (BSND, BS1D, B1ND, B11D, 111D and mixed forms).  BWD runs the
+// transpose of the pair map on an incoming gradient (same access pattern).  x is streamed
 // (non-temporal); cos/sin are streamed too unless a row is shared by several x rows
 // (broadcast), where the caches serve the repeats.
 // ============================================================================================
-template <typename XT, typename CT, bool VEC, int K, bool CNT, bool BWD>
-__global__ __launch_bounds__(kBlock) void inplace_interleave_kernel(InplacePlan p) {
-  // one 16-byte access per lane for the wider of x and cos/sin, 8 bytes for the narrower
-  constexpr int V = VEC ? 16 / (sizeof(XT) > sizeof(CT) ? int(sizeof(XT)) : int(sizeof(CT))) : 2;
+template <typename XT, typename CT, bool VEC, int K, bool CNT, bool BWD, bool HALF>
+__global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
+  // one 16-byte access per lane for the wider of x and cos/sin, 8 bytes for the narrower;
+  // element access: one pair (2 elements) in interleave mode, one element per half in HALF
+  constexpr int V =
+      VEC ? 16 / (sizeof(XT) > sizeof(CT) ? int(sizeof(XT)) : int(sizeof(CT))) : (HALF ? 1 : 2);
+  constexpr int NH = HALF ? 2 : 1;  // chunks per lane item: one, or one in each half
   const uint64_t items = uint64_t(p.items);
   const uint64_t per_block = uint64_t(kBlock) * K;
+  const int64_t hoff = HALF ? p.L / 2 : 0;  // offset of the second half
   for (uint64_t base = uint64_t(blockIdx.x) * per_block; base < items;
        base += uint64_t(gridDim.x) * per_block) {
-    float xv[K][V], cv[K][V], sv[K][V];
+    float xv[K][NH][V], cv[K][NH][V], sv[K][NH][V];
     int64_t xoff[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -361,19 +370,32 @@ __global__ __launch_bounds__(kBlock) void inplace_interleave_kernel(InplacePlan 
       const int64_t crow = int64_t(b) * p.cb + int64_t(s) * p.cs + int64_t(n) * p.cn;
       const int64_t coff = crow * p.L + int64_t(chunk) * V;
       xoff[k] = int64_t(row) * p.D + p.start + int64_t(chunk) * V;
-      load_n<XT, V, VEC, true>(p.x, xoff[k], xv[k]);
-      load_n<CT, V, VEC, CNT>(p.cos, coff, cv[k]);
-      load_n<CT, V, VEC, CNT>(p.sin, coff, sv[k]);
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        load_n<XT, V, VEC, true>(p.x, xoff[k] + hh * hoff, xv[k][hh]);
+        load_n<CT, V, VEC, CNT>(p.cos, coff + hh * hoff, cv[k][hh]);
+        load_n<CT, V, VEC, CNT>(p.sin, coff + hh * hoff, sv[k][hh]);
+      }
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       if (xoff[k] < 0) continue;
-      float y[V];
+      if constexpr (HALF) {
+        float ya[V], yb[V];
 #pragma unroll
-      for (int e = 0; e < V; e += 2)
-        rotate_pair<BWD>(xv[k][e], xv[k][e + 1], cv[k][e], cv[k][e + 1], sv[k][e], sv[k][e + 1],
-                         y[e], y[e + 1]);
-      store_n<XT, V, VEC, true>(p.x, xoff[k], y);
+        for (int e = 0; e < V; ++e)
+          rotate_pair<BWD>(xv[k][0][e], xv[k][1][e], cv[k][0][e], cv[k][1][e], sv[k][0][e],
+                           sv[k][1][e], ya[e], yb[e]);
+        store_n<XT, V, VEC, true>(p.x, xoff[k], ya);
+        store_n<XT, V, VEC, true>(p.x, xoff[k] + hoff, yb);
+      } else {
+        float y[V];
+#pragma unroll
+        for (int e = 0; e < V; e += 2)
+          rotate_pair<BWD>(xv[k][0][e], xv[k][0][e + 1], cv[k][0][e], cv[k][0][e + 1],
+                           sv[k][0][e], sv[k][0][e + 1], y[e], y[e + 1]);
+        store_n<XT, V, VEC, true>(p.x, xoff[k], y);
+      }
     }
   }
 }
@@ -740,25 +762,26 @@ int launch(const void *fn, int64_t blocks, int threads, size_t lds, void *stream
   return ROPE_OK;
 }
 
-template <typename XT, typename CT, bool BWD>
+template <typename XT, typename CT, bool BWD, bool HALF>
 const void *pick_inplace(bool vec, bool cos_stream) {
   constexpr int K = kInplaceItemsPerLane;
   if (vec)
     return cos_stream ? reinterpret_cast<const void *>(
-                            &inplace_interleave_kernel<XT, CT, true, K, true, BWD>)
+                            &inplace_rope_kernel<XT, CT, true, K, true, BWD, HALF>)
                       : reinterpret_cast<const void *>(
-                            &inplace_interleave_kernel<XT, CT, true, K, false, BWD>);
-  return reinterpret_cast<const void *>(&inplace_interleave_kernel<XT, CT, false, K, false, BWD>);
+                            &inplace_rope_kernel<XT, CT, true, K, false, BWD, HALF>);
+  return reinterpret_cast<const void *>(&inplace_rope_kernel<XT, CT, false, K, false, BWD, HALF>);
 }
 
-template <bool BWD>
+template <bool BWD, bool HALF>
 const void *pick_inplace_dtype(const InplacePlan &p) {
-  if (p.xdt == ROPE_F32) return pick_inplace<float, float, BWD>(p.vector_io, p.cos_stream);
+  const bool v = p.vector_io, cs = p.cos_stream;
+  if (p.xdt == ROPE_F32) return pick_inplace<float, float, BWD, HALF>(v, cs);
   if (p.xdt == ROPE_F16)
-    return p.cdt == ROPE_F32 ? pick_inplace<_Float16, float, BWD>(p.vector_io, p.cos_stream)
-                             : pick_inplace<_Float16, _Float16, BWD>(p.vector_io, p.cos_stream);
-  return p.cdt == ROPE_F32 ? pick_inplace<__bf16, float, BWD>(p.vector_io, p.cos_stream)
-                           : pick_inplace<__bf16, __bf16, BWD>(p.vector_io, p.cos_stream);
+    return p.cdt == ROPE_F32 ? pick_inplace<_Float16, float, BWD, HALF>(v, cs)
+                             : pick_inplace<_Float16, _Float16, BWD, HALF>(v, cs);
+  return p.cdt == ROPE_F32 ? pick_inplace<__bf16, float, BWD, HALF>(v, cs)
+                           : pick_inplace<__bf16, __bf16, BWD, HALF>(v, cs);
 }
 
 template <typename T, bool MULTI>
@@ -800,7 +823,10 @@ int run_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor 
   }
   g_last_error.clear();
   if (plan.noop) return ROPE_OK;
-  const void *fn = backward ? pick_inplace_dtype<true>(plan) : pick_inplace_dtype<false>(plan);
+  const void *fn = plan.half ? (backward ? pick_inplace_dtype<true, true>(plan)
+                                         : pick_inplace_dtype<false, true>(plan))
+                            : (backward ? pick_inplace_dtype<true, false>(plan)
+                                        : pick_inplace_dtype<false, false>(plan));
   const int64_t per_block = int64_t(kBlock) * kInplaceItemsPerLane;
   return launch(fn, (plan.items + per_block - 1) / per_block, kBlock, 0, stream, &plan);
 }

@@ -105,8 +105,10 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
     return reject(err, ROPE_ERR_PARAM_INVALID, "cos and sin dtypes differ");
   if (cos->dtype != x->dtype && cos->dtype != ROPE_F32)
     return reject(err, ROPE_ERR_PARAM_INVALID, "cos/sin must have xRef's dtype or float32");
-  if (rotary_mode != 1)
-    return reject(err, ROPE_ERR_PARAM_INVALID, "rotary_mode must be 1 (interleave)");
+  // rotary_mode ([IPRM §参数说明]): 1 interleave; 0 half mode, which the pages list but
+  // have not enabled -- enabled here with x1, x2 the two halves of the slice.
+  if (rotary_mode != 0 && rotary_mode != 1)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "rotary_mode must be 1 (interleave) or 0 (half)");
 
   for (const rope_tensor *t : {x, cos, sin})
     if (!valid_rank(t) || t->ndim != 4)
@@ -143,6 +145,7 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
       return reject(err, ROPE_ERR_PARAM_INVALID, "cos/sin do not broadcast to xRef");
 
   InplacePlan &p = *plan;
+  p.half = rotary_mode == 0;
   p.xdt = x->dtype;
   p.cdt = cos->dtype;
   p.x = x->data;
@@ -168,15 +171,19 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
 
   // Lane chunks of V elements: a 16-byte access for the wider of x and cos/sin (8 bytes for
   // the narrower) when every chunk start is aligned to its access size; else element access.
+  // Half mode: a lane owns chunk u of each half (its pairs are (i, i + L/2)), so the halves
+  // must split into whole chunks.
   const int xs = bytes_of(p.xdt), cs = bytes_of(p.cdt);
   const int64_t v = 16 / std::max(xs, cs);
-  const bool aligned = L % v == 0 && (D * xs) % (v * xs) == 0 && (start * xs) % (v * xs) == 0 &&
+  const int64_t span = p.half ? L / 2 : L;  // elements one lane's chunks are taken from
+  const bool aligned = span % v == 0 && (D * xs) % (v * xs) == 0 &&
+                       (start * xs) % (v * xs) == 0 &&
                        (reinterpret_cast<uintptr_t>(p.x) % uintptr_t(v * xs)) == 0 &&
                        (reinterpret_cast<uintptr_t>(p.cos) % uintptr_t(v * cs)) == 0 &&
                        (reinterpret_cast<uintptr_t>(p.sin) % uintptr_t(v * cs)) == 0;
   p.vector_io = aligned;
-  p.vec = aligned ? uint32_t(v) : 2u;
-  p.chunks_per_row = uint32_t(L / p.vec);
+  p.vec = aligned ? uint32_t(v) : (p.half ? 1u : 2u);
+  p.chunks_per_row = uint32_t(span / p.vec);
   p.items = p.rows * p.chunks_per_row;
   p.idx32 = p.items < (int64_t(1) << 32);
   p.div_cpr = make_fastdiv(p.chunks_per_row);

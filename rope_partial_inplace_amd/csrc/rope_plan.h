@@ -35,11 +35,14 @@ inline uint32_t fastdiv_host(const FastDiv &f, uint32_t n) {
   return (t + ((n - t) >> f.s1)) >> f.s2;
 }
 
-// ---- in-place partial interleave ----------------------------------------------------------
-// The slice of every row (b, s, n) is cut into `chunks_per_row` chunks of `vec` elements;
-// one GPU lane owns one chunk (all pairs of a chunk are lane-local because vec is even and
-// chunks start at even offsets from the slice start).
+// ---- in-place partial RoPE ----------------------------------------------------------------
+// Interleave mode: the slice of every row (b, s, n) is cut into `chunks_per_row` chunks of
+// `vec` elements; one GPU lane owns one chunk (all pairs of a chunk are lane-local because
+// vec is even and chunks start at even offsets from the slice start).  Half mode: the first
+// half of the slice is cut into chunks; the lane owning chunk u also owns chunk u of the
+// second half, which holds the partners (i + L/2) of its elements.
 struct InplacePlan {
+  bool half = false;  // rotary_mode 0
   rope_dtype xdt = ROPE_F32, cdt = ROPE_F32;
   bool vector_io = false;  // 16-byte x accesses (else one element at a time)
   bool noop = false;       // nothing to launch
@@ -49,7 +52,7 @@ struct InplacePlan {
   int64_t rows = 0;             // B*S*N
   int64_t items = 0;            // rows * chunks_per_row
   uint32_t vec = 2;             // elements per lane chunk
-  uint32_t chunks_per_row = 0;  // L / vec
+  uint32_t chunks_per_row = 0;  // L / vec (half mode: (L/2) / vec)
   // cos/sin row of x-row (b, s, n) = b*cb + s*cs + n*cn (in rows of L elements)
   int64_t cb = 0, cs = 0, cn = 0;
   bool cos_stream = false;  // every cos/sin row is read by exactly one x row (no broadcast)

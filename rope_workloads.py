@@ -51,6 +51,14 @@ def pairwise_tables(pos: np.ndarray, length: int, dtype) -> tuple[torch.Tensor, 
     return c, s
 
 
+def half_tables(pos: np.ndarray, length: int, dtype) -> tuple[torch.Tensor, torch.Tensor]:
+    """cos/sin rows of `length` elements for the half (rotate-half) layout: the angles of the
+    length/2 frequencies, written twice (element i and element i + length/2 share one)."""
+    a = angles(pos, length // 2, length)
+    a = np.concatenate([a, a], axis=1)
+    return torch.from_numpy(np.cos(a)).to(dtype), torch.from_numpy(np.sin(a)).to(dtype)
+
+
 def cos_sin_cache(max_seq: int, rotary_dim: int, dtype) -> torch.Tensor:
     """[max_seq, rotary_dim] cache: cos of the rotary_dim/2 angles, then their sin."""
     a = angles(np.arange(max_seq), rotary_dim // 2, rotary_dim)
@@ -71,14 +79,16 @@ class InplaceCase:
     tokens: int           # B*S
     algo_bytes: int       # bytes the op must move (slice read+write, cos, sin)
     backward: bool = False  # run the gradient op (x is then the incoming gradient)
+    rotary_mode: int = 1    # 1 interleave, 0 half
 
 
 def inplace_case(name, B, S, N, D, xdtype, cdtype, partial_slice, cos_shape=None, seed=0,
-                 table="angles", device="cpu"):
+                 table="angles", device="cpu", rotary_mode=1):
     """x ~ N(0,1) of shape [B,S,N,D]; cos/sin of `cos_shape` (default BS1D) over the slice.
 
-    table="angles": cos/sin from angle s * theta^(-2i/L) repeated per pair (s = sequence
-    index of the row); table="randn": independent N(0,1) values (per-element cos/sin).
+    table="angles": cos/sin from angle s * theta^(-2i/L) (s = sequence index of the row),
+    laid out for the mode: repeated per pair (interleave) or written once per half (half);
+    table="randn": independent N(0,1) values (per-element cos/sin).
     """
     g = generator(seed, device)
     x = randn((B, S, N, D), xdtype, g)
@@ -87,7 +97,8 @@ def inplace_case(name, B, S, N, D, xdtype, cdtype, partial_slice, cos_shape=None
     cshape = list(cos_shape) if cos_shape is not None else [B, S, 1, L]
     if table == "angles":
         pos = np.arange(cshape[1]) if cshape[1] > 1 else np.zeros(1)
-        c, s = pairwise_tables(pos, L, cdtype)          # [Sc, L]
+        tables = pairwise_tables if rotary_mode == 1 else half_tables
+        c, s = tables(pos, L, cdtype)                    # [Sc, L]
         c = c.reshape(1, cshape[1], 1, L).expand(cshape).contiguous().to(device)
         s = s.reshape(1, cshape[1], 1, L).expand(cshape).contiguous().to(device)
     else:
@@ -98,7 +109,7 @@ def inplace_case(name, B, S, N, D, xdtype, cdtype, partial_slice, cos_shape=None
     rows = B * S * N
     crow_count = int(np.prod(cshape[:3]))
     algo = rows * L * xs * 2 + 2 * crow_count * L * cs
-    return InplaceCase(name, x, c, s, partial_slice, B * S, algo)
+    return InplaceCase(name, x, c, s, partial_slice, B * S, algo, rotary_mode=rotary_mode)
 
 
 def inplace_f32_small(device="cpu"):
@@ -198,6 +209,14 @@ def cache_mrope_interleaved(device="cpu"):
                       mrope_section=[24, 20, 20], positions=pos, device=device, cache_mode=1)
 
 
+def inplace_half_bf16_slice(device="cpu"):
+    """Half mode (rotary_mode 0) on the headline shape: bf16 x [8,4096,1,576], slice
+    [512,576), fp32 rotate-half cos/sin [8,4096,1,64]."""
+    return inplace_case("inplace_half_bf16x_f32cs_8x4096x1x576_slice512_576", 8, 4096, 1, 576,
+                        torch.bfloat16, torch.float32, [512, 576], seed=1007, device=device,
+                        rotary_mode=0)
+
+
 def inplace_bf16_slice_backward(device="cpu"):
     """The gradient op on the headline shape: incoming gradient bf16 [8,4096,1,576]."""
     case = inplace_bf16_slice(device)
@@ -215,5 +234,6 @@ CONFIGS = {
 }
 CONFIGS["inplace_backward_bf16_8x4096x1x576_s512"] = inplace_bf16_slice_backward
 CONFIGS["cache_mrope_interleaved_neox_bf16_t16384"] = cache_mrope_interleaved
+CONFIGS["inplace_half_bf16_8x4096x1x576_s512"] = inplace_half_bf16_slice
 HEADLINE = "inplace_bf16_8x4096x1x576_s512"
 

@@ -79,16 +79,27 @@ def check_bits_equal(a: torch.Tensor, b: torch.Tensor, what: str):
 
 # ---- magnitude scales of the two products of every output element (for the f32 bound) ----
 
-def inplace_scale(x: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, start: int, end: int):
-    """[..., L] scale of the rotated slice: |x0 c0| + |x1 s0| and |x1 c1| + |x0 s1|."""
+def inplace_scale(x: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, start: int, end: int,
+                  mode: int = 1, backward: bool = False):
+    """[..., L] scale of the rotated slice for the pairs (j, k) of the mode ((2i, 2i+1)
+    interleave, (i, i + L/2) half): forward |x_j c_j| + |x_k s_j| and |x_k c_k| + |x_j s_k|;
+    backward |x_j c_j| + |x_k s_k| and |x_k c_k| + |x_j s_j|."""
     xs = as_f64(x)[..., start:end]
     L = end - start
     c = np.broadcast_to(as_f64(cos), xs.shape[:-1] + (L,))
     s = np.broadcast_to(as_f64(sin), xs.shape[:-1] + (L,))
-    a, b = xs[..., 0::2], xs[..., 1::2]
+    if mode == 1:
+        j, k = np.arange(0, L, 2), np.arange(1, L, 2)
+    else:
+        j, k = np.arange(L // 2), np.arange(L // 2, L)
+    a, b = xs[..., j], xs[..., k]
     out = np.empty_like(xs)
-    out[..., 0::2] = np.abs(a * c[..., 0::2]) + np.abs(b * s[..., 0::2])
-    out[..., 1::2] = np.abs(b * c[..., 1::2]) + np.abs(a * s[..., 1::2])
+    if not backward:
+        out[..., j] = np.abs(a * c[..., j]) + np.abs(b * s[..., j])
+        out[..., k] = np.abs(b * c[..., k]) + np.abs(a * s[..., k])
+    else:
+        out[..., j] = np.abs(a * c[..., j]) + np.abs(b * s[..., k])
+        out[..., k] = np.abs(b * c[..., k]) + np.abs(a * s[..., j])
     return out
 
 

@@ -120,7 +120,8 @@ INPLACE_CASES = [
     ("cos f16 with bf16 x", lambda b: (b[0], dict(b[1], dtype=1), dict(b[2], dtype=1), 1,
                                        [0, 8]), INVALID),
     ("cos/sin dtypes differ", lambda b: (b[0], b[1], dict(b[2], dtype=2), 1, [0, 8]), INVALID),
-    ("half mode", lambda b: (b[0], b[1], b[2], 0, [0, 8]), INVALID),
+    ("mode 2", lambda b: (b[0], b[1], b[2], 2, [0, 8]), INVALID),
+    ("mode -1", lambda b: (b[0], b[1], b[2], -1, [0, 8]), INVALID),
     ("mode 3", lambda b: (b[0], b[1], b[2], 3, [0, 8]), INVALID),
     ("x 3-D", lambda b: (dict(b[0], ndim=3), b[1], b[2], 1, [0, 8]), INVALID),
     ("cos 3-D", lambda b: (b[0], dict(b[1], ndim=3), dict(b[2], ndim=3), 1, [0, 8]), INVALID),
@@ -156,10 +157,15 @@ INPLACE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("mode", [1, 0], ids=["interleave", "half"])
 @pytest.mark.parametrize("backward", [False, True], ids=["forward", "backward"])
 @pytest.mark.parametrize("name,build,expected", INPLACE_CASES, ids=[c[0] for c in INPLACE_CASES])
-def test_inplace_validation(name, build, expected, backward):
-    args = build(inplace_base())
+def test_inplace_validation(name, build, expected, backward, mode):
+    """Every case in interleave mode and again in half mode (cases written with mode 1 take
+    the parametrized mode; the others keep their own)."""
+    args = list(build(inplace_base()))
+    if args[3] == 1:
+        args[3] = mode
     lib_st, ora_st = call_inplace(*args, backward=backward)
     assert lib_st == expected, ra.last_error()
     assert ora_st == expected, oracle.last_error()
@@ -337,6 +343,16 @@ def test_runtime_error_without_gpu():
                                      *ints([0, 8]), None)
     assert st == ra.ROPE_ERR_RUNTIME
     assert "launch" in ra.last_error()
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU error path")
+@pytest.mark.parametrize("backward", [False, True], ids=["forward", "backward"])
+def test_half_mode_accepted(backward):
+    """rotary_mode 0 passes validation in both implementations: the oracle computes, the
+    library reaches the launch (which fails without a GPU)."""
+    lib_st, ora_st = call_inplace(*inplace_base(), 0, [0, 8], backward=backward)
+    assert ora_st == 0, oracle.last_error()
+    assert lib_st == ra.ROPE_ERR_RUNTIME and "launch" in ra.last_error()
 
 
 def test_binding_refuses_host_tensors():

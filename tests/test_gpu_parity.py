@@ -27,11 +27,11 @@ HALF = (torch.float16, torch.bfloat16)
 # in-place op
 # ------------------------------------------------------------------------------------------
 
-def check_inplace(x_before, x_after_gpu, cos, sin, sl, what):
+def check_inplace(x_before, x_after_gpu, cos, sin, sl, what, mode=1):
     """x_before: host copy of x before the call; the rest compared to the oracle."""
     x_cpu = x_before.clone()
     c_cpu, s_cpu = cos.cpu(), sin.cpu()
-    st, x64 = oracle.rope_partial_inplace(x_cpu, c_cpu, s_cpu, 1, sl, twin=True)
+    st, x64 = oracle.rope_partial_inplace(x_cpu, c_cpu, s_cpu, mode, sl, twin=True)
     assert st == 0, oracle.last_error()
     D = x_before.shape[-1]
     start, end = (0, D) if sl is None else sl
@@ -41,24 +41,26 @@ def check_inplace(x_before, x_after_gpu, cos, sin, sl, what):
     check_bits_equal(got[..., end:], x_before[..., end:], what + " [end,D)")
     if x_before.dtype in HALF:
         return check_half(got[..., start:end], x_cpu[..., start:end], what)
-    scale = inplace_scale(x_before, c_cpu, s_cpu, start, end)
+    scale = inplace_scale(x_before, c_cpu, s_cpu, start, end, mode)
     return check_f32(got[..., start:end], x64[..., start:end], scale, what)
 
 
 def run_inplace(case, stream=None):
     x = case.x.to(DEV)
     before = x.cpu()
-    ra.rope_partial_inplace(x, case.cos.to(DEV), case.sin.to(DEV), 1, case.partial_slice,
-                            stream=stream)
+    ra.rope_partial_inplace(x, case.cos.to(DEV), case.sin.to(DEV), case.rotary_mode,
+                            case.partial_slice, stream=stream)
     torch.cuda.synchronize()
     return before, x
 
 
-@pytest.mark.parametrize("cfg", ["inplace_f32_1x16x2x64", "inplace_bf16_8x4096x1x576_s512"])
+@pytest.mark.parametrize("cfg", ["inplace_f32_1x16x2x64", "inplace_bf16_8x4096x1x576_s512",
+                                 "inplace_half_bf16_8x4096x1x576_s512"])
 def test_inplace_configs_full(cfg):
     case = W.CONFIGS[cfg](DEV)
     before, x = run_inplace(case)
-    check_inplace(before, x, case.cos, case.sin, case.partial_slice, case.name)
+    check_inplace(before, x, case.cos, case.sin, case.partial_slice, case.name,
+                  case.rotary_mode)
 
 
 LAYOUTS = {"BSND": lambda B, S, N: (B, S, N), "BS1D": lambda B, S, N: (B, S, 1),
@@ -431,9 +433,10 @@ def test_binding_errors_touch_nothing():
 # backward of the in-place op ([IPRM §Python 接口与自动微分]; transpose of the pair map)
 # ------------------------------------------------------------------------------------------
 
-def check_backward(g_before, g_after_gpu, cos, sin, sl, what):
+def check_backward(g_before, g_after_gpu, cos, sin, sl, what, mode=1):
     ref = g_before.clone()
-    st, g64 = oracle.rope_partial_inplace_backward(ref, cos.cpu(), sin.cpu(), 1, sl, twin=True)
+    st, g64 = oracle.rope_partial_inplace_backward(ref, cos.cpu(), sin.cpu(), mode, sl,
+                                                   twin=True)
     assert st == 0, oracle.last_error()
     D = g_before.shape[-1]
     start, end = (0, D) if sl is None else sl
@@ -442,15 +445,7 @@ def check_backward(g_before, g_after_gpu, cos, sin, sl, what):
     check_bits_equal(got[..., end:], g_before[..., end:], what + " [end,D)")
     if g_before.dtype in HALF:
         return check_half(got[..., start:end], ref[..., start:end], what)
-    # scale of the transposed products: |g0 c0| + |g1 s1| and |g1 c1| + |g0 s0|
-    gs = as_f64(g_before)[..., start:end]
-    L = end - start
-    c = np.broadcast_to(as_f64(cos), gs.shape[:-1] + (L,))
-    s = np.broadcast_to(as_f64(sin), gs.shape[:-1] + (L,))
-    a, b = gs[..., 0::2], gs[..., 1::2]
-    scale = np.empty_like(gs)
-    scale[..., 0::2] = np.abs(a * c[..., 0::2]) + np.abs(b * s[..., 1::2])
-    scale[..., 1::2] = np.abs(b * c[..., 1::2]) + np.abs(a * s[..., 0::2])
+    scale = inplace_scale(g_before, cos.cpu(), sin.cpu(), start, end, mode, backward=True)
     return check_f32(got[..., start:end], g64[..., start:end], scale, what)
 
 
@@ -493,3 +488,59 @@ def test_autograd_wrapper_gradient():
     (y * w).sum().backward()
     torch.cuda.synchronize()
     check_backward(w.cpu(), x.grad, c, s, sl, "autograd")
+
+
+# ------------------------------------------------------------------------------------------
+# half mode, rotary_mode 0 (x1, x2 the two halves of the slice)
+# ------------------------------------------------------------------------------------------
+
+HALF_SHAPES = [((3, 37, 5, 96), [16, 80]),    # ragged rows, inner slice, vector path
+               ((2, 65, 3, 64), None),        # whole D
+               ((1, 300, 2, 40), [1, 37]),    # odd start: element path
+               ((2, 9, 2, 48), [8, 20]),      # halves of 6: element path for 16-bit types
+               ((4, 7, 1, 1024), [0, 1024]),  # D at its maximum
+               ((2, 3, 2, 10), [4, 6])]       # one pair per row
+
+
+@pytest.mark.parametrize("direction", ["forward", "backward"])
+@pytest.mark.parametrize("xdt,cdt", DTYPE_PAIRS, ids=lambda d: str(d).split(".")[-1])
+@pytest.mark.parametrize("layout", ["BSND", "BS1D", "B1ND", "111D"])
+@pytest.mark.parametrize("shape,sl", HALF_SHAPES)
+def test_half_mode_sweep(xdt, cdt, layout, shape, sl, direction):
+    B, S, N, D = shape
+    start, end = (0, D) if sl is None else sl
+    cshape = LAYOUTS[layout](B, S, N) + (end - start,)
+    case = W.inplace_case("half", B, S, N, D, xdt, cdt, sl, cos_shape=cshape, seed=B * 11 + S,
+                          table="randn", device=DEV, rotary_mode=0)
+    what = f"half {direction} {layout} {shape} {sl} {xdt}/{cdt}"
+    if direction == "forward":
+        before, x = run_inplace(case)
+        check_inplace(before, x, case.cos, case.sin, sl, what, mode=0)
+    else:
+        g = case.x
+        before = g.cpu()
+        ra.rope_partial_inplace_backward(g, case.cos, case.sin, 0, sl)
+        torch.cuda.synchronize()
+        check_backward(before, g, case.cos, case.sin, sl, what, mode=0)
+
+
+def test_half_mode_backward_full_and_autograd():
+    case = W.inplace_half_bf16_slice(DEV)
+    g = case.x
+    before = g.cpu()
+    ra.rope_partial_inplace_backward(g, case.cos, case.sin, 0, case.partial_slice)
+    torch.cuda.synchronize()
+    check_backward(before, g, case.cos, case.sin, case.partial_slice, "half backward full",
+                   mode=0)
+    # autograd wrapper in half mode: gradient of sum(w * y) is the backward op applied to w
+    x0 = W.randn((2, 16, 3, 64), torch.float32, W.generator(45, DEV))
+    c = W.randn((2, 16, 1, 32), torch.float32, W.generator(46, DEV))
+    s = W.randn((2, 16, 1, 32), torch.float32, W.generator(47, DEV))
+    w = W.randn((2, 16, 3, 64), torch.float32, W.generator(48, DEV))
+    xl = x0.clone().requires_grad_(True)
+    y = ra.InplacePartialRotaryMul.apply(xl * 1.0, c, s, [16, 48], 0)
+    (y * w).sum().backward()
+    expect = w.clone()
+    ra.rope_partial_inplace_backward(expect, c, s, 0, [16, 48])
+    torch.cuda.synchronize()
+    check_bits_equal(xl.grad.cpu(), expect.cpu(), "autograd half mode")

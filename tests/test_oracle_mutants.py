@@ -57,6 +57,13 @@ MUTANTS = [
      "else if (i % 3 == 2 && i < 3 * sec[1] - 3) row_sel = 2;", "interleaved"),
     ("f16 subnormal decode", "v = ldexpf((float)m, -24);", "v = ldexpf((float)m, -23);",
      "decoding"),
+    ("half mode rotate sign", "const float rot = i < h ? -v[i + h] : v[i - h];",
+     "const float rot = i < h ? v[i + h] : -v[i - h];", "half"),
+    ("half mode partner index", "const float rot = i < h ? -v[i + h] : v[i - h];",
+     "const float rot = i < h ? -v[h - 1 - i] : v[L - 1 - i];", "half"),
+    ("half mode backward sign", "q = -(v[i - h] * sp);", "q = v[i - h] * sp;", "half"),
+    ("half mode backward sin index", "const float sp = load_f32(sin_t, crow + i + h);",
+     "const float sp = load_f32(sin_t, crow + i);", "half"),
 ]
 
 

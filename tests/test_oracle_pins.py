@@ -43,9 +43,9 @@ def raw_bits(t):
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def run_inplace(x, cos, sin, sl, twin=False):
+def run_inplace(x, cos, sin, sl, twin=False, mode=1):
     x = x.clone()
-    st, x64 = oracle.rope_partial_inplace(x, cos, sin, 1, sl, twin=twin)
+    st, x64 = oracle.rope_partial_inplace(x, cos, sin, mode, sl, twin=twin)
     assert st == oracle.OK, oracle.last_error()
     return x, x64
 
@@ -484,9 +484,9 @@ def test_oracle_refuses_out_of_range_positions_without_writing():
 # Backward of the in-place op ([IPRM §Python 接口与自动微分]; the transpose of the pair map)
 # ------------------------------------------------------------------------------------------
 
-def run_backward(g, cos, sin, sl, twin=False):
+def run_backward(g, cos, sin, sl, twin=False, mode=1):
     g = g.clone()
-    st, g64 = oracle.rope_partial_inplace_backward(g, cos, sin, 1, sl, twin=twin)
+    st, g64 = oracle.rope_partial_inplace_backward(g, cos, sin, mode, sl, twin=twin)
     assert st == oracle.OK, oracle.last_error()
     return g, g64
 
@@ -676,3 +676,131 @@ def test_interleaved_equal_rows_and_rope_mode_and_validation():
     st, *_ = run_cache_v2(p.repeat(4, 1).contiguous(), q, q[:, :H].clone(), cache,
                           [16, 16, 16, 16], H, True, 1)
     assert st == oracle.ERR_PARAM_INVALID
+
+
+# ------------------------------------------------------------------------------------------
+# Half mode, rotary_mode = 0 ([IPRM §参数说明]; reading R21: x1, x2 are the slice's halves)
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("direction", ["forward", "backward"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+def test_golden_half_mode(dt, direction):
+    gj = golden("t9_half_mode.json")
+    x = torch.tensor(gj["x"], dtype=DT[dt]).reshape(gj["x_shape"])
+    c = torch.tensor(gj["cos"], dtype=DT[dt]).reshape(1, 1, 1, 4)
+    s = torch.tensor(gj["sin"], dtype=DT[dt]).reshape(1, 1, 1, 4)
+    run = run_inplace if direction == "forward" else run_backward
+    y, _ = run(x, c, s, gj["partial_slice"], mode=0)
+    assert f64(y).ravel().tolist() == gj[f"expected_{direction}"]
+
+
+def half_to_interleave(n):
+    """Index map taking a slice in half layout (x1 then x2) to the interleaved layout:
+    interleaved element 2i is half element i, 2i+1 is half element i + n/2."""
+    h = n // 2
+    idx = np.empty(n, dtype=np.int64)
+    idx[0::2] = np.arange(h)
+    idx[1::2] = np.arange(h) + h
+    return idx
+
+
+@pytest.mark.parametrize("direction", ["forward", "backward"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_half_mode_is_interleave_after_permutation(dt, direction):
+    """Half mode on (x, cos, sin) equals interleave mode (pinned on its own) on the same slice
+    with its elements, cos and sin permuted so that the pairs (i, i + L/2) become adjacent:
+    bit for bit, since each output is the same two float32 products and one sum."""
+    gen = torch.Generator().manual_seed(41)
+    B_, S, N, D, sl = 2, 5, 3, 40, [6, 38]
+    L = sl[1] - sl[0]
+    x = torch.randn(B_, S, N, D, generator=gen).to(DT[dt])
+    c = torch.randn(B_, S, 1, L, generator=gen).to(DT[dt])
+    s = torch.randn(B_, S, 1, L, generator=gen).to(DT[dt])
+    perm = torch.from_numpy(half_to_interleave(L))
+    xp = x.clone()
+    xp[..., sl[0]:sl[1]] = x[..., sl[0]:sl[1]][..., perm]
+    run = run_inplace if direction == "forward" else run_backward
+    y_half, _ = run(x, c, s, sl, mode=0)
+    y_int, _ = run(xp, c[..., perm].contiguous(), s[..., perm].contiguous(), sl, mode=1)
+    back = y_int.clone()
+    back[..., sl[0] + perm] = y_int[..., sl[0]:sl[1]]
+    assert (raw_bits(y_half) == raw_bits(back)).all()
+
+
+@pytest.mark.parametrize("cos_layout", ["BSND", "BS1D", "B11D", "111D"])
+def test_half_mode_matches_complex_multiplication(cos_layout):
+    """With the rotate-half table layout (cos[i] = cos[i + L/2] = cos(theta_i), same for sin),
+    half mode multiplies z_i = x[i] + j x[i + L/2] by e^{j theta_i} (NumPy complex128)."""
+    B_, S, N, D, sl = 2, 6, 4, 48, [8, 40]
+    L, h = sl[1] - sl[0], (sl[1] - sl[0]) // 2
+    cshape = {"BSND": (B_, S, N, h), "BS1D": (B_, S, 1, h), "B11D": (B_, 1, 1, h),
+              "111D": (1, 1, 1, h)}[cos_layout]
+    gen = torch.Generator().manual_seed(42)
+    x = torch.randn(B_, S, N, D, generator=gen, dtype=torch.float64)
+    theta = torch.rand(cshape, generator=gen, dtype=torch.float64) * 6.283
+    c = torch.cat([torch.cos(theta)] * 2, dim=-1).float()
+    s = torch.cat([torch.sin(theta)] * 2, dim=-1).float()
+    xf = x.float()
+    _, y64 = run_inplace(xf, c, s, sl, twin=True, mode=0)
+    xs = f64(xf)[..., sl[0]:sl[1]]
+    z = xs[..., :h] + 1j * xs[..., h:]
+    # the float32 tables' own (cos, sin) as the unit complex number e^{j theta}
+    rot = np.broadcast_to(f64(c)[..., :h] + 1j * f64(s)[..., :h], z.shape)
+    w = z * rot
+    np.testing.assert_allclose(y64[..., sl[0]:sl[0] + h], w.real, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(y64[..., sl[0] + h:sl[1]], w.imag, rtol=0, atol=1e-12)
+    assert (y64[..., :sl[0]] == f64(xf)[..., :sl[0]]).all()
+    assert (y64[..., sl[1]:] == f64(xf)[..., sl[1]:]).all()
+
+
+def test_half_mode_backward_adjoint_and_autograd():
+    """<F(x), v> = <x, B(v)> with per-element tables, and B equals PyTorch autograd of the
+    half-mode forward written with torch.chunk / torch.cat in float64."""
+    B_, S, N, D, sl = 2, 4, 3, 36, [4, 36]
+    L = sl[1] - sl[0]
+    gen = torch.Generator().manual_seed(43)
+    x = torch.randn(B_, S, N, D, generator=gen, dtype=torch.float64)
+    v = torch.randn(B_, S, N, D, generator=gen, dtype=torch.float64)
+    c = torch.randn(B_, S, 1, L, generator=gen, dtype=torch.float64)
+    s = torch.randn(B_, S, 1, L, generator=gen, dtype=torch.float64)
+    _, fx = run_inplace(x.float(), c.float(), s.float(), sl, twin=True, mode=0)
+    _, bv = run_backward(v.float(), c.float(), s.float(), sl, twin=True, mode=0)
+    lhs = float((fx * f64(v.float())).sum())
+    rhs = float((f64(x.float()) * bv).sum())
+    assert abs(lhs - rhs) <= 1e-12 * (abs(lhs) + abs(rhs) + 1)
+
+    xr = x.float().double().requires_grad_(True)
+    cf, sf = c.float().double(), s.float().double()
+    part = xr[..., sl[0]:sl[1]]
+    x1, x2 = torch.chunk(part, 2, dim=-1)
+    y = torch.cat([xr[..., :sl[0]], part * cf + torch.cat((-x2, x1), dim=-1) * sf,
+                   xr[..., sl[1]:]], dim=-1)
+    (grad,) = torch.autograd.grad(y, xr, v.float().double())
+    np.testing.assert_allclose(bv, grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_half_mode_untouched_noop_and_inverse():
+    gen = torch.Generator().manual_seed(44)
+    x = torch.randn(2, 3, 2, 20, generator=gen).to(torch.bfloat16)
+    c = torch.randn(2, 3, 1, 8, generator=gen).to(torch.bfloat16)
+    out, _ = run_inplace(x, c, c.clone(), [6, 14], mode=0)
+    assert (raw_bits(out)[..., :6] == raw_bits(x)[..., :6]).all()
+    assert (raw_bits(out)[..., 14:] == raw_bits(x)[..., 14:]).all()
+    same, _ = run_inplace(x, c, c.clone(), [6, 6], mode=0)
+    assert (raw_bits(same) == raw_bits(x)).all()
+    # rotate-half tables: the gradient op undoes the rotation (R^T R = I)
+    theta = torch.rand(2, 3, 1, 16, generator=gen, dtype=torch.float64) * 6.283
+    cc = torch.cat([torch.cos(theta)] * 2, -1).float()
+    ss = torch.cat([torch.sin(theta)] * 2, -1).float()
+    xf = torch.randn(2, 3, 2, 40, generator=gen)
+    y, _ = run_inplace(xf, cc, ss, [4, 36], mode=0)
+    back, _ = run_backward(y, cc, ss, [4, 36], mode=0)
+    np.testing.assert_allclose(f64(back), f64(xf), rtol=0, atol=1e-5)
+
+
+def test_rotary_modes_other_than_0_and_1_refused():
+    x = torch.zeros(1, 2, 1, 8)
+    c = torch.zeros(1, 2, 1, 8)
+    for mode in (2, 3, -1):
+        st, _ = oracle.rope_partial_inplace(x, c, c, mode, None)
+        assert st == oracle.ERR_PARAM_INVALID
