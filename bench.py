@@ -167,6 +167,44 @@ def traffic_for(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def size_sweep(torch, ra, W, dev, cyc):
+    """Per-launch time of the same kernels at growing token counts, and the least-squares fit
+    time = fixed + bytes / marginal_rate: the fixed part is what bounds a short launch."""
+    import numpy as np
+    shapes = {
+        "inplace_rope_kernel": [
+            (f"bf16 x [{8 * m},4096,1,576] slice [512,576) f32 cos/sin", m,
+             lambda m=m: W.inplace_case("sweep", 8 * m, 4096, 1, 576, torch.bfloat16,
+                                        torch.float32, [512, 576], seed=1100 + m, device=dev))
+            for m in (1, 2, 4, 8, 16)],
+        "cos_sin_cache_kernel": [
+            (f"rope NeoX bf16 T={8192 * m} q 32x128 k 8x128", m,
+             lambda m=m: W.cache_case("sweep", 8192 * m, 32, 8, 128, 128, torch.bfloat16, True,
+                                      32768, seed=1200 + m, device=dev))
+            for m in (1, 2, 4, 8)],
+    }
+    out = {}
+    for kern, rows in shapes.items():
+        pts = []
+        for what, m, make in rows:
+            case = make()
+            n_sets = n_sets_for(case.algo_bytes)
+            calls = (inplace_calls(ra, case, n_sets) if hasattr(case, "x")
+                     else cache_calls(ra, torch, case, n_sets))
+            us = time_launches(torch, calls, 100, 10, cyc) * 1e3
+            pts.append({"workload": what, "tokens": case.tokens, "bytes": case.algo_bytes,
+                        "us": round(us, 3), "gbs": round(case.algo_bytes / us / 1e3, 1)})
+            log(f"sweep {kern} {what}: {us:.3f} us, {case.algo_bytes / us / 1e3:.0f} GB/s")
+            del calls, case
+            torch.cuda.empty_cache()
+        b = np.array([p["bytes"] for p in pts], dtype=np.float64)
+        t = np.array([p["us"] for p in pts], dtype=np.float64)
+        slope, fixed = np.polyfit(b, t, 1)
+        out[kern] = {"points": pts, "fit_fixed_us": round(float(fixed), 3),
+                     "fit_marginal_gbs": round(float(1e-3 / slope), 1)}
+    return {"sweep": out, "kernel_source_sha256_16": kernel_source_hash()}
+
+
 # ------------------------------------------------------------------------------------------
 # CPU baseline: the oracle, as it stands, on the host
 # ------------------------------------------------------------------------------------------
@@ -210,12 +248,17 @@ def main() -> int:
                          "cache_mrope_neox_bf16_t16384",
                          "inplace_backward_bf16_8x4096x1x576_s512",
                          "cache_mrope_interleaved_neox_bf16_t16384",
-                         "inplace_half_bf16_8x4096x1x576_s512"]),
+                         "inplace_half_bf16_8x4096x1x576_s512",
+                         "inplace_heads_bf16_4x2048x32x192_s128_bs1d"]),
                     help="first is the headline; the rest are reported under `kernels`")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--resident", action="store_true",
                     help="also time without buffer rotation (Infinity-Cache-resident)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark line, time the headline in-place shape and "
+                         "the rope NeoX cache shape at 1..16x their tokens and fit fixed cost "
+                         "+ bytes / marginal bandwidth (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -235,6 +278,9 @@ def main() -> int:
     log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), "
         f"{props.multi_processor_count} CUs")
     cyc = spin_cycles_per_ms(torch)
+    if args.sweep:
+        print(json.dumps(size_sweep(torch, ra, W, dev, cyc)), flush=True)
+        return 0
     names = [w.strip() for w in args.workloads.split(",") if w.strip()]
     results = {}
     cases = {}
@@ -251,7 +297,8 @@ def main() -> int:
              "us_per_launch": round(ms * 1e3, 3), "gbs": round(gbs, 1),
              "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
              "tokens_per_s": round(case.tokens / (ms * 1e-3), 1),
-             "algo_bytes_per_launch": case.algo_bytes, "buffer_sets": n_sets, "steps": steps}
+             "algo_bytes_per_launch": case.algo_bytes, "buffer_sets": n_sets, "steps": steps,
+             "traffic": traffic_for(name)}
         if args.resident:
             ms_r = time_launches(torch, calls[:1], steps, args.warmup, cyc)
             r["resident_us_per_launch"] = round(ms_r * 1e3, 3)

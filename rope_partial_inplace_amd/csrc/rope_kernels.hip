@@ -217,6 +217,40 @@ __device__ inline void store_n(void *p, int64_t i, const float *f) {
   }
 }
 
+// BYTES (8 or a multiple of 16) raw bytes in 32-bit words: lets a lane issue all of its
+// loads before converting any of them (converting at once makes the compiler wait for each
+// load in turn to keep fewer registers live).
+template <int BYTES>
+struct Words {
+  static_assert(BYTES == 8 || BYTES % 16 == 0, "8 bytes or a multiple of 16");
+  uint32_t w[BYTES / 4];
+};
+
+template <int BYTES, bool NT>
+__device__ inline void load_words(const void *p, Words<BYTES> &r) {
+  if constexpr (BYTES == 8) {
+    const u32x2 v = ld8<NT>(p);
+    r.w[0] = v.x;
+    r.w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int c = 0; c < BYTES / 16; ++c) {
+      const u32x4 v = ld16<NT>(static_cast<const char *>(p) + 16 * c);
+      r.w[4 * c] = v.x;
+      r.w[4 * c + 1] = v.y;
+      r.w[4 * c + 2] = v.z;
+      r.w[4 * c + 3] = v.w;
+    }
+  }
+}
+
+template <typename T, int N>
+__device__ inline void words_to_floats(const Words<N * int(sizeof(T))> &r, float *f) {
+#pragma unroll
+  for (int q = 0; q < N * int(sizeof(T)) / 4; ++q)
+    Io<T>::word_to_floats(r.w[q], f + q * Io<T>::kPerWord);
+}
+
 // Raw copy of N elements (pass-through data is moved as bits, never converted).
 template <typename T, int N, bool VEC>
 struct RawN {
@@ -318,84 +352,116 @@ __device__ inline void rotate_pair(float a, float b, float c0, float c1, float s
 
 // ============================================================================================
 // K1: in-place partial RoPE ([IPRM §计算原理与公式], [IPRM §partial_slice 局部旋转机制]).
-// Interleave mode: a lane owns K chunks of V slice elements (V/2 pairs); chunks of one row
-// are adjacent lanes, so a wavefront reads and writes whole 16-byte-aligned runs of each
-// row's slice.  HALF (rotary_mode 0, [IPRM §参数说明]; x1, x2 the two halves of the slice,
+// Interleave mode: a lane owns a chunk of V slice elements (V/2 pairs); chunks of one row are
+// adjacent lanes, so a wavefront reads and writes whole 16-byte-aligned runs of each row's
+// slice.  HALF (rotary_mode 0, [IPRM §参数说明]; x1, x2 the two halves of the slice,
 // x_rotate = cat(-x2, x1)): a lane owns chunk u of the first half and chunk u of the second,
 // so every pair (i, i + L/2) is lane-local and both halves are read as contiguous runs.
-// Elements outside [start, end) are never touched.  cos/sin rows are addressed with zero
-// strides on broadcast dims (BSND, BS1D, B1ND, B11D, 111D and mixed forms).  BWD runs the
-// transpose of the pair map on an incoming gradient (same access pattern).  x is streamed
-// (non-temporal); cos/sin are streamed too unless a row is shared by several x rows
-// (broadcast), where the caches serve the repeats.
+// NHL > 1 (cos/sin broadcast over the heads): the lane owns its chunk in NHL consecutive
+// heads of one (b, s) and loads the cos/sin chunk once for all of them.  Elements outside
+// [start, end) are never touched.  cos/sin rows are addressed with zero strides on broadcast
+// dims (BSND, BS1D, B1ND, B11D, 111D and mixed forms).  BWD runs the transpose of the pair map
+// on an incoming gradient (same access pattern).  x is streamed (non-temporal); cos/sin are
+// streamed too when each of their rows is read by one lane group, else (broadcast) loaded
+// normally so that the caches serve the repeats.
 // ============================================================================================
-template <typename XT, typename CT, bool VEC, int K, bool CNT, bool BWD, bool HALF>
-__global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
+// One lane item: chunk `chunk` of the NHL x rows starting at row r * NHL, whose cos/sin row
+// is that of (b, s, head g * NHL).
+template <typename XT, typename CT, bool VEC, int NHL, bool CNT, bool BWD, bool HALF>
+__device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, uint64_t chunk,
+                                             uint64_t b, uint64_t s, uint64_t g) {
   // one 16-byte access per lane for the wider of x and cos/sin, 8 bytes for the narrower;
   // element access: one pair (2 elements) in interleave mode, one element per half in HALF
   constexpr int V =
       VEC ? 16 / (sizeof(XT) > sizeof(CT) ? int(sizeof(XT)) : int(sizeof(CT))) : (HALF ? 1 : 2);
-  constexpr int NH = HALF ? 2 : 1;  // chunks per lane item: one, or one in each half
-  const uint64_t items = uint64_t(p.items);
-  const uint64_t per_block = uint64_t(kBlock) * K;
+  constexpr int NH = HALF ? 2 : 1;          // chunks per head: one, or one in each half
   const int64_t hoff = HALF ? p.L / 2 : 0;  // offset of the second half
-  for (uint64_t base = uint64_t(blockIdx.x) * per_block; base < items;
-       base += uint64_t(gridDim.x) * per_block) {
-    float xv[K][NH][V], cv[K][NH][V], sv[K][NH][V];
-    int64_t xoff[K];
+  const int64_t crow = int64_t(b) * p.cb + int64_t(s) * p.cs + int64_t(g) * NHL * p.cn;
+  const int64_t coff = crow * p.L + int64_t(chunk) * V;
+  const int64_t x0 = int64_t(r) * NHL * p.D + p.start + int64_t(chunk) * V;
+  float xv[NHL][NH][V], cv[NH][V], sv[NH][V];
+  if constexpr (VEC) {
+    constexpr int XB = V * int(sizeof(XT)), CB = V * int(sizeof(CT));
+    Words<XB> xr[NHL][NH];
+    Words<CB> cr[NH], sr[NH];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const uint64_t it = base + uint64_t(k) * kBlock + threadIdx.x;
-      xoff[k] = -1;
-      if (it >= items) continue;
-      uint64_t row, chunk, n, s, b;
-      if (p.idx32) {
-        const uint32_t i32 = uint32_t(it);
-        const uint32_t r32 = fdiv(p.div_cpr, i32);
-        chunk = i32 - r32 * p.chunks_per_row;
-        const uint32_t bs = fdiv(p.div_n, r32);
-        n = r32 - bs * uint32_t(p.N);
-        const uint32_t b32 = fdiv(p.div_s, bs);
-        s = bs - b32 * uint32_t(p.S);
-        b = b32;
-        row = r32;
-      } else {
-        row = it / p.chunks_per_row;
-        chunk = it - row * p.chunks_per_row;
-        const uint64_t bs = row / uint64_t(p.N);
-        n = row - bs * uint64_t(p.N);
-        b = bs / uint64_t(p.S);
-        s = bs - b * uint64_t(p.S);
-      }
-      const int64_t crow = int64_t(b) * p.cb + int64_t(s) * p.cs + int64_t(n) * p.cn;
-      const int64_t coff = crow * p.L + int64_t(chunk) * V;
-      xoff[k] = int64_t(row) * p.D + p.start + int64_t(chunk) * V;
+    for (int j = 0; j < NHL; ++j)
 #pragma unroll
-      for (int hh = 0; hh < NH; ++hh) {
-        load_n<XT, V, VEC, true>(p.x, xoff[k] + hh * hoff, xv[k][hh]);
-        load_n<CT, V, VEC, CNT>(p.cos, coff + hh * hoff, cv[k][hh]);
-        load_n<CT, V, VEC, CNT>(p.sin, coff + hh * hoff, sv[k][hh]);
-      }
+      for (int hh = 0; hh < NH; ++hh)
+        load_words<XB, true>(static_cast<const XT *>(p.x) + x0 + j * p.D + hh * hoff, xr[j][hh]);
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      load_words<CB, CNT>(static_cast<const CT *>(p.cos) + coff + hh * hoff, cr[hh]);
+      load_words<CB, CNT>(static_cast<const CT *>(p.sin) + coff + hh * hoff, sr[hh]);
     }
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      if (xoff[k] < 0) continue;
-      if constexpr (HALF) {
-        float ya[V], yb[V];
+    for (int hh = 0; hh < NH; ++hh) {
 #pragma unroll
-        for (int e = 0; e < V; ++e)
-          rotate_pair<BWD>(xv[k][0][e], xv[k][1][e], cv[k][0][e], cv[k][1][e], sv[k][0][e],
-                           sv[k][1][e], ya[e], yb[e]);
-        store_n<XT, V, VEC, true>(p.x, xoff[k], ya);
-        store_n<XT, V, VEC, true>(p.x, xoff[k] + hoff, yb);
-      } else {
-        float y[V];
+      for (int j = 0; j < NHL; ++j) words_to_floats<XT, V>(xr[j][hh], xv[j][hh]);
+      words_to_floats<CT, V>(cr[hh], cv[hh]);
+      words_to_floats<CT, V>(sr[hh], sv[hh]);
+    }
+  } else {
 #pragma unroll
-        for (int e = 0; e < V; e += 2)
-          rotate_pair<BWD>(xv[k][0][e], xv[k][0][e + 1], cv[k][0][e], cv[k][0][e + 1],
-                           sv[k][0][e], sv[k][0][e + 1], y[e], y[e + 1]);
-        store_n<XT, V, VEC, true>(p.x, xoff[k], y);
-      }
+    for (int j = 0; j < NHL; ++j)
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+        load_n<XT, V, false, true>(p.x, x0 + j * p.D + hh * hoff, xv[j][hh]);
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      load_n<CT, V, false, CNT>(p.cos, coff + hh * hoff, cv[hh]);
+      load_n<CT, V, false, CNT>(p.sin, coff + hh * hoff, sv[hh]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NHL; ++j) {
+    if constexpr (HALF) {
+      float ya[V], yb[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        rotate_pair<BWD>(xv[j][0][e], xv[j][1][e], cv[0][e], cv[1][e], sv[0][e], sv[1][e],
+                         ya[e], yb[e]);
+      store_n<XT, V, VEC, true>(p.x, x0 + j * p.D, ya);
+      store_n<XT, V, VEC, true>(p.x, x0 + j * p.D + hoff, yb);
+    } else {
+      float y[V];
+#pragma unroll
+      for (int e = 0; e < V; e += 2)
+        rotate_pair<BWD>(xv[j][0][e], xv[j][0][e + 1], cv[0][e], cv[0][e + 1], sv[0][e],
+                         sv[0][e + 1], y[e], y[e + 1]);
+      store_n<XT, V, VEC, true>(p.x, x0 + j * p.D, y);
+    }
+  }
+}
+
+template <typename XT, typename CT, bool VEC, int NHL, bool CNT, bool BWD, bool HALF>
+__global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
+  // item it -> (row group r = (b, s, head group g), chunk).  Two loops: 32-bit indices with
+  // multiply-high division (the usual case), and plain 64-bit division for huge tensors, kept
+  // apart so that the 64-bit division setup never runs in the 32-bit case.
+  if (p.idx32) {
+    const uint32_t items = uint32_t(p.items), ng = uint32_t(p.N / NHL);
+    for (uint32_t it = blockIdx.x * uint32_t(kBlock) + threadIdx.x; it < items;
+         it += gridDim.x * uint32_t(kBlock)) {
+      const uint32_t r = fdiv(p.div_cpr, it);
+      const uint32_t chunk = it - r * p.chunks_per_row;
+      const uint32_t bs = fdiv(p.div_ng, r);
+      const uint32_t g = r - bs * ng;
+      const uint32_t b = fdiv(p.div_s, bs);
+      const uint32_t s = bs - b * uint32_t(p.S);
+      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF>(p, r, chunk, b, s, g);
+    }
+  } else {
+    const uint64_t items = uint64_t(p.items), ng = uint64_t(p.N) / NHL;
+    for (uint64_t it = uint64_t(blockIdx.x) * kBlock + threadIdx.x; it < items;
+         it += uint64_t(gridDim.x) * kBlock) {
+      const uint64_t r = it / p.chunks_per_row;
+      const uint64_t chunk = it - r * p.chunks_per_row;
+      const uint64_t bs = r / ng;
+      const uint64_t g = r - bs * ng;
+      const uint64_t b = bs / uint64_t(p.S);
+      const uint64_t s = bs - b * uint64_t(p.S);
+      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF>(p, r, chunk, b, s, g);
     }
   }
 }
@@ -763,25 +829,27 @@ int launch(const void *fn, int64_t blocks, int threads, size_t lds, void *stream
 }
 
 template <typename XT, typename CT, bool BWD, bool HALF>
-const void *pick_inplace(bool vec, bool cos_stream) {
-  constexpr int K = kInplaceItemsPerLane;
-  if (vec)
-    return cos_stream ? reinterpret_cast<const void *>(
-                            &inplace_rope_kernel<XT, CT, true, K, true, BWD, HALF>)
-                      : reinterpret_cast<const void *>(
-                            &inplace_rope_kernel<XT, CT, true, K, false, BWD, HALF>);
-  return reinterpret_cast<const void *>(&inplace_rope_kernel<XT, CT, false, K, false, BWD, HALF>);
+const void *pick_inplace(const InplacePlan &p) {
+#define ROPE_K1(VEC, NHL, CNT) \
+  reinterpret_cast<const void *>(&inplace_rope_kernel<XT, CT, VEC, NHL, CNT, BWD, HALF>)
+  if (!p.vector_io) return ROPE_K1(false, 1, false);
+  if (p.nhl == 1) return p.cos_stream ? ROPE_K1(true, 1, true) : ROPE_K1(true, 1, false);
+  if (p.nhl == 2) return p.cos_stream ? ROPE_K1(true, 2, true) : ROPE_K1(true, 2, false);
+  if (p.nhl == 4) return p.cos_stream ? ROPE_K1(true, 4, true) : ROPE_K1(true, 4, false);
+  if constexpr (!HALF)
+    return p.cos_stream ? ROPE_K1(true, 8, true) : ROPE_K1(true, 8, false);
+  return nullptr;  // the plan never gives half mode 8 heads per lane
+#undef ROPE_K1
 }
 
 template <bool BWD, bool HALF>
 const void *pick_inplace_dtype(const InplacePlan &p) {
-  const bool v = p.vector_io, cs = p.cos_stream;
-  if (p.xdt == ROPE_F32) return pick_inplace<float, float, BWD, HALF>(v, cs);
+  if (p.xdt == ROPE_F32) return pick_inplace<float, float, BWD, HALF>(p);
   if (p.xdt == ROPE_F16)
-    return p.cdt == ROPE_F32 ? pick_inplace<_Float16, float, BWD, HALF>(v, cs)
-                             : pick_inplace<_Float16, _Float16, BWD, HALF>(v, cs);
-  return p.cdt == ROPE_F32 ? pick_inplace<__bf16, float, BWD, HALF>(v, cs)
-                           : pick_inplace<__bf16, __bf16, BWD, HALF>(v, cs);
+    return p.cdt == ROPE_F32 ? pick_inplace<_Float16, float, BWD, HALF>(p)
+                             : pick_inplace<_Float16, _Float16, BWD, HALF>(p);
+  return p.cdt == ROPE_F32 ? pick_inplace<__bf16, float, BWD, HALF>(p)
+                           : pick_inplace<__bf16, __bf16, BWD, HALF>(p);
 }
 
 template <typename T, bool MULTI>
@@ -827,8 +895,11 @@ int run_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor 
                                          : pick_inplace_dtype<false, true>(plan))
                             : (backward ? pick_inplace_dtype<true, false>(plan)
                                         : pick_inplace_dtype<false, false>(plan));
-  const int64_t per_block = int64_t(kBlock) * kInplaceItemsPerLane;
-  return launch(fn, (plan.items + per_block - 1) / per_block, kBlock, 0, stream, &plan);
+  if (fn == nullptr) {
+    g_last_error = "internal: no kernel for this plan";
+    return ROPE_ERR_RUNTIME;
+  }
+  return launch(fn, (plan.items + kBlock - 1) / kBlock, kBlock, 0, stream, &plan);
 }
 
 }  // namespace

@@ -166,8 +166,7 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
   p.cn = cos->shape[2] == 1 ? 0 : 1;
   p.cs = cos->shape[1] == 1 ? 0 : Nc;
   p.cb = cos->shape[0] == 1 ? 0 : Sc * Nc;
-  p.cos_stream = (cos->shape[0] == p.B || p.B == 1) && (cos->shape[1] == p.S || p.S == 1) &&
-                 (cos->shape[2] == p.N || p.N == 1);
+  const bool bs_stream = (cos->shape[0] == p.B || p.B == 1) && (cos->shape[1] == p.S || p.S == 1);
 
   // Lane chunks of V elements: a 16-byte access for the wider of x and cos/sin (8 bytes for
   // the narrower) when every chunk start is aligned to its access size; else element access.
@@ -184,12 +183,25 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
   p.vector_io = aligned;
   p.vec = aligned ? uint32_t(v) : (p.half ? 1u : 2u);
   p.chunks_per_row = uint32_t(span / p.vec);
-  p.items = p.rows * p.chunks_per_row;
+  // Heads per lane: with cos/sin broadcast over N, a lane rotates its chunk in nhl consecutive
+  // heads with one cos/sin load (the largest of 8, 4, 2 that divides N; 4 at most in half
+  // mode, whose lanes already hold two chunks per head).  Vector path only.
+  p.nhl = 1;
+  if (p.cn == 0 && p.N > 1 && p.vector_io)
+    for (uint32_t c : {8u, 4u, 2u})
+      if (p.N % c == 0 && !(p.half && c > 4)) {
+        p.nhl = c;
+        break;
+      }
+  // cos/sin are streamed (non-temporal) when each cos/sin row is read by one lane group only
+  p.cos_stream = bs_stream && (cos->shape[2] == p.N || p.N == int64_t(p.nhl));
+  const int64_t ng = p.N / p.nhl;
+  p.items = p.B * p.S * ng * p.chunks_per_row;
   p.idx32 = p.items < (int64_t(1) << 32);
   p.div_cpr = make_fastdiv(p.chunks_per_row);
-  p.div_n = make_fastdiv(uint32_t(std::min<int64_t>(p.N, 0xffffffff)));
+  p.div_ng = make_fastdiv(uint32_t(std::min<int64_t>(ng, 0xffffffff)));
   p.div_s = make_fastdiv(uint32_t(std::min<int64_t>(p.S, 0xffffffff)));
-  if (p.N > 0xffffffffLL || p.S > 0xffffffffLL) p.idx32 = false;
+  if (ng > 0xffffffffLL || p.S > 0xffffffffLL) p.idx32 = false;
   return ROPE_OK;
 }
 

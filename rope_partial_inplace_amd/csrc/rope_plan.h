@@ -40,9 +40,12 @@ inline uint32_t fastdiv_host(const FastDiv &f, uint32_t n) {
 // `vec` elements; one GPU lane owns one chunk (all pairs of a chunk are lane-local because
 // vec is even and chunks start at even offsets from the slice start).  Half mode: the first
 // half of the slice is cut into chunks; the lane owning chunk u also owns chunk u of the
-// second half, which holds the partners (i + L/2) of its elements.
+// second half, which holds the partners (i + L/2) of its elements.  When cos/sin are shared
+// by the heads of a (b, s) (broadcast over N), a lane owns that chunk of `nhl` consecutive
+// heads and loads the cos/sin chunk once for all of them.
 struct InplacePlan {
   bool half = false;  // rotary_mode 0
+  uint32_t nhl = 1;   // heads per lane (1, 2, 4 or 8); > 1 only when cos/sin broadcast over N
   rope_dtype xdt = ROPE_F32, cdt = ROPE_F32;
   bool vector_io = false;  // 16-byte x accesses (else one element at a time)
   bool noop = false;       // nothing to launch
@@ -50,14 +53,14 @@ struct InplacePlan {
   const void *cos = nullptr, *sin = nullptr;
   int64_t B = 0, S = 0, N = 0, D = 0, start = 0, L = 0;
   int64_t rows = 0;             // B*S*N
-  int64_t items = 0;            // rows * chunks_per_row
+  int64_t items = 0;            // (rows / nhl) * chunks_per_row
   uint32_t vec = 2;             // elements per lane chunk
   uint32_t chunks_per_row = 0;  // L / vec (half mode: (L/2) / vec)
   // cos/sin row of x-row (b, s, n) = b*cb + s*cs + n*cn (in rows of L elements)
   int64_t cb = 0, cs = 0, cn = 0;
-  bool cos_stream = false;  // every cos/sin row is read by exactly one x row (no broadcast)
+  bool cos_stream = false;  // every cos/sin row is read by exactly one lane group (streamed)
   bool idx32 = true;  // rows and items fit in 32 bits: use FastDiv below
-  FastDiv div_cpr, div_n, div_s;
+  FastDiv div_cpr, div_ng, div_s;  // by chunks_per_row, N / nhl, S
 };
 
 // ---- cos/sin cache --------------------------------------------------------------------------
@@ -109,7 +112,6 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
 constexpr int kBlock = 1024;      // in-place kernel workgroup (few, large workgroups: the
                                   // headline launch is short and dispatch-bound)
 constexpr int kCacheBlock = 256;  // cache kernel workgroup (one token tile)
-constexpr int kInplaceItemsPerLane = 1;
 constexpr int kNeoxItemsPerLane = 2;  // NeoX units are two vectors
 constexpr int kGptjItemsPerLane = 2;  // GPT-J units are one vector
 

@@ -217,6 +217,14 @@ def inplace_half_bf16_slice(device="cpu"):
                         rotary_mode=0)
 
 
+def inplace_heads_bf16_bs1d(device="cpu"):
+    """Query-side shape of the same layout family: bf16 x [4,2048,32,192], rope slice
+    [128,192) in each of 32 heads, fp32 cos/sin [4,2048,1,64] shared by the heads (BS1D)."""
+    return inplace_case("inplace_heads_bf16x_f32cs_4x2048x32x192_slice128_192_bs1d", 4, 2048, 32,
+                        192, torch.bfloat16, torch.float32, [128, 192], seed=1008,
+                        device=device)
+
+
 def inplace_bf16_slice_backward(device="cpu"):
     """The gradient op on the headline shape: incoming gradient bf16 [8,4096,1,576]."""
     case = inplace_bf16_slice(device)
@@ -235,5 +243,6 @@ CONFIGS = {
 CONFIGS["inplace_backward_bf16_8x4096x1x576_s512"] = inplace_bf16_slice_backward
 CONFIGS["cache_mrope_interleaved_neox_bf16_t16384"] = cache_mrope_interleaved
 CONFIGS["inplace_half_bf16_8x4096x1x576_s512"] = inplace_half_bf16_slice
+CONFIGS["inplace_heads_bf16_4x2048x32x192_s128_bs1d"] = inplace_heads_bf16_bs1d
 HEADLINE = "inplace_bf16_8x4096x1x576_s512"
 

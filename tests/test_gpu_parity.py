@@ -55,7 +55,8 @@ def run_inplace(case, stream=None):
 
 
 @pytest.mark.parametrize("cfg", ["inplace_f32_1x16x2x64", "inplace_bf16_8x4096x1x576_s512",
-                                 "inplace_half_bf16_8x4096x1x576_s512"])
+                                 "inplace_half_bf16_8x4096x1x576_s512",
+                                 "inplace_heads_bf16_4x2048x32x192_s128_bs1d"])
 def test_inplace_configs_full(cfg):
     case = W.CONFIGS[cfg](DEV)
     before, x = run_inplace(case)
@@ -77,7 +78,10 @@ DTYPE_PAIRS = [(torch.float32, torch.float32), (torch.float16, torch.float16),
                                       ((2, 65, 3, 64), None),        # whole D
                                       ((1, 300, 2, 40), [1, 37]),    # odd start: element path
                                       ((4, 7, 1, 1024), [0, 1024]),  # D at its maximum
-                                      ((2, 3, 2, 10), [4, 6])])      # one pair per row
+                                      ((2, 3, 2, 10), [4, 6]),       # one pair per row
+                                      ((2, 33, 8, 64), None),        # 8 heads per lane
+                                      ((3, 17, 12, 96), [32, 96]),   # 4 heads per lane
+                                      ((2, 9, 6, 48), [16, 48])])    # 2 heads per lane
 def test_inplace_sweep(xdt, cdt, layout, shape, sl):
     B, S, N, D = shape
     start, end = (0, D) if sl is None else sl
@@ -461,7 +465,8 @@ def test_backward_configs_full(cfg):
 
 @pytest.mark.parametrize("xdt,cdt", DTYPE_PAIRS, ids=lambda d: str(d).split(".")[-1])
 @pytest.mark.parametrize("layout", ["BSND", "BS1D", "B11D", "111D"])
-@pytest.mark.parametrize("shape,sl", [((3, 37, 5, 96), [16, 80]), ((1, 300, 2, 40), [1, 37])])
+@pytest.mark.parametrize("shape,sl", [((3, 37, 5, 96), [16, 80]), ((1, 300, 2, 40), [1, 37]),
+                                      ((2, 33, 8, 64), [0, 64]), ((3, 17, 12, 96), [32, 96])])
 def test_backward_sweep(xdt, cdt, layout, shape, sl):
     B, S, N, D = shape
     L = sl[1] - sl[0]
@@ -499,7 +504,9 @@ HALF_SHAPES = [((3, 37, 5, 96), [16, 80]),    # ragged rows, inner slice, vector
                ((1, 300, 2, 40), [1, 37]),    # odd start: element path
                ((2, 9, 2, 48), [8, 20]),      # halves of 6: element path for 16-bit types
                ((4, 7, 1, 1024), [0, 1024]),  # D at its maximum
-               ((2, 3, 2, 10), [4, 6])]       # one pair per row
+               ((2, 3, 2, 10), [4, 6]),       # one pair per row
+               ((2, 33, 8, 64), None),        # 4 heads per lane (half mode's maximum)
+               ((2, 9, 6, 48), [16, 48])]     # 2 heads per lane
 
 
 @pytest.mark.parametrize("direction", ["forward", "backward"])
