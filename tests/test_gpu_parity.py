@@ -551,3 +551,53 @@ def test_half_mode_backward_full_and_autograd():
     ra.rope_partial_inplace_backward(expect, c, s, 0, [16, 48])
     torch.cuda.synchronize()
     check_bits_equal(xl.grad.cpu(), expect.cpu(), "autograd half mode")
+
+
+# ------------------------------------------------------------------------------------------
+# HIP graph capture: the library allocates nothing, never synchronizes and records no memset,
+# so both operations can be captured and replayed; every replay is checked against eager runs
+# (with eager work and synchronizations between the replays).
+# ------------------------------------------------------------------------------------------
+
+def test_graph_capture_replays_match_eager():
+    # in-place op: each replay rotates x again, so k replays equal k eager calls
+    case = W.inplace_case("graph", 2, 64, 4, 96, torch.bfloat16, torch.float32, [32, 96],
+                          cos_shape=(2, 64, 1, 64), seed=61, device=DEV)
+    x_static = case.x.clone()
+    x_eager = case.x.clone()
+    # cache op (interleaved mrope through the V2 entry point): outputs are rewritten per replay
+    pos = W.mrope_positions(40, 2, 4, 5, m=3).to(DEV)
+    ccase = W.cache_case("graph", pos.shape[1], 4, 2, 128, 128, torch.bfloat16, True, 100,
+                         seed=62, mrope_section=[24, 20, 20], positions=pos, device=DEV,
+                         cache_mode=1)
+    q_static, k_static = ccase.query.clone(), ccase.key.clone()
+    qo = torch.empty_like(q_static)
+    ko = torch.empty_like(k_static)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a side stream, as graph capture requires
+        ra.rope_partial_inplace(x_static.clone(), case.cos, case.sin, 1, [32, 96])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ra.rope_partial_inplace(x_static, case.cos, case.sin, 1, [32, 96])
+        ra.rope_with_cos_sin_cache_v2(ccase.positions, q_static, k_static, ccase.cache,
+                                      [24, 20, 20], 128, True, 1, query_out=qo, key_out=ko)
+    gen = W.generator(63, DEV)
+    for replay in range(4):
+        # new cache-op inputs in the captured buffers (eager work between replays)
+        q_static.copy_(W.randn(q_static.shape, torch.bfloat16, gen))
+        k_static.copy_(W.randn(k_static.shape, torch.bfloat16, gen))
+        torch.cuda.synchronize()
+        g.replay()
+        ra.rope_partial_inplace(x_eager, case.cos, case.sin, 1, [32, 96])
+        q_ref, k_ref = ra.rope_with_cos_sin_cache_v2(ccase.positions, q_static, k_static,
+                                                     ccase.cache, [24, 20, 20], 128, True, 1)
+        torch.cuda.synchronize()
+        check_bits_equal(x_static.cpu(), x_eager.cpu(), f"in-place replay {replay}")
+        check_bits_equal(qo.cpu(), q_ref.cpu(), f"cache q replay {replay}")
+        check_bits_equal(ko.cpu(), k_ref.cpu(), f"cache k replay {replay}")
+    # and the replayed cache op against the oracle on the last inputs
+    compare_cache(ccase.positions.cpu(), q_static.cpu(), k_static.cpu(), ccase.cache.cpu(),
+                  [24, 20, 20], 128, True, qo.cpu(), ko.cpu(), "graph replay vs oracle", 1)
