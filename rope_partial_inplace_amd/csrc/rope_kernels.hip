@@ -469,9 +469,9 @@ __global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
 // ============================================================================================
 // K2: RoPE with a cos/sin cache ([RSCC §设计动机], rope and mrope modes, NeoX and GPT-J).
 // A workgroup owns a tile of tokens.  Stage: its lanes gather each token's cos|sin row from
-// the cache (mrope: element i from the position row whose section holds i), raise it to
-// float32 and keep it in LDS, so it is read from HBM once per token and reused by every q/k
-// head.  Then lanes walk (token, head, unit) items.  NeoX: a unit is two V-element vectors,
+// the cache (mrope: element i from the position row that the stitching assigns it) and keep
+// it in LDS in the cache's own element type (raised to float32 at use), so it is read from
+// HBM once per token and reused by every q/k head.  Then lanes walk (token, head, unit) items.  NeoX: a unit is two V-element vectors,
 // u and u + rd/(2V) of the rotated part (its pairs lie across the halves), or the same
 // two-vector shape over [rd, H) copied as raw bits.  GPT-J: a unit is one vector (its pairs
 // lie inside it), rotated below rd and copied above.  The units of one head are adjacent
@@ -508,28 +508,6 @@ __device__ inline int64_t clamp_position(const CachePlan &p, int64_t pos) {
 // Word j of a 16-byte raw vector.
 __device__ inline uint32_t word_of(const u32x4 &v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
-}
-
-// N floats from LDS: N a multiple of 4 at a 16-byte aligned address, or N == 2 at an 8-byte
-// aligned address.
-template <int N>
-__device__ inline void lds_read(const float *src, float *dst) {
-  static_assert(N % 4 == 0 || N == 2, "lds_read takes 2 or a multiple of 4 floats");
-  if constexpr (N == 2) {
-    const float2 v = *reinterpret_cast<const float2 *>(src);
-    dst[0] = v.x;
-    dst[1] = v.y;
-  } else {
-    const float4 *q = reinterpret_cast<const float4 *>(src);
-#pragma unroll
-    for (int c = 0; c < N / 4; ++c) {
-      const float4 v = q[c];
-      dst[4 * c] = v.x;
-      dst[4 * c + 1] = v.y;
-      dst[4 * c + 2] = v.z;
-      dst[4 * c + 3] = v.w;
-    }
-  }
 }
 
 // Where one item of a tile lives: token, q or k, head, unit, and the element offsets of its

@@ -371,7 +371,8 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
   p.items_per_token = uint32_t(ipt);
   // Tokens per workgroup: the tile's items are processed in passes of kBlock*K; pick the
   // smallest tile that fills its passes to >= 90% (at most 8 passes), else the best filled
-  // one; the LDS tile of cos|sin (tile_tokens * rd floats) stays within 32 KiB.
+  // one.  The LDS tile holds tile_tokens * rd elements of the cache type; it is sized here
+  // as if they were 4-byte floats (an upper bound), within 32 KiB.
   const int64_t pass = int64_t(kCacheBlock) * (p.neox ? kNeoxItemsPerLane : kGptjItemsPerLane);
   const int64_t tt_lds = std::max<int64_t>(1, (32 * 1024) / (rd * 4));
   int64_t tt = 1;

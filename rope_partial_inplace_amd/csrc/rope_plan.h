@@ -65,7 +65,7 @@ struct InplacePlan {
 
 // ---- cos/sin cache --------------------------------------------------------------------------
 // A workgroup owns a tile of `tile_tokens` tokens.  It first stages the tile's cos|sin rows
-// (gathered, mrope-stitched, raised to float32) in LDS, then its lanes walk the tile's
+// (gathered, mrope-stitched, in the cache's element type) in LDS, then its lanes walk the tile's
 // (token, head, unit) items.  NeoX: a unit is two vectors of `vec` elements (vector u and
 // vector u + rd/(2 vec) of the rotated part, or the same shape over the pass-through part).
 // GPT-J: a unit is one vector.
