@@ -19,3 +19,19 @@ def test_fastdiv_matches_integer_division(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert out.returncode == 0, out.stdout + out.stderr
     assert out.stdout.startswith("ok")
+
+
+def test_inplace_plan_covers_every_slice_element_once(tmp_path):
+    """The in-place launch plan and the kernel's item decode (written out for the host in
+    tests/inplace_plan_check.cpp): every slice element is touched by exactly one work item and
+    paired with its own cos/sin element, over both modes, every dtype pair and broadcast
+    layout, vector and element paths and 1-8 heads per lane; a 2^32-item plan takes the
+    64-bit decode and stays in bounds."""
+    exe = tmp_path / "inplace_plan_check"
+    csrc = os.path.join(ROOT, "rope_partial_inplace_amd", "csrc")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"), "-I", csrc,
+                    os.path.join(ROOT, "tests", "inplace_plan_check.cpp"),
+                    os.path.join(csrc, "rope_plan.cpp"), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert out.stdout.startswith("ok")
