@@ -601,3 +601,33 @@ def test_graph_capture_replays_match_eager():
     # and the replayed cache op against the oracle on the last inputs
     compare_cache(ccase.positions.cpu(), q_static.cpu(), k_static.cpu(), ccase.cache.cpu(),
                   [24, 20, 20], 128, True, qo.cpu(), ko.cpu(), "graph replay vs oracle", 1)
+
+
+def test_inplace_64bit_item_decode():
+    """2^32 work items, past the 32-bit decode: x bf16 [1, 2^25, 1, 1024] (64 GiB), whole-D
+    slice, bf16 cos/sin broadcast (111D).  x is filled from a seeded 65536-row block scaled per
+    block (so every row's input can be rebuilt); sampled rows, including the first and last,
+    are compared with the oracle.  The decode's bounds are checked on the host by
+    tests/inplace_plan_check.cpp."""
+    S, D, R = 1 << 25, 1024, 1 << 16
+    gen = W.generator(71, DEV)
+    base = W.randn((R, D), torch.bfloat16, gen)
+    scales = [1.0 + 0.125 * k for k in range(7)]
+
+    def block(blk):
+        return base * scales[blk % 7]
+
+    x = torch.empty((1, S, 1, D), dtype=torch.bfloat16, device=DEV)
+    for blk in range(S // R):
+        x[0, blk * R:(blk + 1) * R, 0] = block(blk)
+    c = W.randn((1, 1, 1, D), torch.bfloat16, gen)
+    s = W.randn((1, 1, 1, D), torch.bfloat16, gen)
+    ra.rope_partial_inplace(x, c, s, 1, None)
+    torch.cuda.synchronize()
+    pick = torch.randint(0, S, (200,), generator=torch.Generator().manual_seed(72)).tolist()
+    rows = sorted(set([0, 1, R - 1, R, S // 2, S - 2, S - 1] + pick))
+    before = torch.stack([block(r // R)[r % R] for r in rows]).cpu().reshape(1, len(rows), 1, D)
+    after = torch.stack([x[0, r, 0] for r in rows]).cpu().reshape(1, len(rows), 1, D)
+    del x
+    torch.cuda.empty_cache()
+    check_inplace(before, after, c, s, None, "2^32 items, sampled rows")
