@@ -1,0 +1,213 @@
+// Host check of the cos/sin-cache op's launch plan (rope_plan.cpp) together with the way
+// cos_sin_cache_kernel walks it, written out here for the host: tiles of tokens, the
+// (token, head, unit) items of a tile and the cos|sin staging chunks.  For each plan it
+// checks that
+//   - every element of query_out and key_out is written by exactly one item, from the input
+//     element at the same position of the same head (NeoX units pair elements i and
+//     i + rotaryDim/2, GPT-J units hold whole pairs), and inputs are read inside their rows;
+//   - the rotated part of each unit reads the cos|sin elements of its own pair indices;
+//   - the staging chunks of a tile write each of its tile_tokens * rotaryDim LDS elements once,
+//     inside the LDS size the launch requests, and each element's position row is the one the
+//     stitching assigns (sections for cacheMode 0, the i mod 3 rule below 3 * mropeSection[1]
+//     for cacheMode 1), with one row per chunk unless the plan takes the multi-row path.
+// Shapes cover every dtype, both styles, rope mode, every whitelisted mropeSection and both
+// cacheModes, pass-through parts, token counts that leave a ragged last tile, and padded row
+// strides.  No GPU and no tensor data are involved.
+// Prints "ok <plans> <items>" or the first failure; exit status 1 on failure.
+#include <cstdint>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "rope.h"
+#include "rope_plan.h"
+
+using namespace ropeamd;
+
+static rope_tensor t2(uintptr_t addr, rope_dtype dt, int64_t rows, int64_t cols,
+                      int64_t row_stride) {
+  rope_tensor t{};
+  t.data = reinterpret_cast<void *>(addr);
+  t.dtype = dt;
+  t.ndim = 2;
+  t.shape[0] = rows;
+  t.shape[1] = cols;
+  t.stride[0] = row_stride;
+  t.stride[1] = 1;
+  return t;
+}
+
+static int fails = 0;
+static uint64_t items_checked = 0;
+
+#define CHECK(cond, ...)                                  \
+  do {                                                    \
+    if (!(cond)) {                                        \
+      if (fails++ == 0) {                                 \
+        std::printf("FAIL %s:%d: ", __FILE__, __LINE__); \
+        std::printf(__VA_ARGS__);                         \
+        std::printf("\n");                                \
+      }                                                   \
+      return false;                                       \
+    }                                                     \
+  } while (0)
+
+// The position row that the stitching assigns to element i (< rd/2) of cos/sin, from the
+// definitions: sections (cacheMode 0) or the interleaved rule (cacheMode 1).
+static int assigned_row(const std::vector<int64_t> &sec, int64_t cache_mode, int64_t i) {
+  if (sec.empty() || sec[0] == 0) return 0;
+  if (cache_mode == 1) {
+    if (i % 3 == 1 && i < 3 * sec[1]) return 1;
+    if (i % 3 == 2 && i < 3 * sec[1]) return 2;
+    return 0;
+  }
+  int64_t acc = 0;
+  for (size_t k = 0; k < sec.size(); ++k) {
+    acc += sec[k];
+    if (i < acc) return int(k);
+  }
+  return -1;
+}
+
+static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, int64_t H,
+                 int64_t rd, std::vector<int64_t> sec, int64_t cache_mode, int64_t q_pad) {
+  const int64_t m = sec.empty() ? 0 : int64_t(sec.size());
+  rope_tensor pos{};
+  pos.data = reinterpret_cast<void *>(uintptr_t(0x20000000));
+  pos.dtype = ROPE_I64;
+  if (m) {
+    pos.ndim = 2;
+    pos.shape[0] = m;
+    pos.shape[1] = T;
+    pos.stride[0] = T;
+    pos.stride[1] = 1;
+  } else {
+    pos.ndim = 1;
+    pos.shape[0] = T;
+    pos.stride[0] = 1;
+  }
+  const int64_t qs = nq * H + q_pad;
+  const rope_tensor q = t2(0x30000000, dt, T, nq * H, qs);
+  const rope_tensor k = t2(0x50000000, dt, T, nk * H, nk * H);
+  const rope_tensor c = t2(0x70000000, dt, 4096, rd, rd);
+  const rope_tensor qo = t2(0x80000000, dt, T, nq * H, nq * H);
+  const rope_tensor ko = t2(0xA0000000, dt, T, nk * H, nk * H);
+  CachePlan p;
+  std::string err;
+  const int st = plan_cache(&pos, &q, &k, &c, m ? sec.data() : nullptr, m, H, neox ? 1 : 0,
+                            cache_mode, &qo, &ko, &p, &err);
+  CHECK(st == ROPE_OK, "plan rejected: %s", err.c_str());
+  const int64_t V = p.vec, half = rd / 2;
+  const int64_t es = dt == ROPE_F32 ? 4 : 2;
+  CHECK(V * es == 16, "vector of %lld elements", (long long)V);
+  const int64_t lds_elems = int64_t(p.tile_tokens) * rd;  // the LDS the launch requests
+  std::vector<uint8_t> hq(size_t(T * nq * H), 0), hk(size_t(T * nk * H), 0);
+  for (int64_t tile = 0; tile < p.tiles; ++tile) {
+    const int64_t t0 = tile * int64_t(p.tile_tokens);
+    const int64_t ntok = std::min<int64_t>(p.T - t0, int64_t(p.tile_tokens));
+    CHECK(ntok >= 1, "empty tile %lld", (long long)tile);
+    // staging
+    std::vector<uint8_t> lds(size_t(lds_elems), 0);
+    const uint32_t stage_items = uint32_t(ntok) * p.stage_chunks;
+    for (uint32_t idx = 0; idx < stage_items; ++idx) {
+      const uint32_t tl = fastdiv_host(p.div_stage, idx);
+      const int64_t i0 = int64_t(idx - tl * p.stage_chunks) * V;
+      CHECK(tl < uint32_t(ntok) && i0 + V <= half, "staging chunk %u", idx);
+      int first_row = assigned_row(sec, cache_mode, i0);
+      for (int64_t e = 0; e < V; ++e) {
+        const int r = assigned_row(sec, cache_mode, i0 + e);
+        CHECK(r >= 0 && (m == 0 ? r == 0 : r < m), "row %d", r);
+        CHECK(p.multi_row || r == first_row,
+              "chunk at %lld mixes rows %d and %d without the multi-row path", (long long)i0,
+              first_row, r);
+        for (int64_t h2 : {int64_t(0), half}) {
+          const int64_t li = int64_t(tl) * rd + h2 + i0 + e;
+          CHECK(li < lds_elems, "LDS index %lld beyond %lld", (long long)li,
+                (long long)lds_elems);
+          CHECK(lds[size_t(li)] == 0, "LDS element %lld staged twice", (long long)li);
+          lds[size_t(li)] = 1;
+        }
+      }
+    }
+    for (int64_t i = 0; i < ntok * rd; ++i) CHECK(lds[size_t(i)] == 1, "LDS %lld unset", (long long)i);
+    // items
+    const uint32_t tile_items = uint32_t(ntok) * p.items_per_token;
+    for (uint32_t it = 0; it < tile_items; ++it) {
+      const uint32_t tl = fastdiv_host(p.div_ipt, it);
+      const uint32_t r = it - tl * p.items_per_token;
+      const uint32_t h = fastdiv_host(p.div_units, r);
+      const uint32_t u = r - h * p.units;
+      CHECK(tl < uint32_t(ntok) && h < uint32_t(nq + nk), "item %u", it);
+      const int64_t t = t0 + tl;
+      const bool is_q = h < uint32_t(nq);
+      const int64_t hh = is_q ? int64_t(h) : int64_t(h) - nq;
+      const int64_t in_row = t * (is_q ? qs : nk * H) + hh * H;
+      const int64_t out_row = t * ((is_q ? nq : nk) * H) + hh * H;
+      std::vector<uint8_t> &hit = is_q ? hq : hk;
+      std::vector<int64_t> offs;
+      const bool rotated = u < p.rot_units;
+      if (neox) {
+        if (rotated) {
+          offs = {int64_t(u) * V, half + int64_t(u) * V};
+        } else {
+          const int64_t v = int64_t(u - p.rot_units) * V;
+          offs = {rd + v, rd + (H - rd) / 2 + v};
+        }
+      } else {
+        offs = {int64_t(u) * V};
+      }
+      for (size_t a = 0; a < offs.size(); ++a)
+        for (int64_t e = 0; e < V; ++e) {
+          const int64_t col = offs[a] + e;  // position inside the head
+          CHECK(col >= 0 && col < H, "column %lld outside the head", (long long)col);
+          CHECK(rotated == (col < rd), "column %lld on the wrong side of rotaryDim",
+                (long long)col);
+          CHECK(in_row + col < T * qs || !is_q, "q input out of bounds");
+          const size_t oi = size_t(out_row + col);
+          CHECK(hit[oi] == 0, "output %zu written twice", oi);
+          hit[oi] = 1;
+          if (rotated) {
+            // the pair index whose cos|sin this element uses
+            const int64_t pair = neox ? (col < half ? col : col - half) : col / 2;
+            const int64_t lds_cos = neox ? int64_t(u) * V + e : int64_t(u) * (V / 2) + e / 2;
+            CHECK(pair == lds_cos, "column %lld reads cos %lld, wants %lld", (long long)col,
+                  (long long)lds_cos, (long long)pair);
+            if (neox && a == 1)
+              CHECK(offs[1] - offs[0] == half, "NeoX halves not rd/2 apart");
+          }
+        }
+      ++items_checked;
+    }
+  }
+  for (size_t i = 0; i < hq.size(); ++i) CHECK(hq[i] == 1, "q output %zu unwritten", i);
+  for (size_t i = 0; i < hk.size(); ++i) CHECK(hk[i] == 1, "k output %zu unwritten", i);
+  return true;
+}
+
+int main() {
+  int plans = 0;
+  const std::vector<std::vector<int64_t>> mlists = {
+      {}, {16, 24, 24}, {8, 12, 12}, {24, 20, 20}, {11, 11, 10}, {16, 16, 16, 16}};
+  for (rope_dtype dt : {ROPE_F32, ROPE_F16, ROPE_BF16}) {
+    const int64_t align = 64 / (dt == ROPE_F32 ? 4 : 2);
+    for (bool neox : {true, false})
+      for (const auto &sec : mlists)
+        for (int64_t cm : {int64_t(0), int64_t(1)}) {
+          if (cm == 1 && sec.size() != 3) continue;
+          std::vector<int64_t> rds;
+          if (sec.empty()) rds = {align, 2 * align, 4 * align};
+          else rds = {2 * (sec[0] + sec[1] + sec[2] + (sec.size() == 4 ? sec[3] : 0))};
+          for (int64_t rd : rds)
+            for (int64_t extra : {int64_t(0), align, 2 * align})
+              for (int64_t T : {int64_t(1), int64_t(7), int64_t(61)})
+                for (auto hq : {std::pair<int64_t, int64_t>{1, 1}, {5, 3}, {32, 8}}) {
+                  const int64_t pad = (T == 7) ? align : 0;
+                  if (!walk(dt, neox, T, hq.first, hq.second, rd + extra, rd, sec, cm, pad))
+                    return 1;
+                  ++plans;
+                }
+        }
+  }
+  std::printf("ok %d %llu\n", plans, (unsigned long long)items_checked);
+  return 0;
+}

@@ -35,3 +35,19 @@ def test_inplace_plan_covers_every_slice_element_once(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert out.returncode == 0, out.stdout + out.stderr
     assert out.stdout.startswith("ok")
+
+
+def test_cache_plan_covers_every_output_once(tmp_path):
+    """The cos/sin-cache launch plan and the kernel's tile / item / staging walk (written out
+    for the host in tests/cache_plan_check.cpp): every output element written once from its
+    own input position, rotated elements paired with their own cos|sin index, every LDS
+    element staged once with the position row the stitching assigns, over every dtype,
+    style, mrope list and cacheMode, pass-through parts and ragged last tiles."""
+    exe = tmp_path / "cache_plan_check"
+    csrc = os.path.join(ROOT, "rope_partial_inplace_amd", "csrc")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"), "-I", csrc,
+                    os.path.join(ROOT, "tests", "cache_plan_check.cpp"),
+                    os.path.join(csrc, "rope_plan.cpp"), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert out.stdout.startswith("ok")
