@@ -718,8 +718,15 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
   const int64_t rd = p.rd, half = rd / 2;
   const uint32_t pass = uint32_t(kCacheBlock) * K;
   for (int64_t tile = blockIdx.x; tile < p.tiles; tile += gridDim.x) {
-    const int64_t t0 = tile * int64_t(p.tile_tokens);
-    const int64_t ntok = (p.T - t0) < int64_t(p.tile_tokens) ? (p.T - t0) : int64_t(p.tile_tokens);
+    // tiles [0, big_tiles) hold tile_tokens tokens, later ones a single token (tapered end)
+    int64_t t0, ntok;
+    if (tile < p.big_tiles) {
+      t0 = tile * int64_t(p.tile_tokens);
+      ntok = int64_t(p.tile_tokens);
+    } else {
+      t0 = p.big_tokens + (tile - p.big_tiles);
+      ntok = 1;
+    }
     const uint32_t tile_items = uint32_t(ntok) * p.items_per_token;
 
     // The position of this lane's first staging chunk is loaded before the first pass's q/k

@@ -393,6 +393,16 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
     return reject(err, ROPE_ERR_PARAM_INVALID, "rotaryDim too large for the LDS tile (max 16384)");
   p.tile_tokens = uint32_t(tt);
   p.tiles = (T + tt - 1) / tt;
+  // Tapered end: a workgroup lives for a few loaded round trips, and the last round drains
+  // at falling occupancy; one-token tiles for the last ~round of tokens shorten that drain.
+  p.big_tiles = p.tiles;
+  p.big_tokens = T;
+  if (tt > 1) {
+    const int64_t taper = std::min<int64_t>(kTaperTokens, T / 4);
+    p.big_tiles = (T - taper) / tt;
+    p.big_tokens = p.big_tiles * tt;
+    p.tiles = p.big_tiles + (T - p.big_tokens);
+  }
   p.div_units = make_fastdiv(p.units);
   p.div_ipt = make_fastdiv(p.items_per_token);
   p.cache_vec = aligned16(p.cache) && (p.cache_stride * es) % 16 == 0;

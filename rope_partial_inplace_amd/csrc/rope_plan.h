@@ -91,6 +91,9 @@ struct CachePlan {
   uint32_t items_per_token = 0;
   uint32_t tile_tokens = 1;
   int64_t tiles = 0;
+  // Tapered end: tiles [0, big_tiles) hold tile_tokens tokens each (tokens [0, big_tokens));
+  // every later tile holds one token, so the workgroups of the last round are short.
+  int64_t big_tiles = 0, big_tokens = 0;
   bool cache_vec = false;       // cache rows can be read with 16-byte loads
   uint32_t stage_chunks = 0;    // (rd/2) / vec: vector chunks of one cos (or sin) half-row
   FastDiv div_units, div_ipt, div_stage;
@@ -112,6 +115,9 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
 constexpr int kBlock = 1024;      // in-place kernel workgroup (few, large workgroups: the
                                   // headline launch is short and dispatch-bound)
 constexpr int kCacheBlock = 256;  // cache kernel workgroup (one token tile)
+// Tokens given one-token tiles at the end of a cache launch: about one round of resident
+// cache workgroups on MI355X (256 CUs x 5 workgroups at the kernel's register use).
+constexpr int64_t kTaperTokens = 1280;
 constexpr int kNeoxItemsPerLane = 2;  // NeoX units are two vectors
 constexpr int kGptjItemsPerLane = 2;  // GPT-J units are one vector
 

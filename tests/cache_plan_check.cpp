@@ -6,13 +6,15 @@
 //     element at the same position of the same head (NeoX units pair elements i and
 //     i + rotaryDim/2, GPT-J units hold whole pairs), and inputs are read inside their rows;
 //   - the rotated part of each unit reads the cos|sin elements of its own pair indices;
+//   - every token belongs to exactly one tile (tiles of tile_tokens, then one-token tiles);
 //   - the staging chunks of a tile write each of its tile_tokens * rotaryDim LDS elements once,
 //     inside the LDS size the launch requests, and each element's position row is the one the
 //     stitching assigns (sections for cacheMode 0, the i mod 3 rule below 3 * mropeSection[1]
 //     for cacheMode 1), with one row per chunk unless the plan takes the multi-row path.
 // Shapes cover every dtype, both styles, rope mode, every whitelisted mropeSection and both
-// cacheModes, pass-through parts, token counts that leave a ragged last tile, and padded row
-// strides.  No GPU and no tensor data are involved.
+// cacheModes, pass-through parts, token counts that leave a ragged last tile or reach the
+// one-token tiles of the tapered end, and padded row strides.  No GPU and no tensor data are
+// involved.
 // Prints "ok <plans> <items>" or the first failure; exit status 1 on failure.
 #include <cstdint>
 #include <cstdio>
@@ -102,10 +104,22 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
   CHECK(V * es == 16, "vector of %lld elements", (long long)V);
   const int64_t lds_elems = int64_t(p.tile_tokens) * rd;  // the LDS the launch requests
   std::vector<uint8_t> hq(size_t(T * nq * H), 0), hk(size_t(T * nk * H), 0);
+  std::vector<uint8_t> tok_seen(size_t(T), 0);
   for (int64_t tile = 0; tile < p.tiles; ++tile) {
-    const int64_t t0 = tile * int64_t(p.tile_tokens);
-    const int64_t ntok = std::min<int64_t>(p.T - t0, int64_t(p.tile_tokens));
-    CHECK(ntok >= 1, "empty tile %lld", (long long)tile);
+    int64_t t0, ntok;  // the kernel's tile -> tokens map (tapered end: one-token tiles)
+    if (tile < p.big_tiles) {
+      t0 = tile * int64_t(p.tile_tokens);
+      ntok = int64_t(p.tile_tokens);
+    } else {
+      t0 = p.big_tokens + (tile - p.big_tiles);
+      ntok = 1;
+    }
+    CHECK(ntok >= 1 && t0 >= 0 && t0 + ntok <= T, "tile %lld covers tokens [%lld, %lld)",
+          (long long)tile, (long long)t0, (long long)(t0 + ntok));
+    for (int64_t t = t0; t < t0 + ntok; ++t) {
+      CHECK(tok_seen[size_t(t)] == 0, "token %lld in two tiles", (long long)t);
+      tok_seen[size_t(t)] = 1;
+    }
     // staging
     std::vector<uint8_t> lds(size_t(lds_elems), 0);
     const uint32_t stage_items = uint32_t(ntok) * p.stage_chunks;
@@ -179,6 +193,7 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
       ++items_checked;
     }
   }
+  for (size_t t = 0; t < tok_seen.size(); ++t) CHECK(tok_seen[t] == 1, "token %zu in no tile", t);
   for (size_t i = 0; i < hq.size(); ++i) CHECK(hq[i] == 1, "q output %zu unwritten", i);
   for (size_t i = 0; i < hk.size(); ++i) CHECK(hk[i] == 1, "k output %zu unwritten", i);
   return true;
@@ -199,8 +214,9 @@ int main() {
           else rds = {2 * (sec[0] + sec[1] + sec[2] + (sec.size() == 4 ? sec[3] : 0))};
           for (int64_t rd : rds)
             for (int64_t extra : {int64_t(0), align, 2 * align})
-              for (int64_t T : {int64_t(1), int64_t(7), int64_t(61)})
+              for (int64_t T : {int64_t(1), int64_t(7), int64_t(61), int64_t(5123)})
                 for (auto hq : {std::pair<int64_t, int64_t>{1, 1}, {5, 3}, {32, 8}}) {
+                  if (T > 1000 && hq.first != 1) continue;  // the long case: one head each
                   const int64_t pad = (T == 7) ? align : 0;
                   if (!walk(dt, neox, T, hq.first, hq.second, rd + extra, rd, sec, cm, pad))
                     return 1;
