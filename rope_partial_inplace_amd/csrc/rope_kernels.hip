@@ -357,6 +357,9 @@ __device__ inline void rotate_pair(float a, float b, float c0, float c1, float s
 // slice.  HALF (rotary_mode 0, [IPRM §参数说明]; x1, x2 the two halves of the slice,
 // x_rotate = cat(-x2, x1)): a lane owns chunk u of the first half and chunk u of the second,
 // so every pair (i, i + L/2) is lane-local and both halves are read as contiguous runs.
+// XCH (half mode, 1..16 chunks per half, a power of two): a lane owns one chunk of one half
+// and reads its pair partners from lane (lane ^ chunks per half) with ds_bpermute, so the
+// launch has as many lanes, and each lane as few loads, as in interleave mode.
 // NHL > 1 (cos/sin broadcast over the heads): the lane owns its chunk in NHL consecutive
 // heads of one (b, s) and loads the cos/sin chunk once for all of them.  Elements outside
 // [start, end) are never touched.  cos/sin rows are addressed with zero strides on broadcast
@@ -367,19 +370,20 @@ __device__ inline void rotate_pair(float a, float b, float c0, float c1, float s
 // ============================================================================================
 // One lane item: chunk `chunk` of the NHL x rows starting at row r * NHL, whose cos/sin row
 // is that of (b, s, head g * NHL).
-template <typename XT, typename CT, bool VEC, int NHL, bool CNT, bool BWD, bool HALF>
+template <typename XT, typename CT, bool VEC, int NHL, bool CNT, bool BWD, bool HALF, bool XCH>
 __device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, uint64_t chunk,
                                              uint64_t b, uint64_t s, uint64_t g) {
   // one 16-byte access per lane for the wider of x and cos/sin, 8 bytes for the narrower;
   // element access: one pair (2 elements) in interleave mode, one element per half in HALF
   constexpr int V =
       VEC ? 16 / (sizeof(XT) > sizeof(CT) ? int(sizeof(XT)) : int(sizeof(CT))) : (HALF ? 1 : 2);
-  constexpr int NH = HALF ? 2 : 1;          // chunks per head: one, or one in each half
+  constexpr int NH = HALF && !XCH ? 2 : 1;  // chunks per head: one, or one in each half
   const int64_t hoff = HALF ? p.L / 2 : 0;  // offset of the second half
   const int64_t crow = int64_t(b) * p.cb + int64_t(s) * p.cs + int64_t(g) * NHL * p.cn;
   const int64_t coff = crow * p.L + int64_t(chunk) * V;
   const int64_t x0 = int64_t(r) * NHL * p.D + p.start + int64_t(chunk) * V;
   float xv[NHL][NH][V], cv[NH][V], sv[NH][V];
+  float xpv[XCH ? NHL : 1][V], spv[XCH && BWD ? V : 1];  // XCH: the partner lane's x, sin
   if constexpr (VEC) {
     constexpr int XB = V * int(sizeof(XT)), CB = V * int(sizeof(CT));
     Words<XB> xr[NHL][NH];
@@ -393,6 +397,28 @@ __device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, u
     for (int hh = 0; hh < NH; ++hh) {
       load_words<CB, CNT>(static_cast<const CT *>(p.cos) + coff + hh * hoff, cr[hh]);
       load_words<CB, CNT>(static_cast<const CT *>(p.sin) + coff + hh * hoff, sr[hh]);
+    }
+    if constexpr (XCH) {
+      // The pair partners of this lane's chunk sit in the same chunk of the other half,
+      // owned by lane (lane ^ xch) of this wavefront (a row's 2 * xch lanes are consecutive
+      // and aligned).  The raw words are exchanged: forward needs the partner's x, the
+      // gradient also the partner's sin.
+      const int src = int((__lane_id() ^ p.xch) << 2);
+#pragma unroll
+      for (int j = 0; j < NHL; ++j) {
+        Words<XB> xw;
+#pragma unroll
+        for (int q = 0; q < XB / 4; ++q)
+          xw.w[q] = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(xr[j][0].w[q])));
+        words_to_floats<XT, V>(xw, xpv[j]);
+      }
+      if constexpr (BWD) {
+        Words<CB> sw;
+#pragma unroll
+        for (int q = 0; q < CB / 4; ++q)
+          sw.w[q] = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(sr[0].w[q])));
+        words_to_floats<CT, V>(sw, spv);
+      }
     }
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
@@ -412,6 +438,24 @@ __device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, u
       load_n<CT, V, false, CNT>(p.cos, coff + hh * hoff, cv[hh]);
       load_n<CT, V, false, CNT>(p.sin, coff + hh * hoff, sv[hh]);
     }
+  }
+  if constexpr (XCH) {
+    static_assert(HALF && VEC, "the lane exchange is a half-mode vector path");
+    const bool second = chunk >= p.xch;  // this chunk lies in the second half
+#pragma unroll
+    for (int j = 0; j < NHL; ++j) {
+      // first half: forward x*c - x'*s, gradient x*c + x'*s'; second half: the other signs
+      // (x' and s' the partner's values; the same products and sums as the pair map)
+      float y[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float pr = xv[j][0][e] * cv[0][e];
+        const float qr = xpv[j][e] * (BWD ? spv[e] : sv[0][e]);
+        y[e] = (second == BWD) ? pr - qr : pr + qr;
+      }
+      store_n<XT, V, VEC, true>(p.x, x0 + j * p.D, y);
+    }
+    return;
   }
 #pragma unroll
   for (int j = 0; j < NHL; ++j) {
@@ -434,7 +478,7 @@ __device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, u
   }
 }
 
-template <typename XT, typename CT, bool VEC, int NHL, bool CNT, bool BWD, bool HALF>
+template <typename XT, typename CT, bool VEC, int NHL, bool CNT, bool BWD, bool HALF, bool XCH>
 __global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
   // item it -> (row group r = (b, s, head group g), chunk).  Two loops: 32-bit indices with
   // multiply-high division (the usual case), and plain 64-bit division for huge tensors, kept
@@ -449,7 +493,7 @@ __global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
       const uint32_t g = r - bs * ng;
       const uint32_t b = fdiv(p.div_s, bs);
       const uint32_t s = bs - b * uint32_t(p.S);
-      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF>(p, r, chunk, b, s, g);
+      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF, XCH>(p, r, chunk, b, s, g);
     }
   } else {
     const uint64_t items = uint64_t(p.items), ng = uint64_t(p.N) / NHL;
@@ -461,7 +505,7 @@ __global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
       const uint64_t g = r - bs * ng;
       const uint64_t b = bs / uint64_t(p.S);
       const uint64_t s = bs - b * uint64_t(p.S);
-      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF>(p, r, chunk, b, s, g);
+      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF, XCH>(p, r, chunk, b, s, g);
     }
   }
 }
@@ -818,18 +862,27 @@ int launch(const void *fn, int64_t blocks, int threads, size_t lds, void *stream
   return ROPE_OK;
 }
 
+template <typename XT, typename CT, bool BWD, bool HALF, bool XCH>
+const void *pick_inplace_vec(const InplacePlan &p) {
+#define ROPE_K1(NHL, CNT) \
+  reinterpret_cast<const void *>(&inplace_rope_kernel<XT, CT, true, NHL, CNT, BWD, HALF, XCH>)
+  if (p.nhl == 1) return p.cos_stream ? ROPE_K1(1, true) : ROPE_K1(1, false);
+  if (p.nhl == 2) return p.cos_stream ? ROPE_K1(2, true) : ROPE_K1(2, false);
+  if (p.nhl == 4) return p.cos_stream ? ROPE_K1(4, true) : ROPE_K1(4, false);
+  if constexpr (!HALF || XCH)
+    return p.cos_stream ? ROPE_K1(8, true) : ROPE_K1(8, false);
+  return nullptr;  // the plan gives a two-chunk half-mode lane at most 4 heads
+#undef ROPE_K1
+}
+
 template <typename XT, typename CT, bool BWD, bool HALF>
 const void *pick_inplace(const InplacePlan &p) {
-#define ROPE_K1(VEC, NHL, CNT) \
-  reinterpret_cast<const void *>(&inplace_rope_kernel<XT, CT, VEC, NHL, CNT, BWD, HALF>)
-  if (!p.vector_io) return ROPE_K1(false, 1, false);
-  if (p.nhl == 1) return p.cos_stream ? ROPE_K1(true, 1, true) : ROPE_K1(true, 1, false);
-  if (p.nhl == 2) return p.cos_stream ? ROPE_K1(true, 2, true) : ROPE_K1(true, 2, false);
-  if (p.nhl == 4) return p.cos_stream ? ROPE_K1(true, 4, true) : ROPE_K1(true, 4, false);
-  if constexpr (!HALF)
-    return p.cos_stream ? ROPE_K1(true, 8, true) : ROPE_K1(true, 8, false);
-  return nullptr;  // the plan never gives half mode 8 heads per lane
-#undef ROPE_K1
+  if (!p.vector_io)
+    return reinterpret_cast<const void *>(
+        &inplace_rope_kernel<XT, CT, false, 1, false, BWD, HALF, false>);
+  if constexpr (HALF)
+    if (p.xch != 0) return pick_inplace_vec<XT, CT, BWD, true, true>(p);
+  return pick_inplace_vec<XT, CT, BWD, HALF, false>(p);
 }
 
 template <bool BWD, bool HALF>

@@ -183,13 +183,20 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
   p.vector_io = aligned;
   p.vec = aligned ? uint32_t(v) : (p.half ? 1u : 2u);
   p.chunks_per_row = uint32_t(span / p.vec);
+  // Half mode, vector path, 1..16 chunks per half (a power of two): one chunk per lane, the
+  // pair partner in lane (lane ^ chunks per half) -- twice the lanes, half the loads each.
+  const uint32_t cph = p.chunks_per_row;
+  if (p.half && aligned && cph <= 16 && (cph & (cph - 1)) == 0) {
+    p.xch = cph;
+    p.chunks_per_row = 2 * cph;
+  }
   // Heads per lane: with cos/sin broadcast over N, a lane rotates its chunk in nhl consecutive
-  // heads with one cos/sin load (the largest of 8, 4, 2 that divides N; 4 at most in half
-  // mode, whose lanes already hold two chunks per head).  Vector path only.
+  // heads with one cos/sin load (the largest of 8, 4, 2 that divides N; 4 at most when a
+  // half-mode lane holds two chunks per head).  Vector path only.
   p.nhl = 1;
   if (p.cn == 0 && p.N > 1 && p.vector_io)
     for (uint32_t c : {8u, 4u, 2u})
-      if (p.N % c == 0 && !(p.half && c > 4)) {
+      if (p.N % c == 0 && !(p.half && p.xch == 0 && c > 4)) {
         p.nhl = c;
         break;
       }

@@ -5,7 +5,9 @@
 //     item, and nothing outside the slices is touched;
 //   - the cos/sin element each x element is paired with is the one of its own (b, s, n) row
 //     (broadcast dims give index 0) at the same slice position, inside the cos/sin tensor;
-//   - in half mode an item's two chunks lie L/2 apart in one row.
+//   - in half mode an item's two chunks lie L/2 apart in one row; or, when the plan splits a
+//     pair across lanes (xch), the item it ^ xch -- the lane it ^ xch of the same wavefront --
+//     holds the same row's chunk L/2 away, and a row's lanes never straddle a wavefront.
 // Shapes cover both modes, every dtype pair, every broadcast layout, aligned and unaligned
 // pointers (vector and element paths) and 1/2/4/8 heads per lane.  A plan with 2^32 items is
 // checked for taking the 64-bit decode, with sampled items checked for bounds.  No GPU and no
@@ -98,7 +100,12 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
   const int st = plan_inplace(&x, &c, &sn, mode, sl, 2, &p, &err);
   CHECK(st == ROPE_OK, "plan rejected: %s", err.c_str());
   if (p.noop) return true;
-  const int64_t V = p.vec, NHL = p.nhl, NH = p.half ? 2 : 1, hoff = p.half ? L / 2 : 0;
+  const int64_t V = p.vec, NHL = p.nhl, NH = (p.half && !p.xch) ? 2 : 1;
+  const int64_t hoff = p.half ? L / 2 : 0;
+  CHECK(p.xch == 0 || (p.half && p.vector_io && (p.xch & (p.xch - 1)) == 0 && p.xch <= 16 &&
+                       p.chunks_per_row == 2 * p.xch && int64_t(p.xch) * V == L / 2),
+        "lane exchange with xch %u, chunks %u, V %lld, L %lld", p.xch, p.chunks_per_row,
+        (long long)V, (long long)L);
   CHECK(NHL == 1 || (Nc == 1 && N % NHL == 0), "heads per lane %lld with Nc %lld N %lld",
         (long long)NHL, (long long)Nc, (long long)N);
   CHECK(uint64_t(p.items) * NHL * NH * V == uint64_t(B * S * N * L),
@@ -112,6 +119,15 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
     const int64_t crow = int64_t(d.b) * p.cb + int64_t(d.s) * p.cs + int64_t(d.g) * NHL * p.cn;
     const int64_t coff = crow * L + int64_t(d.chunk) * V;
     const int64_t x0 = int64_t(d.r) * NHL * D + start + int64_t(d.chunk) * V;
+    if (p.xch) {
+      const Decoded q = decode(p, it ^ p.xch);
+      CHECK(q.r == d.r && q.chunk == (d.chunk ^ p.xch) && (it & 63) / (2 * p.xch) ==
+                                                              ((it ^ p.xch) & 63) / (2 * p.xch),
+            "item %llu and its partner lane are not the pair chunks of one row",
+            (unsigned long long)it);
+      const int64_t xq = int64_t(q.r) * NHL * D + start + int64_t(q.chunk) * V;
+      CHECK(xq - x0 == (d.chunk < p.xch ? hoff : -hoff), "partner chunk not L/2 away");
+    }
     for (int64_t j = 0; j < NHL; ++j)
       for (int64_t hh = 0; hh < NH; ++hh)
         for (int64_t e = 0; e < V; ++e) {

@@ -499,14 +499,15 @@ def test_autograd_wrapper_gradient():
 # half mode, rotary_mode 0 (x1, x2 the two halves of the slice)
 # ------------------------------------------------------------------------------------------
 
-HALF_SHAPES = [((3, 37, 5, 96), [16, 80]),    # ragged rows, inner slice, vector path
+HALF_SHAPES = [((3, 37, 5, 96), [16, 80]),    # ragged rows, inner slice, lane pairs
                ((2, 65, 3, 64), None),        # whole D
                ((1, 300, 2, 40), [1, 37]),    # odd start: element path
                ((2, 9, 2, 48), [8, 20]),      # halves of 6: element path for 16-bit types
                ((4, 7, 1, 1024), [0, 1024]),  # D at its maximum
                ((2, 3, 2, 10), [4, 6]),       # one pair per row
                ((2, 33, 8, 64), None),        # 4 heads per lane (half mode's maximum)
-               ((2, 9, 6, 48), [16, 48])]     # 2 heads per lane
+               ((2, 9, 6, 48), [16, 48]),     # 2 heads per lane
+               ((2, 9, 3, 128), [32, 128])]   # 12 or 6 chunks per half: two chunks per lane
 
 
 @pytest.mark.parametrize("direction", ["forward", "backward"])
