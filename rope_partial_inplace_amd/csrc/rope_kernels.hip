@@ -360,7 +360,7 @@ __device__ inline void rotate_pair(float a, float b, float c0, float c1, float s
 // XCH (half mode, 1..16 chunks per half, a power of two): a lane owns one chunk of one half
 // and reads its pair partners from lane (lane ^ chunks per half) with ds_bpermute, so the
 // launch has as many lanes, and each lane as few loads, as in interleave mode.
-// NHL > 1 (cos/sin broadcast over the heads): the lane owns its chunk in NHL consecutive
+// NHL = 2 or 4 (cos/sin broadcast over the heads): the lane owns its chunk in NHL consecutive
 // heads of one (b, s) and loads the cos/sin chunk once for all of them.  Elements outside
 // [start, end) are never touched.  cos/sin rows are addressed with zero strides on broadcast
 // dims (BSND, BS1D, B1ND, B11D, 111D and mixed forms).  BWD runs the transpose of the pair map
@@ -868,10 +868,7 @@ const void *pick_inplace_vec(const InplacePlan &p) {
   reinterpret_cast<const void *>(&inplace_rope_kernel<XT, CT, true, NHL, CNT, BWD, HALF, XCH>)
   if (p.nhl == 1) return p.cos_stream ? ROPE_K1(1, true) : ROPE_K1(1, false);
   if (p.nhl == 2) return p.cos_stream ? ROPE_K1(2, true) : ROPE_K1(2, false);
-  if (p.nhl == 4) return p.cos_stream ? ROPE_K1(4, true) : ROPE_K1(4, false);
-  if constexpr (!HALF || XCH)
-    return p.cos_stream ? ROPE_K1(8, true) : ROPE_K1(8, false);
-  return nullptr;  // the plan gives a two-chunk half-mode lane at most 4 heads
+  return p.cos_stream ? ROPE_K1(4, true) : ROPE_K1(4, false);
 #undef ROPE_K1
 }
 
@@ -938,10 +935,6 @@ int run_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor 
                                          : pick_inplace_dtype<false, true>(plan))
                             : (backward ? pick_inplace_dtype<true, false>(plan)
                                         : pick_inplace_dtype<false, false>(plan));
-  if (fn == nullptr) {
-    g_last_error = "internal: no kernel for this plan";
-    return ROPE_ERR_RUNTIME;
-  }
   return launch(fn, (plan.items + kBlock - 1) / kBlock, kBlock, 0, stream, &plan);
 }
 

@@ -191,12 +191,14 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
     p.chunks_per_row = 2 * cph;
   }
   // Heads per lane: with cos/sin broadcast over N, a lane rotates its chunk in nhl consecutive
-  // heads with one cos/sin load (the largest of 8, 4, 2 that divides N; 4 at most when a
-  // half-mode lane holds two chunks per head).  Vector path only.
+  // heads with one cos/sin load: the larger of 4, 2 that divides N and keeps a lane's x
+  // bytes at 32 or less (measured best: 4 heads of 8-byte chunks, 2 of 16-byte ones; more
+  // heads per lane leave too few lanes).  Vector path only.
   p.nhl = 1;
+  const uint32_t x_bytes_per_head = p.vec * uint32_t(xs) * (p.half && p.xch == 0 ? 2u : 1u);
   if (p.cn == 0 && p.N > 1 && p.vector_io)
-    for (uint32_t c : {8u, 4u, 2u})
-      if (p.N % c == 0 && !(p.half && p.xch == 0 && c > 4)) {
+    for (uint32_t c : {4u, 2u})
+      if (p.N % c == 0 && c * x_bytes_per_head <= 32) {
         p.nhl = c;
         break;
       }

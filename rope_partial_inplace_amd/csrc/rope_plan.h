@@ -50,7 +50,7 @@ struct InplacePlan {
   // cross-lane read.  Taken when the chunks of a half, xch, are a power of two up to 16, so a
   // row's 2 * xch lanes never straddle a wavefront.  0 = the lane owns both chunks.
   uint32_t xch = 0;
-  uint32_t nhl = 1;   // heads per lane (1, 2, 4 or 8); > 1 only when cos/sin broadcast over N
+  uint32_t nhl = 1;   // heads per lane (1, 2 or 4); > 1 only when cos/sin broadcast over N
   rope_dtype xdt = ROPE_F32, cdt = ROPE_F32;
   bool vector_io = false;  // 16-byte x accesses (else one element at a time)
   bool noop = false;       // nothing to launch
