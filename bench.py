@@ -105,6 +105,12 @@ def copy_ceiling_gbs(torch, nbytes=1 << 30) -> float:
 # workloads
 # ------------------------------------------------------------------------------------------
 
+# Workloads reported beside the configurations, with what they show.
+EXTRA = {"inplace_f32_1x524288x2x64":
+         "scaled variant of the fp32 [1,16,2,64] workload (same dtype, slice and BS1D layout, "
+         "S = 524288): the kernel's streaming rate at 768 MiB per launch"}
+
+
 def n_sets_for(algo_bytes: int) -> int:
     return max(1, math.ceil(MALL_DEFEAT_BYTES / algo_bytes))
 
@@ -285,7 +291,8 @@ def main() -> int:
                          "inplace_backward_bf16_8x4096x1x576_s512",
                          "cache_mrope_interleaved_neox_bf16_t16384",
                          "inplace_half_bf16_8x4096x1x576_s512",
-                         "inplace_heads_bf16_4x2048x32x192_s128_bs1d"]),
+                         "inplace_heads_bf16_4x2048x32x192_s128_bs1d",
+                         "inplace_f32_1x524288x2x64"]),
                     help="first is the headline; the rest are reported under `kernels`")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
@@ -335,6 +342,8 @@ def main() -> int:
              "tokens_per_s": round(case.tokens / (ms * 1e-3), 1),
              "algo_bytes_per_launch": case.algo_bytes, "buffer_sets": n_sets, "steps": steps,
              "traffic": traffic_for(name)}
+        if name in EXTRA:
+            r["extra"] = EXTRA[name]
         if args.resident:
             ms_r = time_launches(torch, calls[:1], steps, args.warmup, cyc)
             r["resident_us_per_launch"] = round(ms_r * 1e3, 3)

@@ -45,18 +45,19 @@ def pairwise_tables(pos: np.ndarray, length: int, dtype) -> tuple[torch.Tensor, 
     """cos/sin rows of `length` elements for the interleave layout: the angle of pair i is
     repeated on elements 2i and 2i+1.  Returns float64-derived tensors of `dtype`."""
     a = angles(pos, length // 2, length)
-    a = np.repeat(a, 2, axis=1)
     c = torch.from_numpy(np.cos(a)).to(dtype)
     s = torch.from_numpy(np.sin(a)).to(dtype)
-    return c, s
+    return (torch.stack([c, c], dim=2).reshape(len(a), length),
+            torch.stack([s, s], dim=2).reshape(len(a), length))
 
 
 def half_tables(pos: np.ndarray, length: int, dtype) -> tuple[torch.Tensor, torch.Tensor]:
     """cos/sin rows of `length` elements for the half (rotate-half) layout: the angles of the
     length/2 frequencies, written twice (element i and element i + length/2 share one)."""
     a = angles(pos, length // 2, length)
-    a = np.concatenate([a, a], axis=1)
-    return torch.from_numpy(np.cos(a)).to(dtype), torch.from_numpy(np.sin(a)).to(dtype)
+    c, s = np.cos(a), np.sin(a)
+    return (torch.from_numpy(np.concatenate([c, c], axis=1)).to(dtype),
+            torch.from_numpy(np.concatenate([s, s], axis=1)).to(dtype))
 
 
 def cos_sin_cache(max_seq: int, rotary_dim: int, dtype) -> torch.Tensor:
@@ -116,6 +117,13 @@ def inplace_f32_small(device="cpu"):
     """fp32 x [1,16,2,64], slice [0,64), cos/sin fp32 [1,16,1,64] from angles per pair."""
     return inplace_case("inplace_f32_1x16x2x64", 1, 16, 2, 64, torch.float32, torch.float32,
                         [0, 64], seed=1001, device=device)
+
+
+def inplace_f32_scaled(device="cpu"):
+    """The [1,16,2,64] fp32 layout with S = 524288, so that one launch moves 768 MiB, above the
+    256 MB Infinity Cache: the streaming rate of the same kernel configuration."""
+    return inplace_case("inplace_f32_1x524288x2x64", 1, 524288, 2, 64, torch.float32,
+                        torch.float32, [0, 64], seed=1009, device=device)
 
 
 def inplace_bf16_slice(device="cpu"):
@@ -244,5 +252,6 @@ CONFIGS["inplace_backward_bf16_8x4096x1x576_s512"] = inplace_bf16_slice_backward
 CONFIGS["cache_mrope_interleaved_neox_bf16_t16384"] = cache_mrope_interleaved
 CONFIGS["inplace_half_bf16_8x4096x1x576_s512"] = inplace_half_bf16_slice
 CONFIGS["inplace_heads_bf16_4x2048x32x192_s128_bs1d"] = inplace_heads_bf16_bs1d
+CONFIGS["inplace_f32_1x524288x2x64"] = inplace_f32_scaled
 HEADLINE = "inplace_bf16_8x4096x1x576_s512"
 

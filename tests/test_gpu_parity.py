@@ -64,6 +64,29 @@ def test_inplace_configs_full(cfg):
                   case.rotary_mode)
 
 
+def test_inplace_f32_scaled_sampled_rows_and_pair_norms():
+    """The 768 MiB fp32 workload [1,524288,2,64]: 4096 seeded sample positions (both heads)
+    compared with the oracle, and for every pair of the whole launch the norm kept: the
+    tables hold cos and sin of one angle per pair, so |(y0, y1)|^2 = |(x0, x1)|^2 up to the
+    fp32 roundings of the tables and the four products (about 11 units of 2^-24 in all)."""
+    case = W.CONFIGS["inplace_f32_1x524288x2x64"](DEV)
+    x = case.x
+    before = x.clone()
+    ra.rope_partial_inplace(x, case.cos, case.sin, 1, case.partial_slice)
+    torch.cuda.synchronize()
+    S = x.shape[1]
+    idx = torch.randperm(S, generator=torch.Generator().manual_seed(45))[:4096].sort().values
+    gi = idx.to(DEV)
+    check_inplace(before[:, gi].cpu(), x[:, gi], case.cos[:, gi], case.sin[:, gi],
+                  case.partial_slice, case.name + " sampled positions")
+    for h in range(0, S, 1 << 17):  # fp64 norms in slices of the sequence
+        a = before[:, h:h + (1 << 17)].double().view(-1, 2)
+        y = x[:, h:h + (1 << 17)].double().view(-1, 2)
+        na, ny = (a * a).sum(1), (y * y).sum(1)
+        worst = ((ny - na).abs() / na.clamp_min(1e-300)).max().item()
+        assert worst <= 2e-6, f"pair norm changed by {worst:.3g} in positions [{h}, {h + (1 << 17)})"
+
+
 LAYOUTS = {"BSND": lambda B, S, N: (B, S, N), "BS1D": lambda B, S, N: (B, S, 1),
            "B1ND": lambda B, S, N: (B, 1, N), "B11D": lambda B, S, N: (B, 1, 1),
            "111D": lambda B, S, N: (1, 1, 1), "1SND": lambda B, S, N: (1, S, N)}
