@@ -154,32 +154,6 @@ __device__ inline void st16(void *p, u32x4 v) {
 
 __device__ inline uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
-// Write-through stores, for data written back where it was just read.  A store with the
-// device-scope bit (sc1) goes through to memory instead of leaving a dirty line in its XCD's
-// L2, so the kernel's end has no write-back of dirty lines to wait for.  No compiler builtin
-// sets that bit on a global store, so these are buffer stores whose resource is based at the
-// address of the wavefront's first active lane, with each lane's 32-bit byte offset from it.
-// The caller guarantees that, for each such store instruction, no active lane's address lies
-// below the first active lane's and none lies 4 GiB or more above it.
-constexpr int kDeviceScope = 16;  // the sc1 bit of a buffer instruction's cache policy
-
-__device__ inline __amdgpu_buffer_rsrc_t wave_based_rsrc(const void *p, uint32_t &off) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a))));
-  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32))));
-  const uint64_t base = (uint64_t(hi) << 32) | lo;
-  off = uint32_t(a - base);
-  // raw buffer: stride 0, the largest record count, 32-bit data format word
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), 0,
-                                           int(0xFFFFFFFFu), 0x00020000);
-}
-
-__device__ inline void st16_through(void *p, u32x4 v) {
-  uint32_t off;
-  const __amdgpu_buffer_rsrc_t r = wave_based_rsrc(p, off);
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, int(off), 0, kDeviceScope);
-}
-
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <bool NT>
@@ -194,12 +168,6 @@ __device__ inline void st8(void *p, u32x2 v) {
   u32x2 *q = static_cast<u32x2 *>(p);
   if constexpr (NT) __builtin_nontemporal_store(v, q);
   else *q = v;
-}
-
-__device__ inline void st8_through(void *p, u32x2 v) {
-  uint32_t off;
-  const __amdgpu_buffer_rsrc_t r = wave_based_rsrc(p, off);
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, int(off), 0, kDeviceScope);
 }
 
 // N consecutive elements starting at element `i` of `p`, as float32.  VEC: the address is
@@ -247,28 +215,6 @@ __device__ inline void store_n(void *p, int64_t i, const float *f) {
   } else {
 #pragma unroll
     for (int e = 0; e < N; ++e) Io<T>::store1(p, i + e, f[e]);
-  }
-}
-
-// store_n with write-through vector stores (st16_through / st8_through and their caller
-// guarantee); the element path stores normally.
-template <typename T, int N, bool VEC>
-__device__ inline void store_n_through(void *p, int64_t i, const float *f) {
-  constexpr int kBytes = N * int(sizeof(T));
-  constexpr int kPW = Io<T>::kPerWord;
-  if constexpr (VEC && kBytes % 16 == 0) {
-    char *q = reinterpret_cast<char *>(static_cast<T *>(p) + i);
-#pragma unroll
-    for (int c = 0; c < kBytes / 16; ++c)
-      st16_through(q + 16 * c, u32x4{Io<T>::floats_to_word(f + (4 * c + 0) * kPW),
-                                     Io<T>::floats_to_word(f + (4 * c + 1) * kPW),
-                                     Io<T>::floats_to_word(f + (4 * c + 2) * kPW),
-                                     Io<T>::floats_to_word(f + (4 * c + 3) * kPW)});
-  } else if constexpr (VEC && kBytes == 8) {
-    st8_through(static_cast<T *>(p) + i,
-                u32x2{Io<T>::floats_to_word(f), Io<T>::floats_to_word(f + kPW)});
-  } else {
-    store_n<T, N, false, false>(p, i, f);
   }
 }
 
@@ -419,12 +365,9 @@ __device__ inline void rotate_pair(float a, float b, float c0, float c1, float s
 // heads of one (b, s) and loads the cos/sin chunk once for all of them.  Elements outside
 // [start, end) are never touched.  cos/sin rows are addressed with zero strides on broadcast
 // dims (BSND, BS1D, B1ND, B11D, 111D and mixed forms).  BWD runs the transpose of the pair map
-// on an incoming gradient (same access pattern).  x is written back with write-through
-// (device-scope) stores, and read with non-temporal loads at one head per lane, normal loads
-// at several (measured faster for each).  Each store instruction's lane addresses rise with
-// the lane and span at most 64 rows of x (D <= 1024), as the write-through stores require.
-// cos/sin are non-temporal too when each of their rows is read by one lane group, else
-// (broadcast) loaded normally so that the caches serve the repeats.
+// on an incoming gradient (same access pattern).  x is streamed (non-temporal); cos/sin are
+// streamed too when each of their rows is read by one lane group, else (broadcast) loaded
+// normally so that the caches serve the repeats.
 // ============================================================================================
 // One lane item: chunk `chunk` of the NHL x rows starting at row r * NHL, whose cos/sin row
 // is that of (b, s, head g * NHL).
@@ -450,8 +393,7 @@ __device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, u
     for (int j = 0; j < NHL; ++j)
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh)
-        load_words<XB, NHL == 1>(static_cast<const XT *>(p.x) + x0 + j * p.D + hh * hoff,
-                                 xr[j][hh]);
+        load_words<XB, true>(static_cast<const XT *>(p.x) + x0 + j * p.D + hh * hoff, xr[j][hh]);
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
       load_words<CB, CNT>(static_cast<const CT *>(p.cos) + coff + hh * hoff, cr[hh]);
@@ -512,7 +454,7 @@ __device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, u
         const float qr = xpv[j][e] * (BWD ? spv[e] : sv[0][e]);
         y[e] = (second == BWD) ? pr - qr : pr + qr;
       }
-      store_n_through<XT, V, VEC>(p.x, x0 + j * p.D, y);
+      store_n<XT, V, VEC, true>(p.x, x0 + j * p.D, y);
     }
     return;
   }
@@ -524,15 +466,15 @@ __device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, u
       for (int e = 0; e < V; ++e)
         rotate_pair<BWD>(xv[j][0][e], xv[j][1][e], cv[0][e], cv[1][e], sv[0][e], sv[1][e],
                          ya[e], yb[e]);
-      store_n_through<XT, V, VEC>(p.x, x0 + j * p.D, ya);
-      store_n_through<XT, V, VEC>(p.x, x0 + j * p.D + hoff, yb);
+      store_n<XT, V, VEC, true>(p.x, x0 + j * p.D, ya);
+      store_n<XT, V, VEC, true>(p.x, x0 + j * p.D + hoff, yb);
     } else {
       float y[V];
 #pragma unroll
       for (int e = 0; e < V; e += 2)
         rotate_pair<BWD>(xv[j][0][e], xv[j][0][e + 1], cv[0][e], cv[0][e + 1], sv[0][e],
                          sv[0][e + 1], y[e], y[e + 1]);
-      store_n_through<XT, V, VEC>(p.x, x0 + j * p.D, y);
+      store_n<XT, V, VEC, true>(p.x, x0 + j * p.D, y);
     }
   }
 }

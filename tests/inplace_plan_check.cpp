@@ -7,10 +7,7 @@
 //     (broadcast dims give index 0) at the same slice position, inside the cos/sin tensor;
 //   - in half mode an item's two chunks lie L/2 apart in one row; or, when the plan splits a
 //     pair across lanes (xch), the item it ^ xch -- the lane it ^ xch of the same wavefront --
-//     holds the same row's chunk L/2 away, and a row's lanes never straddle a wavefront;
-//   - the x address of every item is at or above that of its wavefront's first item
-//     (it & ~63, the first active lane: workgroups and the grid stride are multiples of 64
-//     items) and less than 4 GiB above it, as the kernel's write-through stores require.
+//     holds the same row's chunk L/2 away, and a row's lanes never straddle a wavefront.
 // Shapes cover both modes, every dtype pair, every broadcast layout, aligned and unaligned
 // pointers (vector and element paths) and 1/2/4/8 heads per lane.  A plan with 2^32 items is
 // checked for taking the 64-bit decode, with sampled items checked for bounds.  No GPU and no
@@ -122,13 +119,6 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
     const int64_t crow = int64_t(d.b) * p.cb + int64_t(d.s) * p.cs + int64_t(d.g) * NHL * p.cn;
     const int64_t coff = crow * L + int64_t(d.chunk) * V;
     const int64_t x0 = int64_t(d.r) * NHL * D + start + int64_t(d.chunk) * V;
-    {
-      const Decoded w = decode(p, it & ~uint64_t(63));
-      const int64_t xw = int64_t(w.r) * NHL * D + start + int64_t(w.chunk) * V;
-      CHECK(x0 >= xw && (x0 - xw) * esize(xdt) < (int64_t(1) << 32),
-            "item %llu lies below its wavefront's first item or 4 GiB above it",
-            (unsigned long long)it);
-    }
     if (p.xch) {
       const Decoded q = decode(p, it ^ p.xch);
       CHECK(q.r == d.r && q.chunk == (d.chunk ^ p.xch) && (it & 63) / (2 * p.xch) ==
@@ -188,10 +178,6 @@ static bool huge() {
           (unsigned long long)it);
     CHECK(x0 == int64_t(it) * 8, "item %llu maps to %lld", (unsigned long long)it,
           (long long)x0);
-    const Decoded w = decode(p, it & ~uint64_t(63));
-    const int64_t xw = int64_t(w.r) * D + int64_t(w.chunk) * 8;
-    CHECK(x0 >= xw && (x0 - xw) * 2 < (int64_t(1) << 32), "item %llu vs its wavefront",
-          (unsigned long long)it);
   }
   return true;
 }
