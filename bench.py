@@ -8,8 +8,8 @@ The cos/sin-cache kernel is timed the same way on its three workloads (rope NeoX
 GPT-J fp16 with a pass-through half, mrope bf16) and reported in `kernels`.
 
 Timing: inputs are resident in HBM; launches cycle over enough copies of the inputs that
-every pass touches >= 512 MiB before a buffer is reused (MI355X's 256 MB Infinity Cache
-cannot hold the working set); the host queues the timed launches behind a short GPU spin so
+every pass touches >= 2 GiB before a buffer is reused, so that MI355X's 256 MB Infinity
+Cache holds none of a buffer set's lines when it comes round again; the host queues the timed launches behind a short GPU spin so
 that they run back to back, and two HIP events on the launch stream bracket exactly `steps`
 launches.  Rank 0 prints one JSON line on stdout; progress goes to stderr.
 """
@@ -26,7 +26,11 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
-MALL_DEFEAT_BYTES = 512 << 20  # touched bytes between reuses of one buffer set
+# Bytes touched between reuses of one buffer set.  At 512 MiB, lines of a set were still in
+# the Infinity Cache at its next use (the in-place kernel measured 2-3% faster, a
+# write-through variant of it 7-10%); from 1 GiB to 2 GiB the times are equal, and much
+# larger rotations start to add TLB misses of their own.
+MALL_DEFEAT_BYTES = 2 << 30
 KERNEL_SRC = os.path.join(ROOT, "rope_partial_inplace_amd", "csrc", "rope_kernels.hip")
 
 
