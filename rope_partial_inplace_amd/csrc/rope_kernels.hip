@@ -486,8 +486,7 @@ __global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
   // apart so that the 64-bit division setup never runs in the 32-bit case.
   if (p.idx32) {
     const uint32_t items = uint32_t(p.items), ng = uint32_t(p.N / NHL);
-    for (uint32_t it = blockIdx.x * uint32_t(kBlock) + threadIdx.x; it < items;
-         it += gridDim.x * uint32_t(kBlock)) {
+    for (uint32_t it = blockIdx.x * p.block + threadIdx.x; it < items; it += gridDim.x * p.block) {
       const uint32_t r = fdiv(p.div_cpr, it);
       const uint32_t chunk = it - r * p.chunks_per_row;
       const uint32_t bs = fdiv(p.div_ng, r);
@@ -498,8 +497,8 @@ __global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
     }
   } else {
     const uint64_t items = uint64_t(p.items), ng = uint64_t(p.N) / NHL;
-    for (uint64_t it = uint64_t(blockIdx.x) * kBlock + threadIdx.x; it < items;
-         it += uint64_t(gridDim.x) * kBlock) {
+    for (uint64_t it = uint64_t(blockIdx.x) * p.block + threadIdx.x; it < items;
+         it += uint64_t(gridDim.x) * p.block) {
       const uint64_t r = it / p.chunks_per_row;
       const uint64_t chunk = it - r * p.chunks_per_row;
       const uint64_t bs = r / ng;
@@ -847,7 +846,6 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
 
 // ---- launch helpers -------------------------------------------------------------------------
 
-constexpr int64_t kMaxGrid = int64_t(1) << 20;
 
 thread_local std::string g_last_error;
 
@@ -936,7 +934,7 @@ int run_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor 
                                          : pick_inplace_dtype<false, true>(plan))
                             : (backward ? pick_inplace_dtype<true, false>(plan)
                                         : pick_inplace_dtype<false, false>(plan));
-  return launch(fn, (plan.items + kBlock - 1) / kBlock, kBlock, 0, stream, &plan);
+  return launch(fn, (plan.items + plan.block - 1) / plan.block, int(plan.block), 0, stream, &plan);
 }
 
 }  // namespace

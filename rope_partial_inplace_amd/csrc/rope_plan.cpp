@@ -206,7 +206,10 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
   p.cos_stream = bs_stream && (cos->shape[2] == p.N || p.N == int64_t(p.nhl));
   const int64_t ng = p.N / p.nhl;
   p.items = p.B * p.S * ng * p.chunks_per_row;
-  p.idx32 = p.items < (int64_t(1) << 32);
+  // 32-bit item indices: an index below 2^31 plus the grid stride (at most kMaxGrid * kBlock
+  // = 2^30 lanes) stays below 2^32, so a lane's index never wraps round to a low item.
+  p.idx32 = p.items <= (int64_t(1) << 31);
+  p.block = p.items > kOneRoundLanes ? uint32_t(kBlockMulti) : uint32_t(kBlock);
   p.div_cpr = make_fastdiv(p.chunks_per_row);
   p.div_ng = make_fastdiv(uint32_t(std::min<int64_t>(ng, 0xffffffff)));
   p.div_s = make_fastdiv(uint32_t(std::min<int64_t>(p.S, 0xffffffff)));

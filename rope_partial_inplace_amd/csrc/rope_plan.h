@@ -66,6 +66,7 @@ struct InplacePlan {
   bool cos_stream = false;  // every cos/sin row is read by exactly one lane group (streamed)
   bool idx32 = true;  // rows and items fit in 32 bits: use FastDiv below
   FastDiv div_cpr, div_ng, div_s;  // by chunks_per_row, N / nhl, S
+  uint32_t block = 1024;  // workgroup size: kBlock, or kBlockMulti past one round of lanes
 };
 
 // ---- cos/sin cache --------------------------------------------------------------------------
@@ -117,8 +118,14 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
 // Workgroup size and the work units (16-byte chunks / two-vector units) a lane carries per
 // pass.  Few units per lane and many waves keep more independent HBM requests in flight on
 // gfx950 than deep per-lane unrolling.
-constexpr int kBlock = 1024;      // in-place kernel workgroup (few, large workgroups: the
-                                  // headline launch is short and dispatch-bound)
+// In-place kernel: a launch that fits one round of resident lanes (256 CUs x 2048 lanes)
+// takes kBlock-lane workgroups, which dispatch faster; a longer one takes kBlockMulti, whose
+// slots free up and refill sooner once waves start to finish at different times.
+constexpr int kBlock = 1024;
+constexpr int kBlockMulti = 512;
+constexpr int64_t kOneRoundLanes = int64_t(256) * 2048;
+// Most workgroups in one launch; both kernels loop over the rest of the work.
+constexpr int64_t kMaxGrid = int64_t(1) << 20;
 constexpr int kCacheBlock = 256;  // cache kernel workgroup (one token tile)
 // Tokens given one-token tiles at the end of a cache launch: about one round of resident
 // cache workgroups on MI355X (256 CUs x 5 workgroups at the kernel's register use).

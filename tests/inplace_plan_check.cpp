@@ -9,8 +9,10 @@
 //     pair across lanes (xch), the item it ^ xch -- the lane it ^ xch of the same wavefront --
 //     holds the same row's chunk L/2 away, and a row's lanes never straddle a wavefront.
 // Shapes cover both modes, every dtype pair, every broadcast layout, aligned and unaligned
-// pointers (vector and element paths) and 1/2/4/8 heads per lane.  A plan with 2^32 items is
-// checked for taking the 64-bit decode, with sampled items checked for bounds.  No GPU and no
+// pointers (vector and element paths) and 1/2/4 heads per lane.  Every plan's workgroup size
+// follows its launch length, and a 32-bit plan's item index plus the grid stride never wraps;
+// plans of 2^31, 2^31 + 128 and 3 * 2^30 items sit either side of the 32-bit limit, and a plan
+// with 2^32 items is checked for taking the 64-bit decode, with sampled items in bounds.  No GPU and no
 // tensor data are involved: descriptors carry made-up, suitably aligned addresses.
 // Prints "ok <plans> <items>" or the first failure; exit status 1 on failure.
 #include <cstdint>
@@ -106,6 +108,10 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
                        p.chunks_per_row == 2 * p.xch && int64_t(p.xch) * V == L / 2),
         "lane exchange with xch %u, chunks %u, V %lld, L %lld", p.xch, p.chunks_per_row,
         (long long)V, (long long)L);
+  CHECK(!p.idx32 || uint64_t(p.items) - 1 + uint64_t(kMaxGrid) * p.block < (uint64_t(1) << 32),
+        "32-bit item index can wrap: items %lld, block %u", (long long)p.items, p.block);
+  CHECK(p.block == (p.items > kOneRoundLanes ? uint32_t(kBlockMulti) : uint32_t(kBlock)),
+        "workgroup of %u lanes for %lld items", p.block, (long long)p.items);
   CHECK(NHL == 1 || (Nc == 1 && N % NHL == 0), "heads per lane %lld with Nc %lld N %lld",
         (long long)NHL, (long long)Nc, (long long)N);
   CHECK(uint64_t(p.items) * NHL * NH * V == uint64_t(B * S * N * L),
@@ -152,6 +158,25 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
     const int64_t col = i % D;
     CHECK(hit[size_t(i)] == (col >= start && col < end ? 1 : 0),
           "x index %lld coverage %d", (long long)i, int(hit[size_t(i)]));
+  }
+  return true;
+}
+
+// Plans at the 32-bit limit: 2^31 items is the largest on the 32-bit decode; 2^31 + 128 and
+// 3 * 2^30 items (where a 32-bit index plus the grid stride would wrap) take the 64-bit one.
+static bool limits() {
+  for (int64_t S : {int64_t(1) << 24, (int64_t(1) << 24) + 1, int64_t(3) << 23}) {
+    const rope_tensor x = desc(0x10000000, ROPE_BF16, 1, S, 1, 1024);
+    const rope_tensor c = desc(0x90000000, ROPE_BF16, 1, 1, 1, 1024);
+    InplacePlan p;
+    std::string err;
+    CHECK(plan_inplace(&x, &c, &c, 1, nullptr, 0, &p, &err) == ROPE_OK, "%s", err.c_str());
+    CHECK(p.items == S * 128 && p.idx32 == (p.items <= (int64_t(1) << 31)) &&
+              p.block == uint32_t(kBlockMulti),
+          "S %lld: items %lld idx32 %d block %u", (long long)S, (long long)p.items,
+          int(p.idx32), p.block);
+    CHECK(!p.idx32 || uint64_t(p.items) - 1 + uint64_t(kMaxGrid) * p.block < (uint64_t(1) << 32),
+          "S %lld: 32-bit index can wrap", (long long)S);
   }
   return true;
 }
@@ -206,7 +231,7 @@ int main() {
               return 1;
             ++plans;
           }
-  if (!huge()) return 1;
+  if (!limits() || !huge()) return 1;
   std::printf("ok %d %llu\n", plans, (unsigned long long)items_checked);
   return 0;
 }
