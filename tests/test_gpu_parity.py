@@ -555,6 +555,29 @@ def test_half_mode_sweep(xdt, cdt, layout, shape, sl, direction):
         check_backward(before, g, case.cos, case.sin, sl, what, mode=0)
 
 
+@pytest.mark.parametrize("mode,direction", [(1, "forward"), (0, "forward"), (1, "backward"),
+                                            (0, "backward")])
+@pytest.mark.parametrize("xdt,cdt", DTYPE_PAIRS, ids=lambda d: str(d).split(".")[-1])
+@pytest.mark.parametrize("layout", ["BSND", "BS1D"])
+def test_inplace_past_one_round_of_lanes(xdt, cdt, layout, mode, direction):
+    """Launches longer than one round of resident lanes (256 CUs x 2048) run with 512-lane
+    workgroups: [4,2048,10,128] has 0.65M to 2.6M items (two heads per lane in BS1D)."""
+    B, S, N, D = 4, 2048, 10, 128
+    cshape = LAYOUTS[layout](B, S, N) + (D,)
+    case = W.inplace_case("rounds", B, S, N, D, xdt, cdt, None, cos_shape=cshape, seed=77,
+                          table="randn", device=DEV, rotary_mode=mode)
+    what = f"past one round {layout} mode {mode} {direction} {xdt}/{cdt}"
+    if direction == "forward":
+        before, x = run_inplace(case)
+        check_inplace(before, x, case.cos, case.sin, None, what, mode=mode)
+    else:
+        g = case.x
+        before = g.cpu()
+        ra.rope_partial_inplace_backward(g, case.cos, case.sin, mode, None)
+        torch.cuda.synchronize()
+        check_backward(before, g, case.cos, case.sin, None, what, mode=mode)
+
+
 def test_half_mode_backward_full_and_autograd():
     case = W.inplace_half_bf16_slice(DEV)
     g = case.x
