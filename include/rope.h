@@ -65,7 +65,9 @@ enum {
 };
 
 /* A strided tensor view.  shape[] and stride[] hold `ndim` entries (1..4); strides are in
- * elements.  `data` may be NULL only when the tensor has no elements. */
+ * elements.  `data` may be NULL only when the tensor has no elements.  Every entry point
+ * refuses (ROPE_ERR_PARAM_INVALID) a view with more than 2^53 elements or whose furthest
+ * element lies 2^53 or more elements from its first: no buffer is that large. */
 typedef struct {
   void *data;
   rope_dtype dtype;

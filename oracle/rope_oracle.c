@@ -226,10 +226,34 @@ static int shape_ok(const oro_tensor *t) {
   return 1;
 }
 
+/* Element count; INT64_MAX when the product of the dims would not fit. */
 static int64_t numel(const oro_tensor *t) {
   int64_t n = 1;
-  for (int d = 0; d < t->ndim; ++d) n *= t->shape[d];
+  for (int d = 0; d < t->ndim; ++d) {
+    if (t->shape[d] != 0 && n > INT64_MAX / t->shape[d]) return INT64_MAX;
+    n *= t->shape[d];
+  }
   return n;
+}
+
+/* A descriptor no real buffer can have: more than 2^53 elements, or its furthest element
+ * 2^53 or more elements from the first (sum over dims of (size - 1) * |stride|).  Such a
+ * tensor is an invalid argument (161002, [IPRM §返回值与错误码]); rejecting it also keeps
+ * every index computed below inside int64. */
+static int beyond_limits(const oro_tensor *t) {
+  const int64_t lim = (int64_t)1 << 53;
+  int64_t n = 1, reach = 0;
+  for (int d = 0; d < t->ndim; ++d) {
+    const int64_t size = t->shape[d], stride = t->stride[d];
+    if (size != 0 && n > lim / size) return 1;
+    n *= size;
+    if (size < 2) continue;
+    if (stride == INT64_MIN) return 1;
+    const int64_t step = stride < 0 ? -stride : stride;
+    if (step != 0 && size - 1 > (lim - 1 - reach) / step) return 1;
+    reach += (size - 1) * step;
+  }
+  return 0;
 }
 
 /* Row-major contiguity; the stride of a dimension of size 1 does not matter. */
@@ -312,6 +336,8 @@ static int partial_inplace(const oro_tensor *x, const oro_tensor *cos_t, const o
   for (int i = 0; i < 3; ++i)
     if (!shape_ok(ts[i]) || ts[i]->ndim != 4)
       return fail(ORO_ERR_PARAM_INVALID, "xRef, cos and sin must be 4-D");
+  for (int i = 0; i < 3; ++i)
+    if (beyond_limits(ts[i])) return fail(ORO_ERR_PARAM_INVALID, "tensor too large to exist");
   for (int d = 0; d < 4; ++d)
     if (cos_t->shape[d] != sin_t->shape[d])
       return fail(ORO_ERR_PARAM_INVALID, "cos and sin shapes differ");
@@ -491,6 +517,9 @@ static int cos_sin_cache(const oro_tensor *positions, const oro_tensor *query_in
   for (int i = 0; i < 5; ++i)
     if (!shape_ok(two_d[i]) || two_d[i]->ndim != 2)
       return fail(ORO_ERR_PARAM_INVALID, "queryIn, keyIn, cosSinCache and outputs must be 2-D");
+  for (int i = 0; i < 6; ++i)
+    if (shape_ok(all[i]) && beyond_limits(all[i]))
+      return fail(ORO_ERR_PARAM_INVALID, "tensor too large to exist");
   for (int i = 0; i < 3; ++i)
     if (two_d[i]->shape[0] <= 0 || two_d[i]->shape[1] <= 0)
       return fail(ORO_ERR_PARAM_INVALID, "queryIn, keyIn and cosSinCache must be non-empty");
@@ -512,7 +541,8 @@ static int cos_sin_cache(const oro_tensor *positions, const oro_tensor *query_in
       return fail(ORO_ERR_PARAM_INVALID, "mropeSection must have 3 or 4 elements");
     int64_t sum = 0;
     for (int64_t i = 0; i < mrope_section_len; ++i) {
-      if (mrope_section[i] < 0) return fail(ORO_ERR_PARAM_INVALID, "mropeSection has a negative element");
+      if (mrope_section[i] < 0 || mrope_section[i] > rd)
+        return fail(ORO_ERR_PARAM_INVALID, "mropeSection element outside [0, rotaryDim]");
       sum += mrope_section[i];
     }
     if (mrope_section[0] > 0) {

@@ -34,10 +34,32 @@ bool valid_rank(const rope_tensor *t) {
   return true;
 }
 
+// Elements of t (saturating at INT64_MAX instead of overflowing).
 int64_t count(const rope_tensor *t) {
   int64_t n = 1;
-  for (int d = 0; d < t->ndim; ++d) n *= t->shape[d];
+  for (int d = 0; d < t->ndim; ++d)
+    if (__builtin_mul_overflow(n, t->shape[d], &n)) return INT64_MAX;
   return n;
+}
+
+// The element count and the offset of the furthest element are at most 2^53 (byte offsets of
+// elements of up to 8 bytes stay below 2^56, far beyond any device memory), computed without
+// overflow.  A descriptor outside that cannot describe real memory, and the planning
+// arithmetic on it would overflow.
+bool addressable(const rope_tensor *t) {
+  constexpr int64_t kLimit = int64_t(1) << 53;
+  int64_t n = 1, far = 0;
+  for (int d = 0; d < t->ndim; ++d) {
+    int64_t off;
+    if (__builtin_mul_overflow(n, t->shape[d], &n) || n > kLimit) return false;
+    if (t->shape[d] == 0) continue;
+    if (__builtin_mul_overflow(t->shape[d] - 1, t->stride[d], &off) || off < -kLimit ||
+        off > kLimit)
+      return false;
+    far += off < 0 ? -off : off;  // at most 4 * 2^53: no overflow
+    if (far >= kLimit) return false;
+  }
+  return true;
 }
 
 bool row_major(const rope_tensor *t) {
@@ -113,6 +135,9 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
   for (const rope_tensor *t : {x, cos, sin})
     if (!valid_rank(t) || t->ndim != 4)
       return reject(err, ROPE_ERR_PARAM_INVALID, "xRef, cos and sin must be 4-D");
+  for (const rope_tensor *t : {x, cos, sin})
+    if (!addressable(t))
+      return reject(err, ROPE_ERR_PARAM_INVALID, "tensor extent beyond 2^56 elements or bytes");
   for (int d = 0; d < 4; ++d)
     if (cos->shape[d] != sin->shape[d])
       return reject(err, ROPE_ERR_PARAM_INVALID, "cos and sin shapes differ");
@@ -247,6 +272,10 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
   for (const rope_tensor *t : {query_in, key_in, cache, query_out, key_out})
     if (!valid_rank(t) || t->ndim != 2)
       return reject(err, ROPE_ERR_PARAM_INVALID, "queryIn, keyIn, cache and outputs must be 2-D");
+  if (!valid_rank(positions)) return reject(err, ROPE_ERR_PARAM_INVALID, "bad positions shape");
+  for (const rope_tensor *t : all)
+    if (!addressable(t))
+      return reject(err, ROPE_ERR_PARAM_INVALID, "tensor extent beyond 2^56 elements or bytes");
   for (const rope_tensor *t : {query_in, key_in, cache})
     if (t->shape[0] == 0 || t->shape[1] == 0)
       return reject(err, ROPE_ERR_PARAM_INVALID, "queryIn, keyIn and cache must be non-empty");
@@ -267,8 +296,8 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
       return reject(err, ROPE_ERR_PARAM_INVALID, "mrope_section needs 3 or 4 entries");
     int64_t total = 0;
     for (int64_t i = 0; i < mrope_section_len; ++i) {
-      if (mrope_section[i] < 0)
-        return reject(err, ROPE_ERR_PARAM_INVALID, "negative mrope_section entry");
+      if (mrope_section[i] < 0 || mrope_section[i] > rd)
+        return reject(err, ROPE_ERR_PARAM_INVALID, "mrope_section entry outside [0, rotaryDim]");
       total += mrope_section[i];
     }
     if (mrope_section[0] > 0) {
@@ -303,7 +332,6 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
   if (rd > head_size || rd % align_elems != 0)
     return reject(err, ROPE_ERR_PARAM_INVALID, "rotaryDim must be a 64-byte multiple <= headSize");
 
-  if (!valid_rank(positions)) return reject(err, ROPE_ERR_PARAM_INVALID, "bad positions shape");
   if (!mrope) {
     if (positions->ndim != 1 || positions->shape[0] != T)
       return reject(err, ROPE_ERR_PARAM_INVALID, "rope mode: positions must be [numTokens]");

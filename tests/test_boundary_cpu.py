@@ -149,6 +149,17 @@ INPLACE_CASES = [
     ("negative dim", lambda b: (dict(b[0], shape=[-2, 3, 2, 16]), b[1], b[2], 1, [0, 8]),
      INVALID),
     ("negative slice length", lambda b: (b[0], b[1], b[2], 1, [0, 8], -1), INVALID),
+    # descriptors no buffer can have: refused before any size arithmetic could overflow
+    ("x beyond 2^53 elements", lambda b: (dict(b[0], shape=[1 << 20, 1 << 20, 1 << 14, 16],
+                                               stride=[1 << 38, 1 << 18, 16, 1]), b[1], b[2], 1,
+                                          [0, 8]), INVALID),
+    ("x element count overflows int64", lambda b: (
+        dict(b[0], shape=[1 << 21, 1 << 21, 1 << 21, 16], stride=[1 << 46, 1 << 25, 16, 1]),
+        b[1], b[2], 1, [0, 8]), INVALID),
+    ("cos reaches 2^60 elements", lambda b: (b[0], dict(b[1], stride=[1 << 60, 8, 8, 1]), b[2],
+                                             1, [0, 8]), INVALID),
+    ("x data null, overflowing shape", lambda b: (
+        dict(b[0], data=None, shape=[1 << 40, 1 << 40, 1, 16]), b[1], b[2], 1, [0, 8]), NULLPTR),
     # accepted, nothing launched
     ("empty slice", lambda b: (b[0], b[1], b[2], 1, [4, 4]), 0),
     ("empty slice ignores cos last dim", lambda b: (b[0], b[1], b[2], 1, [6, 6]), 0),
@@ -266,6 +277,14 @@ CACHE_CASES = [
      INVALID),
     ("keyOut overlaps queryIn", lambda a: upd(a, ko=dict(a["ko"], data=a["q"]["data"])),
      INVALID),
+    # descriptors no buffer can have, and mrope entries that would overflow a sum
+    ("query row stride 2^60", lambda a: upd(a, q=dict(a["q"], stride=[1 << 60, 1])), INVALID),
+    ("key element count overflows int64", lambda a: upd(
+        a, k=dict(a["k"], shape=[1 << 62, 1 << 62]), ko=dict(a["ko"], shape=[1 << 62, 1 << 62])),
+     INVALID),
+    ("positions beyond 2^53 elements", lambda a: upd(a, pos=dict(a["pos"], shape=[1 << 60])),
+     INVALID),
+    ("mrope entries of 2^62", lambda a: upd(a, msec=[1 << 62, 1 << 62, 1 << 62]), INVALID),
 ]
 
 
