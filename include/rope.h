@@ -25,6 +25,8 @@
  *    call returns, or synchronizes.  Host arrays (partial_slice, mrope_section) are read
  *    during the call only.
  *  - Stream: `stream` is a hipStream_t (NULL = the null stream of the current device).  The
+ *    kernels run on the current HIP device: the stream and every tensor must belong to it
+ *    (hipSetDevice first when several GPUs are in use).  The
  *    call returns once the work is enqueued; results are visible after the stream is
  *    synchronized.  The library is stateless and reentrant; calls that touch the same
  *    buffers must be ordered by the caller (same stream or events).

@@ -140,14 +140,25 @@ def _check(code: int):
         raise RopeError(code, last_error())
 
 
+def _on_device(dev, fn, args) -> int:
+    """fn(*args) with the tensors' GPU as the current HIP device: the library launches on the
+    current device, which must own the stream and the tensors."""
+    import torch
+    if dev is None or dev.index is None or dev.index == torch.cuda.current_device():
+        return fn(*args)
+    with torch.cuda.device(dev):
+        return fn(*args)
+
+
 def rope_partial_inplace(x, cos, sin, rotary_mode: int = 1, partial_slice=None, stream=None):
     """In-place partial RoPE on x[..., start:end) ([IPRM §计算原理与公式]): rotary_mode 1
     interleave, 0 half mode (x1, x2 the two halves of the slice)."""
     dev = _device_of([x, cos, sin])
     dx, dc, ds = describe(x), describe(cos), describe(sin)
     sl, sl_len = _int_array(partial_slice)
-    _check(LIB.rope_partial_inplace(ctypes.byref(dx), ctypes.byref(dc), ctypes.byref(ds),
-                                    int(rotary_mode), sl, sl_len, _stream_handle(stream, dev)))
+    _check(_on_device(dev, LIB.rope_partial_inplace,
+                      (ctypes.byref(dx), ctypes.byref(dc), ctypes.byref(ds), int(rotary_mode),
+                       sl, sl_len, _stream_handle(stream, dev))))
 
 
 def rope_partial_inplace_backward(g, cos, sin, rotary_mode: int = 1, partial_slice=None,
@@ -157,9 +168,9 @@ def rope_partial_inplace_backward(g, cos, sin, rotary_mode: int = 1, partial_sli
     dev = _device_of([g, cos, sin])
     dg, dc, ds = describe(g), describe(cos), describe(sin)
     sl, sl_len = _int_array(partial_slice)
-    _check(LIB.rope_partial_inplace_backward(ctypes.byref(dg), ctypes.byref(dc),
-                                             ctypes.byref(ds), int(rotary_mode), sl, sl_len,
-                                             _stream_handle(stream, dev)))
+    _check(_on_device(dev, LIB.rope_partial_inplace_backward,
+                      (ctypes.byref(dg), ctypes.byref(dc), ctypes.byref(ds), int(rotary_mode),
+                       sl, sl_len, _stream_handle(stream, dev))))
 
 
 def _autograd_function():
@@ -209,8 +220,9 @@ def _cache_args(positions, query_in, key_in, cos_sin_cache, mrope_section, head_
             ctypes.byref(descs[3]), ms, ms_len, int(head_size), int(bool(is_neox_style)))
     tail = (ctypes.byref(descs[4]), ctypes.byref(descs[5]), _stream_handle(stream, dev))
     if cache_mode is None:
-        return LIB.rope_with_cos_sin_cache, head + tail, (tensors, descs, ms)
-    return LIB.rope_with_cos_sin_cache_v2, head + (int(cache_mode),) + tail, (tensors, descs, ms)
+        return LIB.rope_with_cos_sin_cache, head + tail, (tensors, descs, ms), dev
+    return (LIB.rope_with_cos_sin_cache_v2, head + (int(cache_mode),) + tail,
+            (tensors, descs, ms), dev)
 
 
 def _with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section, head_size,
@@ -222,10 +234,10 @@ def _with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_sectio
         query_out = torch.empty(query_in.shape, dtype=query_in.dtype, device=query_in.device)
     if key_out is None:
         key_out = torch.empty(key_in.shape, dtype=key_in.dtype, device=key_in.device)
-    fn, args, _keep = _cache_args(positions, query_in, key_in, cos_sin_cache, mrope_section,
-                                  head_size, is_neox_style, cache_mode, query_out, key_out,
-                                  stream)
-    _check(fn(*args))
+    fn, args, _keep, dev = _cache_args(positions, query_in, key_in, cos_sin_cache,
+                                       mrope_section, head_size, is_neox_style, cache_mode,
+                                       query_out, key_out, stream)
+    _check(_on_device(dev, fn, args))
     return query_out, key_out
 
 
@@ -255,11 +267,11 @@ class PreparedCall:
     issues exactly one C-ABI call with the prebuilt descriptors.  The tensors must stay
     alive and keep their storage while the object is used."""
 
-    def __init__(self, fn, args, keep):
-        self._fn, self._args, self._keep = fn, args, keep
+    def __init__(self, fn, args, keep, dev=None):
+        self._fn, self._args, self._keep, self._dev = fn, args, keep, dev
 
     def __call__(self) -> None:
-        _check(self._fn(*self._args))
+        _check(_on_device(self._dev, self._fn, self._args))
 
 
 def prepare_partial_inplace(x, cos, sin, rotary_mode: int = 1, partial_slice=None,
@@ -270,14 +282,14 @@ def prepare_partial_inplace(x, cos, sin, rotary_mode: int = 1, partial_slice=Non
     args = (ctypes.byref(dx), ctypes.byref(dc), ctypes.byref(ds), int(rotary_mode), sl, sl_len,
             _stream_handle(stream, dev))
     fn = LIB.rope_partial_inplace_backward if backward else LIB.rope_partial_inplace
-    return PreparedCall(fn, args, (x, cos, sin, dx, dc, ds, sl))
+    return PreparedCall(fn, args, (x, cos, sin, dx, dc, ds, sl), dev)
 
 
 def prepare_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,
                                head_size, is_neox_style, query_out, key_out, stream=None,
                                cache_mode: int | None = None) -> PreparedCall:
     """cache_mode None: the V1 entry point; else the V2 one with that cacheMode."""
-    fn, args, keep = _cache_args(positions, query_in, key_in, cos_sin_cache, mrope_section,
-                                 head_size, is_neox_style, cache_mode, query_out, key_out,
-                                 stream)
-    return PreparedCall(fn, args, keep)
+    fn, args, keep, dev = _cache_args(positions, query_in, key_in, cos_sin_cache, mrope_section,
+                                      head_size, is_neox_style, cache_mode, query_out, key_out,
+                                      stream)
+    return PreparedCall(fn, args, keep, dev)
