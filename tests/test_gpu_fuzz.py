@@ -42,7 +42,7 @@ def inplace_fuzz(seed):
                 backward=backward)
 
 
-@pytest.mark.parametrize("seed", range(80))
+@pytest.mark.parametrize("seed", range(300))
 def test_inplace_fuzz(seed):
     cfg = inplace_fuzz(seed)
     B, S, N, D = cfg["shape"]
@@ -86,7 +86,7 @@ def cache_fuzz(seed):
                 cache_mode=cache_mode, pad_q=pad_q)
 
 
-@pytest.mark.parametrize("seed", range(80))
+@pytest.mark.parametrize("seed", range(300))
 def test_cache_fuzz(seed):
     cfg = cache_fuzz(seed)
     g = W.generator(3000 + seed, DEV)
