@@ -105,6 +105,22 @@ def copy_ceiling_gbs(torch, nbytes=1 << 30) -> float:
     return 2 * a.numel() / (ms * 1e-3) / 1e9
 
 
+def copy_same_bytes(torch, moved: int, cyc: float, steps: int = 100) -> dict:
+    """A device-to-device copy (torch's copy_) that reads and writes `moved` bytes in all,
+    timed like the kernels (buffer pairs rotated over MALL_DEFEAT_BYTES, launches back to
+    back): what a plain copy of the headline's bytes achieves at the same footprint."""
+    half = moved // 2
+    n_sets = max(1, math.ceil(MALL_DEFEAT_BYTES / moved))
+    pairs = [(torch.empty(half, dtype=torch.uint8, device="cuda"),
+              torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(n_sets)]
+    calls = [(lambda a=a, b=b: b.copy_(a)) for a, b in pairs]
+    ms = time_launches(torch, calls, steps, 10, cyc)
+    del calls, pairs
+    torch.cuda.empty_cache()
+    return {"bytes": 2 * half, "us": round(ms * 1e3, 3),
+            "gbs": round(2 * half / (ms * 1e-3) / 1e9, 1), "buffer_sets": n_sets}
+
+
 # ------------------------------------------------------------------------------------------
 # workloads
 # ------------------------------------------------------------------------------------------
@@ -363,6 +379,8 @@ def main() -> int:
     head = names[0]
     hr = results[head]
     ceiling = copy_ceiling_gbs(torch)
+    same = copy_same_bytes(torch, hr["algo_bytes_per_launch"], cyc)
+    log(f"copy of the headline's bytes: {same['us']} us, {same['gbs']} GB/s")
     log(f"device-to-device copy: {ceiling:.0f} GB/s")
     out = {
         "metric": "achieved HBM GB/s (and % of peak) + tokens/sec for RoPE apply on one MI355X",
@@ -386,6 +404,7 @@ def main() -> int:
                      "traffic": traffic_for(head), "kernel": hr["kernel"]},
         "kernels": {k: v for k, v in results.items() if k != head},
         "copy_ceiling_gbs": round(ceiling, 1),
+        "copy_same_bytes": same,
         "kernel_source_sha256_16": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
