@@ -41,6 +41,8 @@
  *  R21 rotary_mode 0 (half mode, listed but not enabled on the pages) is enabled: x1 and x2
  *      are the first and second halves of the slice, x_rotate = cat(-x2, x1), the same formula
  *      x*cos + x_rotate*sin; 2 and 3 stay invalid.
+ *  R22 the in-place op writes xRef while reading cos and sin, so xRef may share no memory
+ *      with either (161002); cos and sin are only read and may share memory.
  */
 #include <math.h>
 #include <stdint.h>
@@ -268,6 +270,14 @@ static int contiguous(const oro_tensor *t) {
 
 static int is_float_dtype(int dt) { return dt == ORO_F32 || dt == ORO_F16 || dt == ORO_BF16; }
 
+/* Whether two contiguous tensors share any byte. */
+static int contiguous_spans_meet(const oro_tensor *a, const oro_tensor *b) {
+  const uintptr_t a0 = (uintptr_t)a->data, b0 = (uintptr_t)b->data;
+  const uintptr_t a1 = a0 + (uintptr_t)numel(a) * (uintptr_t)elem_size(a->dtype);
+  const uintptr_t b1 = b0 + (uintptr_t)numel(b) * (uintptr_t)elem_size(b->dtype);
+  return a0 < b1 && b0 < a1;
+}
+
 /* ==========================================================================================
  * Operation A: in-place partial RoPE, interleave mode (and half mode, reading R21).
  *   [IPRM §计算原理与公式]     x1 = x[..., ::2], x2 = x[..., 1::2], x_rotate from -x2 and x1,
@@ -372,6 +382,10 @@ static int partial_inplace(const oro_tensor *x, const oro_tensor *cos_t, const o
   for (int d = 0; d < 3; ++d)
     if (!(cos_t->shape[d] == 1 || cos_t->shape[d] == x->shape[d]))
       return fail(ORO_ERR_PARAM_INVALID, "cos/sin do not broadcast to xRef");
+  /* reading R22: xRef is written in place, so it may share no memory with cos or sin (they
+   * are only read, and may share memory with each other) */
+  if (numel(x) > 0 && (contiguous_spans_meet(x, cos_t) || contiguous_spans_meet(x, sin_t)))
+    return fail(ORO_ERR_PARAM_INVALID, "xRef overlaps cos or sin");
 
   /* fp64 twin of untouched data: exact copies */
   if (x64)

@@ -187,6 +187,10 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
     p.noop = true;
     return ROPE_OK;
   }
+  // x is written in place while other lanes read cos/sin: no shared memory (cos and sin are
+  // only read and may share memory with each other).
+  if (overlap(x, cos) || overlap(x, sin))
+    return reject(err, ROPE_ERR_PARAM_INVALID, "xRef overlaps cos or sin");
   const int64_t Sc = cos->shape[1], Nc = cos->shape[2];
   p.cn = cos->shape[2] == 1 ? 0 : 1;
   p.cs = cos->shape[1] == 1 ? 0 : Nc;

@@ -162,12 +162,15 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
   return true;
 }
 
+// cos/sin of the very large plans below sit 2^46 bytes up, clear of x's tens of GiB.
+constexpr uintptr_t kFarTables = uintptr_t(1) << 46;
+
 // Plans at the 32-bit limit: 2^31 items is the largest on the 32-bit decode; 2^31 + 128 and
 // 3 * 2^30 items (where a 32-bit index plus the grid stride would wrap) take the 64-bit one.
 static bool limits() {
   for (int64_t S : {int64_t(1) << 24, (int64_t(1) << 24) + 1, int64_t(3) << 23}) {
     const rope_tensor x = desc(0x10000000, ROPE_BF16, 1, S, 1, 1024);
-    const rope_tensor c = desc(0x90000000, ROPE_BF16, 1, 1, 1, 1024);
+    const rope_tensor c = desc(kFarTables, ROPE_BF16, 1, 1, 1, 1024);
     InplacePlan p;
     std::string err;
     CHECK(plan_inplace(&x, &c, &c, 1, nullptr, 0, &p, &err) == ROPE_OK, "%s", err.c_str());
@@ -185,7 +188,7 @@ static bool limits() {
 static bool huge() {
   const int64_t S = int64_t(1) << 25, D = 1024;
   const rope_tensor x = desc(0x10000000, ROPE_BF16, 1, S, 1, D);
-  const rope_tensor c = desc(0x90000000, ROPE_BF16, 1, 1, 1, D);
+  const rope_tensor c = desc(kFarTables, ROPE_BF16, 1, 1, 1, D);
   InplacePlan p;
   std::string err;
   CHECK(plan_inplace(&x, &c, &c, 1, nullptr, 0, &p, &err) == ROPE_OK, "%s", err.c_str());

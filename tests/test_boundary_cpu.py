@@ -149,6 +149,11 @@ INPLACE_CASES = [
     ("negative dim", lambda b: (dict(b[0], shape=[-2, 3, 2, 16]), b[1], b[2], 1, [0, 8]),
      INVALID),
     ("negative slice length", lambda b: (b[0], b[1], b[2], 1, [0, 8], -1), INVALID),
+    # x is written in place: it may share no memory with cos or sin (reading R22)
+    ("cos inside x", lambda b: (b[0], dict(b[1], data=b[0]["data"]), b[2], 1, [0, 8]),
+     INVALID),
+    ("sin overlaps the end of x", lambda b: (b[0], b[1], dict(b[2], data=b[0]["data"] + 320), 1,
+                                             [0, 8]), INVALID),
     # descriptors no buffer can have: refused before any size arithmetic could overflow
     ("x beyond 2^53 elements", lambda b: (dict(b[0], shape=[1 << 20, 1 << 20, 1 << 14, 16],
                                                stride=[1 << 38, 1 << 18, 16, 1]), b[1], b[2], 1,

@@ -116,6 +116,17 @@ def test_inplace_sweep(xdt, cdt, layout, shape, sl):
     check_inplace(before, x, case.cos, case.sin, sl, f"{layout} {shape} {sl} {xdt}/{cdt}")
 
 
+def test_inplace_cos_and_sin_may_share_memory():
+    """cos and sin are only read, so one tensor may serve as both (reading R22 forbids only
+    overlap with x)."""
+    case = W.inplace_case("shared", 2, 33, 4, 64, torch.bfloat16, torch.float32, [0, 64],
+                          seed=9, table="randn", device=DEV)
+    before, x = case.x.cpu(), case.x
+    ra.rope_partial_inplace(x, case.cos, case.cos, 1, [0, 64])
+    torch.cuda.synchronize()
+    check_inplace(before, x, case.cos, case.cos, [0, 64], "cos and sin one tensor")
+
+
 def test_inplace_misaligned_base_uses_element_path():
     """x starts 2 bytes past a 16-byte boundary: the library must take its element-wise path
     and still match."""
