@@ -105,7 +105,8 @@ typedef struct {
  *                ROPE_OK at once without launching anything (and without checking cos/sin's
  *                last dim).  start may be odd.
  * Constraints (else ROPE_ERR_PARAM_INVALID): 4-D tensors, D even and D <= 1024, cos and
- * sin of one shape whose last dim is L, contiguous tensors.  NULL x/cos/sin, or NULL data
+ * sin of one shape whose last dim is L, contiguous tensors, and x sharing no memory with
+ * cos or sin (cos and sin may be one tensor).  NULL x/cos/sin, or NULL data
  * of a non-empty tensor, gives ROPE_ERR_PARAM_NULLPTR.  An x with no elements is a no-op.
  */
 int rope_partial_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor *sin,
