@@ -238,7 +238,9 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
   // 32-bit item indices: an index below 2^31 plus the grid stride (at most kMaxGrid * kBlock
   // = 2^30 lanes) stays below 2^32, so a lane's index never wraps round to a low item.
   p.idx32 = p.items <= (int64_t(1) << 31);
-  p.block = p.items > kOneRoundLanes ? uint32_t(kBlockMulti) : uint32_t(kBlock);
+  uint32_t block = kBlock;
+  while (block > uint32_t(kBlockMin) && p.items < kComputeUnits * int64_t(block)) block /= 2;
+  p.block = p.items > kOneRoundLanes ? uint32_t(kBlockMulti) : block;
   p.div_cpr = make_fastdiv(p.chunks_per_row);
   p.div_ng = make_fastdiv(uint32_t(std::min<int64_t>(ng, 0xffffffff)));
   p.div_s = make_fastdiv(uint32_t(std::min<int64_t>(p.S, 0xffffffff)));
@@ -433,6 +435,7 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
     if (fill >= 0.9) break;
   }
   tt = std::min<int64_t>(tt, T);
+  if (T <= kOneRoundCacheTiles) tt = 1;
   if (rd * 4 * tt > 64 * 1024)
     return reject(err, ROPE_ERR_PARAM_INVALID, "rotaryDim too large for the LDS tile (max 16384)");
   p.tile_tokens = uint32_t(tt);

@@ -118,12 +118,20 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
 // Workgroup size and the work units (16-byte chunks / two-vector units) a lane carries per
 // pass.  Few units per lane and many waves keep more independent HBM requests in flight on
 // gfx950 than deep per-lane unrolling.
-// In-place kernel: a launch that fits one round of resident lanes (256 CUs x 2048 lanes)
-// takes kBlock-lane workgroups, which dispatch faster; a longer one takes kBlockMulti, whose
-// slots free up and refill sooner once waves start to finish at different times.
+// In-place kernel workgroups.  A launch that fits one round of resident lanes (256 CUs x
+// 2048 lanes) takes the largest of kBlock, kBlock/2, ... 64 lanes that still gives every CU a
+// workgroup: large workgroups dispatch faster, but a small launch in a few large workgroups
+// funnels all its traffic through a few CUs.  A longer launch takes kBlockMulti, whose slots
+// free up and refill sooner once waves start to finish at different times.
+constexpr int64_t kComputeUnits = 256;  // MI355X
 constexpr int kBlock = 1024;
 constexpr int kBlockMulti = 512;
-constexpr int64_t kOneRoundLanes = int64_t(256) * 2048;
+constexpr int kBlockMin = 64;
+constexpr int64_t kOneRoundLanes = kComputeUnits * 2048;
+// Cache kernel: with no more tokens than one round of resident workgroups (256 CUs x 7),
+// every token gets a tile of its own, so each workgroup's chain of dependent memory round
+// trips is as short as it can be.
+constexpr int64_t kOneRoundCacheTiles = kComputeUnits * 7;
 // Most workgroups in one launch; both kernels loop over the rest of the work.
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
 constexpr int kCacheBlock = 256;  // cache kernel workgroup (one token tile)

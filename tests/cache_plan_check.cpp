@@ -6,14 +6,16 @@
 //     element at the same position of the same head (NeoX units pair elements i and
 //     i + rotaryDim/2, GPT-J units hold whole pairs), and inputs are read inside their rows;
 //   - the rotated part of each unit reads the cos|sin elements of its own pair indices;
-//   - every token belongs to exactly one tile (tiles of tile_tokens, then one-token tiles);
+//   - every token belongs to exactly one tile (tiles of tile_tokens, then one-token tiles),
+//     and a launch of at most one round of workgroups (256 CUs x 7) has one-token tiles only;
 //   - the staging chunks of a tile write each of its tile_tokens * rotaryDim LDS elements once,
 //     inside the LDS size the launch requests, and each element's position row is the one the
 //     stitching assigns (sections for cacheMode 0, the i mod 3 rule below 3 * mropeSection[1]
 //     for cacheMode 1), with one row per chunk unless the plan takes the multi-row path.
 // Shapes cover every dtype, both styles, rope mode, every whitelisted mropeSection and both
-// cacheModes, pass-through parts, token counts that leave a ragged last tile or reach the
-// one-token tiles of the tapered end, and padded row strides.  No GPU and no tensor data are
+// cacheModes, pass-through parts, token counts that leave a ragged last tile, reach the
+// one-token tiles of the tapered end or sit either side of one round of workgroups, and
+// padded row strides.  No GPU and no tensor data are
 // involved.
 // Prints "ok <plans> <items>" or the first failure; exit status 1 on failure.
 #include <cstdint>
@@ -99,6 +101,8 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
   const int st = plan_cache(&pos, &q, &k, &c, m ? sec.data() : nullptr, m, H, neox ? 1 : 0,
                             cache_mode, &qo, &ko, &p, &err);
   CHECK(st == ROPE_OK, "plan rejected: %s", err.c_str());
+  CHECK(T > 256 * 7 || p.tile_tokens == 1, "%lld tokens fit one round of workgroups but "
+        "share tiles of %u", (long long)T, p.tile_tokens);
   const int64_t V = p.vec, half = rd / 2;
   const int64_t es = dt == ROPE_F32 ? 4 : 2;
   CHECK(V * es == 16, "vector of %lld elements", (long long)V);
@@ -214,7 +218,8 @@ int main() {
           else rds = {2 * (sec[0] + sec[1] + sec[2] + (sec.size() == 4 ? sec[3] : 0))};
           for (int64_t rd : rds)
             for (int64_t extra : {int64_t(0), align, 2 * align})
-              for (int64_t T : {int64_t(1), int64_t(7), int64_t(61), int64_t(5123)})
+              for (int64_t T : {int64_t(1), int64_t(7), int64_t(61), int64_t(1792),
+                                int64_t(1793), int64_t(5123)})
                 for (auto hq : {std::pair<int64_t, int64_t>{1, 1}, {5, 3}, {32, 8}}) {
                   if (T > 1000 && hq.first != 1) continue;  // the long case: one head each
                   const int64_t pad = (T == 7) ? align : 0;

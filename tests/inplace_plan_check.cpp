@@ -110,8 +110,15 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
         (long long)V, (long long)L);
   CHECK(!p.idx32 || uint64_t(p.items) - 1 + uint64_t(kMaxGrid) * p.block < (uint64_t(1) << 32),
         "32-bit item index can wrap: items %lld, block %u", (long long)p.items, p.block);
-  CHECK(p.block == (p.items > kOneRoundLanes ? uint32_t(kBlockMulti) : uint32_t(kBlock)),
-        "workgroup of %u lanes for %lld items", p.block, (long long)p.items);
+  {
+    // the largest power-of-two workgroup (1024 down to 64) that gives each CU one, or 512
+    // lanes past one round of resident lanes
+    uint32_t want = 1024;
+    while (want > 64 && uint64_t(p.items) < 256ull * want) want /= 2;
+    if (p.items > int64_t(256) * 2048) want = 512;
+    CHECK(p.block == want, "workgroup of %u lanes for %lld items, want %u", p.block,
+          (long long)p.items, want);
+  }
   CHECK(NHL == 1 || (Nc == 1 && N % NHL == 0), "heads per lane %lld with Nc %lld N %lld",
         (long long)NHL, (long long)Nc, (long long)N);
   CHECK(uint64_t(p.items) * NHL * NH * V == uint64_t(B * S * N * L),
