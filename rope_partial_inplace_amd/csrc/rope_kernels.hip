@@ -865,9 +865,16 @@ template <typename XT, typename CT, bool BWD, bool HALF, bool XCH>
 const void *pick_inplace_vec(const InplacePlan &p) {
 #define ROPE_K1(NHL, CNT) \
   reinterpret_cast<const void *>(&inplace_rope_kernel<XT, CT, true, NHL, CNT, BWD, HALF, XCH>)
+  // Only the heads-per-lane counts a plan can choose are built: a lane's x bytes stay at 32
+  // or less (x bytes per head: V elements, twice that when a lane owns both halves).
+  constexpr int kV = 16 / int(sizeof(XT) > sizeof(CT) ? sizeof(XT) : sizeof(CT));
+  constexpr int kXBytes = kV * int(sizeof(XT)) * (HALF && !XCH ? 2 : 1);
   if (p.nhl == 1) return p.cos_stream ? ROPE_K1(1, true) : ROPE_K1(1, false);
-  if (p.nhl == 2) return p.cos_stream ? ROPE_K1(2, true) : ROPE_K1(2, false);
-  return p.cos_stream ? ROPE_K1(4, true) : ROPE_K1(4, false);
+  if constexpr (2 * kXBytes <= 32)
+    if (p.nhl == 2) return p.cos_stream ? ROPE_K1(2, true) : ROPE_K1(2, false);
+  if constexpr (4 * kXBytes <= 32)
+    if (p.nhl == 4) return p.cos_stream ? ROPE_K1(4, true) : ROPE_K1(4, false);
+  return nullptr;  // no plan asks for this (the host plan check covers every plan shape)
 #undef ROPE_K1
 }
 
@@ -934,6 +941,10 @@ int run_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor 
                                          : pick_inplace_dtype<false, true>(plan))
                             : (backward ? pick_inplace_dtype<true, false>(plan)
                                         : pick_inplace_dtype<false, false>(plan));
+  if (fn == nullptr) {
+    g_last_error = "internal: no kernel for this plan";
+    return ROPE_ERR_RUNTIME;
+  }
   return launch(fn, (plan.items + plan.block - 1) / plan.block, int(plan.block), 0, stream, &plan);
 }
 

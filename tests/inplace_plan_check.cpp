@@ -119,6 +119,9 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
     CHECK(p.block == want, "workgroup of %u lanes for %lld items, want %u", p.block,
           (long long)p.items, want);
   }
+  CHECK(NHL == 1 || (p.vector_io && NHL * NH * V * esize(xdt) <= 32),
+        "heads per lane %lld with %lld x bytes per head: no kernel is built for it",
+        (long long)NHL, (long long)(NH * V * esize(xdt)));
   CHECK(NHL == 1 || (Nc == 1 && N % NHL == 0), "heads per lane %lld with Nc %lld N %lld",
         (long long)NHL, (long long)Nc, (long long)N);
   CHECK(uint64_t(p.items) * NHL * NH * V == uint64_t(B * S * N * L),
