@@ -250,6 +250,29 @@ def test_cache_configs_full(cfg):
     compare_cache_case(case, qo, ko)
 
 
+@pytest.mark.parametrize("mrope", [False, True], ids=["rope", "mrope"])
+@pytest.mark.parametrize("neox", [True, False], ids=["neox", "gptj"])
+@pytest.mark.parametrize("dt", [torch.float32, torch.float16, torch.bfloat16],
+                         ids=lambda d: str(d).split(".")[-1])
+def test_cache_long_launch_many_tiles(dt, neox, mrope):
+    """Launches of several rounds of workgroups (4000 to 12288 tiles, tapered end included):
+    12288 tokens, 8 + 8 heads of 128, q rows padded by 64 elements, rope or mrope [16,24,24]
+    positions, every dtype and both styles."""
+    T, nq, nk, H = 12288, 8, 8, 128
+    rd = 128 if (neox or mrope) else 64
+    sec = [16, 24, 24] if mrope else None
+    g = W.generator(4100 + int(neox) + 2 * int(mrope), DEV)
+    qbig = W.randn((T, nq * H + 64), dt, g)
+    q = qbig[:, :nq * H]
+    k = W.randn((T, nk * H), dt, g)
+    cache = W.randn((4096, rd), dt, g)
+    pos = torch.randint(0, 4096, (3, T) if mrope else (T,), generator=g, device=DEV)
+    qo, ko = ra.rope_with_cos_sin_cache(pos, q, k, cache, sec, H, neox)
+    torch.cuda.synchronize()
+    compare_cache(pos.cpu(), q.cpu(), k.cpu(), cache.cpu(), sec, H, neox, qo.cpu(), ko.cpu(),
+                  f"long launch {dt} neox={neox} mrope={mrope}")
+
+
 def test_cache_config_c4_sampled_tokens():
     """The 1 GiB GPT-J workload: every token's pass-through half is checked on the GPU; the
     rotated half is compared with the oracle on 4096 seeded sample tokens."""
