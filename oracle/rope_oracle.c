@@ -258,8 +258,10 @@ static int beyond_limits(const oro_tensor *t) {
   return 0;
 }
 
-/* Row-major contiguity; the stride of a dimension of size 1 does not matter. */
+/* Row-major contiguity; the stride of a dimension of size 1 does not matter, and a tensor
+ * with no elements has no layout to check (reading R12: an empty xRef is a no-op). */
 static int contiguous(const oro_tensor *t) {
+  if (numel(t) == 0) return 1;
   int64_t expect = 1;
   for (int d = t->ndim - 1; d >= 0; --d) {
     if (t->shape[d] != 1 && t->stride[d] != expect) return 0;

@@ -62,7 +62,10 @@ bool addressable(const rope_tensor *t) {
   return true;
 }
 
+// Row-major contiguity; a dimension of size 1 may have any stride, and a view with no
+// elements has no layout to check (reading R12: an empty x is a successful no-op).
 bool row_major(const rope_tensor *t) {
+  if (count(t) == 0) return true;
   int64_t want = 1;
   for (int d = t->ndim - 1; d >= 0; --d) {
     if (t->shape[d] > 1 && t->stride[d] != want) return false;

@@ -170,6 +170,10 @@ INPLACE_CASES = [
     ("empty slice ignores cos last dim", lambda b: (b[0], b[1], b[2], 1, [6, 6]), 0),
     ("empty x", lambda b: (dict(b[0], shape=[0, 3, 2, 16]), dict(b[1], shape=[1, 3, 1, 8]),
                            dict(b[2], shape=[1, 3, 1, 8]), 1, [0, 8]), 0),
+    # an empty view keeps the strides torch gives it ([2,0,2,16]: 0 rows in the middle)
+    ("empty x, zero middle dim", lambda b: (dict(b[0], shape=[2, 0, 2, 16], stride=[32, 32, 16, 1]),
+                                            dict(b[1], shape=[1, 1, 1, 8]),
+                                            dict(b[2], shape=[1, 1, 1, 8]), 1, [0, 8]), 0),
 ]
 
 
