@@ -124,6 +124,17 @@ def cache_case(rng):
         ko["data"] += BUF_BYTES // 2               # clear of anything else in buffer 0
     if rng.random() < 0.04:
         qo = dict(q)                               # queryOut aliasing queryIn exactly: allowed
+    r = rng.random()
+    if r < 0.03:
+        k["stride"][1] = 2                         # inner stride 2: refused
+    elif r < 0.06:
+        k["stride"][0] = -k["stride"][0]           # negative row stride: refused
+    elif r < 0.09:
+        pos["stride"][0] = -1                      # negative positions stride: refused
+    elif r < 0.12:
+        qo["stride"][0] = qo["stride"][0] + align  # padded output rows: refused
+    elif r < 0.2:
+        cache["stride"][0] = cache["stride"][0] + align  # padded cache rows: allowed
     cache_mode = pick(rng, [None, None, 0, 1, 2])
     return dict(pos=pos, q=q, k=k, cache=cache, qo=qo, ko=ko, msec=msec, H=H,
                 neox=int(rng.integers(0, 2)), cache_mode=cache_mode)
@@ -155,7 +166,7 @@ def test_inplace_validation_agrees(block):
 def test_cache_validation_agrees(block):
     rng = np.random.default_rng(6000 + block)
     counts = {}
-    for i in range(400):
+    for i in range(600):
         a = cache_case(rng)
         arr, n = ints(a["msec"])
         if a["msec"] is not None and rng.random() < 0.03:
