@@ -640,7 +640,7 @@ static int cos_sin_cache(const oro_tensor *positions, const oro_tensor *query_in
   if (half > 4096) return fail(ORO_ERR_PARAM_INVALID, "oracle limit: rotaryDim above 8192");
 
   for (int64_t t = 0; t < T; ++t) {
-    /* steps 1-2: gather the cache row(s) and split into cos | sin; mrope stitches the
+    /* gather the cache row(s) and split into cos | sin; mrope stitches the
      * sections: element i of cos/sin comes from the position row whose section holds i */
     for (int64_t i = 0; i < half; ++i) {
       int64_t row_sel = 0;
@@ -664,7 +664,7 @@ static int cos_sin_cache(const oro_tensor *positions, const oro_tensor *query_in
       cs_cos[i] = load_f32(cache, p * cache->stride[0] + i);
       cs_sin[i] = load_f32(cache, p * cache->stride[0] + half + i);
     }
-    /* step 3: every query head, then every key head */
+    /* rotate: every query head, then every key head */
     for (int which = 0; which < 2; ++which) {
       const oro_tensor *in = which == 0 ? query_in : key_in;
       const oro_tensor *out = which == 0 ? query_out : key_out;

@@ -515,10 +515,10 @@ __global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
 // A workgroup owns a tile of tokens.  Stage: its lanes gather each token's cos|sin row from
 // the cache (mrope: element i from the position row that the stitching assigns it) and keep
 // it in LDS in the cache's own element type (raised to float32 at use), so it is read from
-// HBM once per token and reused by every q/k head.  Then lanes walk (token, head, unit) items.  NeoX: a unit is two V-element vectors,
-// u and u + rd/(2V) of the rotated part (its pairs lie across the halves), or the same
-// two-vector shape over [rd, H) copied as raw bits.  GPT-J: a unit is one vector (its pairs
-// lie inside it), rotated below rd and copied above.  The units of one head are adjacent
+// HBM once per token and reused by every q/k head.  Then lanes walk (token, head, unit)
+// items.  NeoX: a unit is two V-element vectors, u and u + rd/(2V) of the rotated part (its
+// pairs lie across the halves), or the same two-vector shape over [rd, H) copied as raw bits.
+// GPT-J: a unit is one vector (its pairs lie inside it), rotated below rd and copied above.  The units of one head are adjacent
 // lanes, so each wavefront load/store covers whole runs of 128-byte lines.  q/k are
 // streamed (non-temporal loads and stores); the first pass's loads are issued before the LDS
 // staging so that their latency overlaps the position -> cache gather.
@@ -795,7 +795,7 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
     CacheItems<T, V, VEC, K, NV> w;
     cache_load_pass<T, NEOX, V, VEC, K, NV>(p, t0, tile_items, 0, w);
 
-    // ---- stage the tile's cos|sin rows in LDS (steps 1-2: gather, split, stitch) ----
+    // ---- stage the tile's cos|sin rows in LDS: gather, split, stitch ----
     // One lane per V-element chunk of a token's cos half (and the matching sin chunk).  A
     // chunk drawn from one position row (always, in rope mode) is copied as 16-byte vectors;
     // chunks of a multi-row plan go through stage_multi_row.  An unaligned cache is gathered
@@ -833,7 +833,7 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
     }
     __syncthreads();
 
-    // ---- step 3: rotate the first rd of every q head then k head, copy the rest ----
+    // ---- rotate the first rd of every q head then k head, copy the rest ----
     for (uint32_t pbase = 0;;) {
       cache_store_pass<T, NEOX, V, VEC, K, NV>(p, t0, cs_tile, w);
       pbase += pass;
