@@ -701,60 +701,6 @@ __device__ inline void multi_rows(const CachePlan &p, uint32_t i0, int *row) {
   }
 }
 
-// Positions of rows 0..2 for the chunk.  A row the chunk does not use reads the position of
-// the chunk's first element's row instead, so its cache loads below hit the lines that row
-// brings in rather than fetching another cache row.  Every load is unconditional: loads
-// under divergent branches make the compiler wait for all outstanding loads at each join.
-template <int V>
-__device__ inline void multi_positions(const CachePlan &p, int64_t tok, uint32_t i0,
-                                       int64_t *pos) {
-  int row[V];
-  multi_rows<V>(p, i0, row);
-  bool need[3] = {false, false, false};
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    need[0] |= row[j] == 0;
-    need[1] |= row[j] == 1;
-    need[2] |= row[j] == 2;
-  }
-#pragma unroll
-  for (int r = 0; r < 3; ++r)
-    pos[r] = p.positions[(need[r] ? r : row[0]) * p.pos_stride_row + tok];
-}
-
-// Stages one V-element chunk (elements i0 .. i0+V-1 of the cos half, and the same of the sin
-// half) of a token whose stitched cos/sin draws on several position rows (interleaved
-// stitching, or a section boundary inside the chunk; three rows at most): the chunk of each
-// row is loaded as whole 16-byte vectors, then each element is taken from its row.  `pos`
-// holds the positions from multi_positions for the same chunk.
-template <typename T, int V>
-__device__ inline void stage_multi_row(const CachePlan &p, const int64_t *pos, uint32_t i0,
-                                       int64_t half, T *dst) {
-  using R = typename Io<T>::raw;
-  union Chunk {
-    u32x4 v;
-    R e[V];
-  };
-  int row[V];
-  multi_rows<V>(p, i0, row);
-  Chunk c[3], s[3];
-#pragma unroll
-  for (int r = 0; r < 3; ++r) {
-    const T *src = static_cast<const T *>(p.cache) + clamp_position(p, pos[r]) * p.cache_stride + i0;
-    c[r].v = ld16<false>(src);
-    s[r].v = ld16<false>(src + half);
-  }
-  Chunk co, so;
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const int r = row[j];
-    co.e[j] = r == 0 ? c[0].e[j] : r == 1 ? c[1].e[j] : c[2].e[j];
-    so.e[j] = r == 0 ? s[0].e[j] : r == 1 ? s[1].e[j] : s[2].e[j];
-  }
-  *reinterpret_cast<u32x4 *>(dst) = co.v;
-  *reinterpret_cast<u32x4 *>(dst + half) = so.v;
-}
-
 // MULTI: the plan's stitched cos/sin has chunks drawing on several position rows
 // (CachePlan::multi_row); otherwise every staging chunk comes from one row.
 template <typename T, bool NEOX, bool VEC, int K, bool MULTI>
@@ -796,12 +742,52 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
     cache_load_pass<T, NEOX, V, VEC, K, NV>(p, t0, tile_items, 0, w);
 
     // ---- stage the tile's cos|sin rows in LDS: gather, split, stitch ----
-    // One lane per V-element chunk of a token's cos half (and the matching sin chunk).  A
-    // chunk drawn from one position row (always, in rope mode) is copied as 16-byte vectors;
-    // chunks of a multi-row plan go through stage_multi_row.  An unaligned cache is gathered
-    // element by element.  Values stay in the cache's element type (bits copied, raised to
-    // float32 at use).
-    for (uint32_t idx = threadIdx.x; idx < stage_items; idx += kCacheBlock) {
+    // Values stay in the cache's element type (bits copied, raised to float32 at use).
+    // Chunks that draw on several position rows (MULTI, 16-byte cache rows): one lane per
+    // (chunk, row).  It loads its row's position and 16-byte cos and sin chunks, and writes
+    // the elements that the stitching assigns to that row.  A row the chunk does not use
+    // loads the row of the chunk's first element instead (lines already being fetched) and
+    // writes nothing.  Loads are unconditional: loads under divergent branches make the
+    // compiler wait for every outstanding load at each join.
+    bool staged = false;
+    if constexpr (MULTI) {
+      if (p.cache_vec) {
+        staged = true;
+        using R = typename Io<T>::raw;
+        for (uint32_t idx = threadIdx.x; idx < stage_items * 3u; idx += kCacheBlock) {
+          const uint32_t chunk = idx / 3u, row = idx - chunk * 3u;
+          const uint32_t tl = fdiv(p.div_stage, chunk);
+          const uint32_t i0 = (chunk - tl * p.stage_chunks) * uint32_t(V);
+          int rows[V];
+          multi_rows<V>(p, i0, rows);
+          bool used = false;
+#pragma unroll
+          for (int j = 0; j < V; ++j) used |= rows[j] == int(row);
+          const int64_t rsel = used ? int64_t(row) : int64_t(rows[0]);
+          const int64_t pos = p.positions[rsel * p.pos_stride_row + (t0 + tl) * p.pos_stride_tok];
+          const T *src =
+              static_cast<const T *>(p.cache) + clamp_position(p, pos) * p.cache_stride + i0;
+          union Chunk {
+            u32x4 v;
+            R e[V];
+          };
+          Chunk c, sn;
+          c.v = ld16<false>(src);
+          sn.v = ld16<false>(src + half);
+          R *dst = reinterpret_cast<R *>(cs_tile + int64_t(tl) * rd + i0);
+#pragma unroll
+          for (int j = 0; j < V; ++j)
+            if (rows[j] == int(row)) {
+              dst[j] = c.e[j];
+              dst[half + j] = sn.e[j];
+            }
+        }
+      }
+    }
+    // Otherwise one lane per V-element chunk of a token's cos half (and the matching sin
+    // chunk): a chunk drawn from one position row (always, in rope mode) is copied as 16-byte
+    // vectors; an unaligned cache is gathered element by element.
+    for (uint32_t idx = threadIdx.x; !staged && idx < stage_items; idx += kCacheBlock) {
       const uint32_t tl = fdiv(p.div_stage, idx);
       const uint32_t i0 = (idx - tl * p.stage_chunks) * uint32_t(V);
       const int64_t tok = (t0 + tl) * p.pos_stride_tok;
@@ -817,10 +803,6 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
           reinterpret_cast<R *>(dst)[j] = src[0];
           reinterpret_cast<R *>(dst + half)[j] = src[half];
         }
-      } else if constexpr (MULTI) {
-        int64_t pos[3];
-        multi_positions<V>(p, tok, i0, pos);
-        stage_multi_row<T, V>(p, pos, i0, half, dst);
       } else {
         const int sec = p.mrope ? mrope_section_of(p, i0) : 0;
         const int64_t pos =

@@ -8,10 +8,11 @@
 //   - the rotated part of each unit reads the cos|sin elements of its own pair indices;
 //   - every token belongs to exactly one tile (tiles of tile_tokens, then one-token tiles),
 //     and a launch of at most one round of workgroups (256 CUs x 7) has one-token tiles only;
-//   - the staging chunks of a tile write each of its tile_tokens * rotaryDim LDS elements once,
+//   - the staging lanes of a tile write each of its tile_tokens * rotaryDim LDS elements once,
 //     inside the LDS size the launch requests, and each element's position row is the one the
 //     stitching assigns (sections for cacheMode 0, the i mod 3 rule below 3 * mropeSection[1]
-//     for cacheMode 1), with one row per chunk unless the plan takes the multi-row path.
+//     for cacheMode 1), with one row per chunk unless the plan takes the multi-row path (one
+//     lane per chunk and row, writing that row's elements).
 // Shapes cover every dtype, both styles, rope mode, every whitelisted mropeSection and both
 // cacheModes, pass-through parts, token counts that leave a ragged last tile, reach the
 // one-token tiles of the tapered end or sit either side of one round of workgroups, and
@@ -124,13 +125,18 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
       CHECK(tok_seen[size_t(t)] == 0, "token %lld in two tiles", (long long)t);
       tok_seen[size_t(t)] = 1;
     }
-    // staging
+    // staging: one lane per chunk, or for multi-row plans (16-byte cache rows) one lane per
+    // (chunk, row of rows 0..2) writing only the elements assigned to its row
     std::vector<uint8_t> lds(size_t(lds_elems), 0);
     const uint32_t stage_items = uint32_t(ntok) * p.stage_chunks;
-    for (uint32_t idx = 0; idx < stage_items; ++idx) {
-      const uint32_t tl = fastdiv_host(p.div_stage, idx);
-      const int64_t i0 = int64_t(idx - tl * p.stage_chunks) * V;
-      CHECK(tl < uint32_t(ntok) && i0 + V <= half, "staging chunk %u", idx);
+    const bool per_row = p.multi_row && p.cache_vec;
+    CHECK(!p.multi_row || m == 3, "multi-row plan with %lld position rows", (long long)m);
+    for (uint32_t idx = 0; idx < stage_items * (per_row ? 3u : 1u); ++idx) {
+      const uint32_t chunk = per_row ? idx / 3u : idx;
+      const int lane_row = per_row ? int(idx % 3u) : -1;
+      const uint32_t tl = fastdiv_host(p.div_stage, chunk);
+      const int64_t i0 = int64_t(chunk - tl * p.stage_chunks) * V;
+      CHECK(tl < uint32_t(ntok) && i0 + V <= half, "staging chunk %u", chunk);
       int first_row = assigned_row(sec, cache_mode, i0);
       for (int64_t e = 0; e < V; ++e) {
         const int r = assigned_row(sec, cache_mode, i0 + e);
@@ -138,6 +144,7 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
         CHECK(p.multi_row || r == first_row,
               "chunk at %lld mixes rows %d and %d without the multi-row path", (long long)i0,
               first_row, r);
+        if (per_row && r != lane_row) continue;
         for (int64_t h2 : {int64_t(0), half}) {
           const int64_t li = int64_t(tl) * rd + h2 + i0 + e;
           CHECK(li < lds_elems, "LDS index %lld beyond %lld", (long long)li,
