@@ -177,6 +177,47 @@ def test_inplace_canaries_and_specials(dt):
     check_inplace(before, x, c, s, [8, 40], f"specials {dt}")
 
 
+# Scales that put N(0,1) values into each dtype's subnormal range (below 2^-126 for f32 and
+# bf16, below 2^-14 for f16), so inputs and products are subnormal.  There the f32 rounding
+# error is absolute, so the relative f32 bound does not apply; instead the GPU result must
+# equal the oracle's float32 result bit for bit (same operations in the same order, IEEE
+# subnormals on both sides): a kernel that flushed subnormals to zero would differ.
+SUBNORMAL_SCALE = {torch.float32: 2.0 ** -130, torch.bfloat16: 2.0 ** -130,
+                   torch.float16: 2.0 ** -17}
+
+
+@pytest.mark.parametrize("xdt,cdt", DTYPE_PAIRS, ids=lambda d: str(d).split(".")[-1])
+def test_inplace_subnormal_inputs(xdt, cdt):
+    B, S, N, D = 2, 40, 3, 64
+    g = W.generator(21, DEV)
+    x = (W.randn((B, S, N, D), torch.float32, g) * SUBNORMAL_SCALE[xdt]).to(xdt)
+    c = W.randn((B, S, 1, 48), cdt, g)
+    s = W.randn((B, S, 1, 48), cdt, g)
+    assert (x.float().abs() < 2.0 ** -14).all() and (x != 0).any()
+    ref = x.cpu()
+    assert oracle.rope_partial_inplace(ref, c.cpu(), s.cpu(), 1, [16, 64])[0] == 0
+    ra.rope_partial_inplace(x, c, s, 1, [16, 64])
+    torch.cuda.synchronize()
+    check_bits_equal(x.cpu(), ref, f"subnormal x {xdt}/{cdt}")
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.float16, torch.bfloat16],
+                         ids=lambda d: str(d).split(".")[-1])
+def test_cache_subnormal_inputs(dt):
+    T, nq, nk, H = 33, 3, 2, 128
+    g = W.generator(22, DEV)
+    q = (W.randn((T, nq * H), torch.float32, g) * SUBNORMAL_SCALE[dt]).to(dt)
+    k = (W.randn((T, nk * H), torch.float32, g) * SUBNORMAL_SCALE[dt]).to(dt)
+    cache = W.randn((64, 128), dt, g)
+    pos = torch.randint(0, 64, (T,), generator=g, device=DEV)
+    for neox in (True, False):
+        qo, ko = ra.rope_with_cos_sin_cache(pos, q, k, cache, None, H, neox)
+        torch.cuda.synchronize()
+        rq, rk, _, _ = oracle_cache(pos.cpu(), q.cpu(), k.cpu(), cache.cpu(), None, H, neox)
+        check_bits_equal(qo.cpu(), rq, f"subnormal q {dt} neox={neox}")
+        check_bits_equal(ko.cpu(), rk, f"subnormal k {dt} neox={neox}")
+
+
 def test_inplace_deterministic_and_stream():
     case = W.inplace_bf16_slice(DEV)
     x1 = case.x.clone()
