@@ -218,6 +218,33 @@ def test_cache_subnormal_inputs(dt):
         check_bits_equal(ko.cpu(), rk, f"subnormal k {dt} neox={neox}")
 
 
+@pytest.mark.parametrize("cfg", ["inplace_bf16_8x4096x1x576_s512", "inplace_f32_1x16x2x64",
+                                 "inplace_half_bf16_8x4096x1x576_s512",
+                                 "inplace_heads_bf16_4x2048x32x192_s128_bs1d",
+                                 "cache_rope_neox_bf16_t8192", "cache_mrope_neox_bf16_t16384",
+                                 "cache_mrope_interleaved_neox_bf16_t16384"])
+def test_configs_bit_identical_to_oracle(cfg):
+    """Beyond the tolerances: the kernels perform the oracle's float32 operations in the
+    oracle's order, with one rounding to the storage type, so every output element equals
+    the oracle's bit for bit (NaN-free inputs)."""
+    case = W.CONFIGS[cfg](DEV)
+    if hasattr(case, "x"):
+        ref = case.x.cpu()
+        assert oracle.rope_partial_inplace(ref, case.cos.cpu(), case.sin.cpu(), case.rotary_mode,
+                                           case.partial_slice)[0] == 0
+        ra.rope_partial_inplace(case.x, case.cos, case.sin, case.rotary_mode,
+                                case.partial_slice)
+        torch.cuda.synchronize()
+        check_bits_equal(case.x.cpu(), ref, cfg)
+    else:
+        qo, ko = run_cache_case(case)
+        rq, rk, _, _ = oracle_cache(case.positions.cpu(), case.query.cpu(), case.key.cpu(),
+                                    case.cache.cpu(), case.mrope_section, case.head_size,
+                                    case.is_neox, case.cache_mode)
+        check_bits_equal(qo.cpu(), rq, cfg + " q")
+        check_bits_equal(ko.cpu(), rk, cfg + " k")
+
+
 def test_inplace_deterministic_and_stream():
     case = W.inplace_bf16_slice(DEV)
     x1 = case.x.clone()
