@@ -53,7 +53,7 @@ class RopeError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m rope_partial_inplace_amd.build`")
+            f"{LIB_PATH} is missing: build it with `python __graft_entry__.py` at the repository root")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     lib.rope_partial_inplace.argtypes = [P(RopeTensor), P(RopeTensor), P(RopeTensor),

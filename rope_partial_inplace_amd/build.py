@@ -1,6 +1,6 @@
 """Build librope_amd.so in-tree for gfx950 (MI355X).
 
-``python -m rope_partial_inplace_amd.build`` or ``build()``.  hipcc cross-compiles without
+``python rope_partial_inplace_amd/build.py`` or ``build()``.  hipcc cross-compiles without
 a GPU.  Code object version 5 is emitted so that the kernels load under the HIP runtime the
 process already uses (PyTorch ships its own, older than this compiler).  Device code is
 compiled with: no fused multiply-add contraction (the formulas are
