@@ -826,6 +826,158 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
   }
 }
 
+// ============================================================================================
+// K2, wavefront form (the plans it covers: 16-byte q/k and cache access, at most 64 units per
+// head).  The same operation as cos_sin_cache_kernel, with one wavefront per (token, group of
+// heads) and no LDS and no barrier.  Lane l owns unit u = l % units of head l / units in each
+// of kWaveItemsPerLane rows of wave_hpw heads, so its cos|sin chunk (NeoX: the V elements
+// u*V...; GPT-J: the V/2 pair indices u*V/2...) is the same for all of its items and is read
+// straight from the token's cache row; the lanes of one unit read the same bytes, which the
+// caches serve.  The token's positions are wave-uniform and are read through the scalar
+// cache, so waiting for them does not wait for the q/k loads issued after them.
+// ============================================================================================
+typedef const __attribute__((address_space(4))) int64_t const_i64;
+
+// The lane's cos (or sin) chunk as raw elements of T.
+template <typename T, int CB>
+union CsChunk {
+  Words<CB> w;
+  typename Io<T>::raw e[CB / int(sizeof(T))];
+};
+
+template <typename T, bool NEOX, bool MULTI>
+__global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePlan p) {
+  constexpr int V = Io<T>::kPer16;
+  constexpr int NV = NEOX ? 2 : 1;   // vectors per unit
+  constexpr int K = kWaveItemsPerLane;
+  constexpr int C = NEOX ? V : V / 2;  // cos (and sin) elements of the lane's chunk
+  constexpr int CB = C * int(sizeof(T));  // 16 bytes (NeoX) or 8 (GPT-J)
+  constexpr int PW = Io<T>::kPerWord;
+  const uint32_t lane = __lane_id();
+  const uint32_t hsub = lane / p.units;
+  const uint32_t u = lane - hsub * p.units;
+  const bool lane_on = hsub < p.wave_hpw;  // lanes past the last whole head are idle
+  const uint32_t hs = lane_on ? hsub : 0;   // (idle lanes load like the first head row)
+  const bool rot = u < p.rot_units;
+  const int64_t rd = p.rd, half = rd / 2, nh = p.nq + p.nk;
+  const int64_t i0 = int64_t(rot ? u : 0) * C;  // first cos element of the lane's chunk
+  // element offsets of the lane's vectors inside a head, the same for each of its items
+  int64_t off_a, off_b = 0;
+  if constexpr (NEOX) {
+    if (rot) {
+      off_a = int64_t(u) * V;
+      off_b = half + int64_t(u) * V;
+    } else {
+      const int64_t w = int64_t(u - p.rot_units) * V;
+      off_a = rd + w;
+      off_b = rd + (p.H - rd) / 2 + w;
+    }
+  } else {
+    off_a = int64_t(u) * V;
+  }
+  int rows[C];  // MULTI: the position row of each element of the chunk
+  int sec = 0;  // otherwise: the one row of the whole chunk
+  if constexpr (MULTI) multi_rows<C>(p, uint32_t(i0), rows);
+  else if (p.mrope) sec = mrope_section_of(p, i0);
+  const_i64 *pos_s = reinterpret_cast<const_i64 *>(reinterpret_cast<uintptr_t>(p.positions));
+  const int nrows = p.mrope ? p.nsec : 1;
+  constexpr uint32_t kWpb = kWaveBlock / 64;
+  for (uint32_t gw = __builtin_amdgcn_readfirstlane(blockIdx.x * kWpb + threadIdx.x / 64);
+       gw < uint32_t(p.waves); gw += gridDim.x * kWpb) {
+    const uint32_t t32 = fdiv(p.div_wpt, gw);
+    const int64_t t = t32;
+    const int64_t hbase = int64_t(gw - t32 * p.wave_wpt) * p.wave_heads + hs;
+    // the token's position rows (wave-uniform scalar loads), issued first
+    int64_t prow[4];
+    prow[0] = pos_s[t * p.pos_stride_tok];
+#pragma unroll
+    for (int r = 1; r < 4; ++r)
+      prow[r] = r < nrows ? pos_s[r * p.pos_stride_row + t * p.pos_stride_tok] : prow[0];
+    // q/k loads of every item (a lane past the last head loads the last head again and
+    // stores nothing)
+    RawN<T, V, true> v[K][NV];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      int64_t h = hbase + int64_t(k) * p.wave_hpw;
+      h = h < nh ? h : nh - 1;
+      const bool is_q = h < p.nq;
+      const int64_t in_row = t * (is_q ? p.q_stride : p.k_stride) + (is_q ? h : h - p.nq) * p.H;
+      const void *in = is_q ? p.q_in : p.k_in;
+      load_raw<T, V, true, true>(in, in_row + off_a, v[k][0]);
+      if constexpr (NV == 2) load_raw<T, V, true, true>(in, in_row + off_b, v[k][NV - 1]);
+    }
+    // the lane's cos and sin chunks: gather, split, stitch
+    CsChunk<T, CB> cw, sw;
+    if constexpr (MULTI) {
+      CsChunk<T, CB> cr[3], sr[3];
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        const T *row = static_cast<const T *>(p.cache) + clamp_position(p, prow[r]) * p.cache_stride;
+        load_words<CB, false>(row + i0, cr[r].w);
+        load_words<CB, false>(row + half + i0, sr[r].w);
+      }
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        cw.e[j] = rows[j] == 0 ? cr[0].e[j] : rows[j] == 1 ? cr[1].e[j] : cr[2].e[j];
+        sw.e[j] = rows[j] == 0 ? sr[0].e[j] : rows[j] == 1 ? sr[1].e[j] : sr[2].e[j];
+      }
+    } else {
+      const int64_t pos = sec == 0 ? prow[0] : sec == 1 ? prow[1] : sec == 2 ? prow[2] : prow[3];
+      const T *row = static_cast<const T *>(p.cache) + clamp_position(p, pos) * p.cache_stride;
+      load_words<CB, false>(row + i0, cw.w);
+      load_words<CB, false>(row + half + i0, sw.w);
+    }
+    // rotate the first rd of every head, copy the rest as raw bits
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t h = hbase + int64_t(k) * p.wave_hpw;
+      if (!lane_on || h >= nh) continue;
+      const bool is_q = h < p.nq;
+      const int64_t out_row = t * ((is_q ? p.nq : p.nk) * p.H) + (is_q ? h : h - p.nq) * p.H;
+      void *out = is_q ? p.q_out : p.k_out;
+      if (!rot) {
+        store_raw<T, V, true, true>(out, out_row + off_a, v[k][0]);
+        if constexpr (NV == 2) store_raw<T, V, true, true>(out, out_row + off_b, v[k][NV - 1]);
+        continue;
+      }
+      if constexpr (NEOX) {
+        // [RSCC §rotate_half（GPT-NeoX style）旋转模式]: x1 = a (first half), x2 = b
+        RawN<T, V, true> oa, ob;
+#pragma unroll
+        for (int q = 0; q < V / PW; ++q) {
+          float a[PW], b[PW], ya[PW], yb[PW], cv[PW], sv[PW];
+          raw_word_to_float<T, V, true>(v[k][0], q, a);
+          raw_word_to_float<T, V, true>(v[k][NV - 1], q, b);
+          Io<T>::word_to_floats(cw.w.w[q], cv);
+          Io<T>::word_to_floats(sw.w.w[q], sv);
+#pragma unroll
+          for (int e = 0; e < PW; ++e) {
+            ya[e] = a[e] * cv[e] - b[e] * sv[e];
+            yb[e] = b[e] * cv[e] + a[e] * sv[e];
+          }
+          float_to_raw_word<T, V, true>(ya, q, oa);
+          float_to_raw_word<T, V, true>(yb, q, ob);
+        }
+        store_raw<T, V, true, true>(out, out_row + off_a, oa);
+        store_raw<T, V, true, true>(out, out_row + off_b, ob);
+      } else {
+        // [RSCC §rotate_interleaved（GPT-J style）旋转模式]: pairs (x[2m], x[2m+1]) inside the
+        // vector, with cos/sin entry m of the lane's chunk
+        float a[V], ya[V], cv[C], sv[C];
+        raw_to_float<T, V, true>(v[k][0], a);
+        words_to_floats<T, C>(cw.w, cv);
+        words_to_floats<T, C>(sw.w, sv);
+#pragma unroll
+        for (int m = 0; m < C; ++m) {
+          ya[2 * m] = a[2 * m] * cv[m] - a[2 * m + 1] * sv[m];
+          ya[2 * m + 1] = a[2 * m + 1] * cv[m] + a[2 * m] * sv[m];
+        }
+        store_n<T, V, true, true>(out, out_row + off_a, ya);
+      }
+    }
+  }
+}
+
 // ---- launch helpers -------------------------------------------------------------------------
 
 
@@ -892,6 +1044,12 @@ const void *pick_cache_rows(bool neox, bool vec) {
 
 template <typename T>
 const void *pick_cache(const CachePlan &p) {
+  if (p.wave) {
+#define ROPE_K2W(NX, MU) reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, MU>)
+    if (p.neox) return p.multi_row ? ROPE_K2W(true, true) : ROPE_K2W(true, false);
+    return p.multi_row ? ROPE_K2W(false, true) : ROPE_K2W(false, false);
+#undef ROPE_K2W
+  }
   return p.multi_row ? pick_cache_rows<T, true>(p.neox, p.vector_io)
                      : pick_cache_rows<T, false>(p.neox, p.vector_io);
 }
@@ -967,6 +1125,9 @@ ROPE_API int rope_with_cos_sin_cache_v2(const rope_tensor *positions, const rope
   const void *fn = plan.dt == ROPE_F32   ? pick_cache<float>(plan)
                    : plan.dt == ROPE_F16 ? pick_cache<_Float16>(plan)
                                          : pick_cache<__bf16>(plan);
+  if (plan.wave)
+    return launch(fn, (plan.waves + kWaveBlock / 64 - 1) / (kWaveBlock / 64), kWaveBlock, 0,
+                  stream, &plan);
   const size_t esize = plan.dt == ROPE_F32 ? 4 : 2;
   const size_t lds = size_t(plan.tile_tokens) * size_t(plan.rd) * esize;
   return launch(fn, plan.tiles, kCacheBlock, lds, stream, &plan);

@@ -470,6 +470,23 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
   // list has its boundaries on vector edges and allows cacheMode 0 only).
   if (p.multi_row && nsec != 3)
     return reject(err, ROPE_ERR_PARAM_INVALID, "mropeSection layout not supported");
+  // The wavefront path needs 16-byte q/k and cache access, a head of at most 64 units (one
+  // row of lanes), positions readable as aligned 8-byte words (they go through the scalar
+  // cache), and a wave count that fits its 32-bit index.
+  if (p.vector_io && p.cache_vec && p.units >= 1 && p.units <= 64 &&
+      (reinterpret_cast<uintptr_t>(p.positions) & 7u) == 0) {
+    const uint32_t hpw = 64u / p.units;
+    const uint32_t heads = uint32_t(kWaveItemsPerLane) * hpw;
+    const int64_t wpt = (p.nq + p.nk + heads - 1) / heads;
+    if (wpt <= int64_t(0x7fffffff) && T <= kMaxWaves / wpt) {
+      p.wave = true;
+      p.wave_hpw = hpw;
+      p.wave_heads = heads;
+      p.wave_wpt = uint32_t(wpt);
+      p.waves = T * wpt;
+      p.div_wpt = make_fastdiv(p.wave_wpt);
+    }
+  }
   return ROPE_OK;
 }
 

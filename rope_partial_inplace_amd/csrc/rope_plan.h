@@ -103,6 +103,16 @@ struct CachePlan {
   bool cache_vec = false;       // cache rows can be read with 16-byte loads
   uint32_t stage_chunks = 0;    // (rd/2) / vec: vector chunks of one cos (or sin) half-row
   FastDiv div_units, div_ipt, div_stage;
+  // Wavefront path (cos_sin_cache_wave_kernel): one wavefront per (token, group of heads), no
+  // LDS.  Lane l owns unit l % units of head l / units of each of kWaveItemsPerLane rows of
+  // wave_hpw heads, so its cos|sin chunk is the same for all its items and is read straight
+  // from the cache row.  Lanes from wave_hpw * units up are idle.
+  bool wave = false;
+  uint32_t wave_hpw = 0;        // heads per row of 64 lanes: floor(64 / units)
+  uint32_t wave_heads = 0;      // heads per wavefront: kWaveItemsPerLane * wave_hpw
+  uint32_t wave_wpt = 0;        // wavefronts per token: ceil((nq + nk) / wave_heads)
+  int64_t waves = 0;            // T * wave_wpt (< 2^31)
+  FastDiv div_wpt;
 };
 
 int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor *sin,
@@ -140,5 +150,13 @@ constexpr int kCacheBlock = 256;  // cache kernel workgroup (one token tile)
 constexpr int64_t kTaperTokens = 1280;
 constexpr int kNeoxItemsPerLane = 2;  // NeoX units are two vectors
 constexpr int kGptjItemsPerLane = 2;  // GPT-J units are one vector
+// Wavefront cache kernel: 256-lane workgroups of four independent wavefronts, two items (head
+// rows) per lane.  Measured on the rope NeoX bf16, GPT-J f16 and mrope bf16 workloads against
+// one item per lane (3-30% slower) and three (2-6% slower); 64-lane workgroups were within 1%,
+// 512- and 1024-lane ones up to 8% slower.
+constexpr int kWaveBlock = 256;
+constexpr int kWaveItemsPerLane = 2;
+// Waves of one launch stay below 2^31, so a wave index plus the grid stride fits 32 bits.
+constexpr int64_t kMaxWaves = (int64_t(1) << 31) - (int64_t(1) << 24);
 
 }  // namespace ropeamd

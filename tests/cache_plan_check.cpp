@@ -74,11 +74,122 @@ static int assigned_row(const std::vector<int64_t> &sec, int64_t cache_mode, int
   return -1;
 }
 
+// The wavefront kernel's position row for element j of the chunk starting at cos element i0
+// (3-section plans on the multi-row path), as the kernel computes it, without branches.
+static int wave_multi_row(const CachePlan &p, uint32_t i0, int j) {
+  const uint32_t e = i0 + uint32_t(j);
+  uint32_t m = i0 % 3u + uint32_t(j % 3);
+  m = m >= 3u ? m - 3u : m;
+  const int ri = int32_t(e) < p.interleave_end ? int(m) : 0;
+  const int rs = int(int32_t(e) >= p.sec_end[0]) + int(int32_t(e) >= p.sec_end[1]);
+  return p.interleaved ? ri : rs;
+}
+
+// The wavefront path (plan.wave): waves of 64 lanes, wave gw -> token gw / wave_wpt and head
+// group gw % wave_wpt; lane l -> unit l % units of head row l / units (idle from wave_hpw up);
+// kWaveItemsPerLane head rows of wave_hpw heads.  Checks that every output element is written
+// once from its own input element, that every load (idle and clamped lanes included) stays
+// inside the input rows, that a rotated element reads the cos|sin entry of its own pair, and
+// that the position row of each cos|sin element is the one the stitching assigns.
+static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int64_t nk,
+                       int64_t H, int64_t rd, const std::vector<int64_t> &sec,
+                       int64_t cache_mode, int64_t qs) {
+  const int64_t V = p.vec, half = rd / 2, nh = nq + nk;
+  const int64_t C = neox ? V : V / 2;
+  CHECK(p.units >= 1 && p.units <= 64 && p.wave_hpw == 64 / p.units, "wave plan units %u hpw %u",
+        p.units, p.wave_hpw);
+  CHECK(p.wave_heads == uint32_t(kWaveItemsPerLane) * p.wave_hpw, "wave heads %u", p.wave_heads);
+  CHECK(int64_t(p.wave_wpt) * p.wave_heads >= nh &&
+            int64_t(p.wave_wpt - 1) * p.wave_heads < nh, "waves per token %u", p.wave_wpt);
+  CHECK(p.waves == T * int64_t(p.wave_wpt) && p.waves < kMaxWaves, "waves %lld",
+        (long long)p.waves);
+  std::vector<uint8_t> hq(size_t(T * nq * H), 0), hk(size_t(T * nk * H), 0);
+  for (int64_t gw = 0; gw < p.waves; ++gw) {
+    const uint32_t t32 = fastdiv_host(p.div_wpt, uint32_t(gw));
+    CHECK(t32 == uint32_t(gw / p.wave_wpt), "wave %lld decodes to token %u", (long long)gw, t32);
+    const int64_t t = t32;
+    const int64_t hbase0 = int64_t(uint32_t(gw) - t32 * p.wave_wpt) * p.wave_heads;
+    for (uint32_t lane = 0; lane < 64; ++lane) {
+      const uint32_t hsub = lane / p.units, u = lane - hsub * p.units;
+      const bool on = hsub < p.wave_hpw;
+      const int64_t hbase = hbase0 + (on ? hsub : 0);
+      const bool rot = u < p.rot_units;
+      const int64_t i0 = int64_t(rot ? u : 0) * C;
+      CHECK(i0 + C <= half, "cos chunk [%lld, %lld) beyond rd/2", (long long)i0,
+            (long long)(i0 + C));
+      // rows of the chunk's elements: one row (the section of i0) unless multi-row
+      int first = -1;
+      for (int64_t j = 0; j < C; ++j) {
+        const int want = assigned_row(sec, cache_mode, i0 + j);
+        int got;
+        if (p.multi_row) {
+          got = wave_multi_row(p, uint32_t(i0), int(j));
+        } else if (p.mrope) {
+          got = int(i0 >= p.sec_end[0]) + int(i0 >= p.sec_end[1]) +
+                (p.nsec == 4 ? int(i0 >= p.sec_end[2]) : 0);
+        } else {
+          got = 0;
+        }
+        if (first < 0) first = got;
+        CHECK(got == want, "lane %u element %lld: row %d, stitching assigns %d", lane,
+              (long long)(i0 + j), got, want);
+        CHECK(got < (p.mrope ? p.nsec : 1), "row %d beyond the position rows", got);
+      }
+      std::vector<int64_t> offs;
+      if (neox) {
+        if (rot) {
+          offs = {int64_t(u) * V, half + int64_t(u) * V};
+        } else {
+          const int64_t w = int64_t(u - p.rot_units) * V;
+          offs = {rd + w, rd + (H - rd) / 2 + w};
+        }
+      } else {
+        offs = {int64_t(u) * V};
+      }
+      for (int k = 0; k < kWaveItemsPerLane; ++k) {
+        const int64_t h = hbase + int64_t(k) * p.wave_hpw;
+        const int64_t hl = h < nh ? h : nh - 1;  // the head the loads address
+        const bool lq = hl < nq;
+        const int64_t lrow = t * (lq ? qs : nk * H) + (lq ? hl : hl - nq) * H;
+        for (int64_t o : offs)
+          CHECK(o >= 0 && o + V <= H && lrow + o + V <= T * (lq ? qs : nk * H),
+                "load outside the input rows");
+        if (!on || h >= nh) continue;
+        const bool is_q = h < nq;
+        const int64_t out_row = t * ((is_q ? nq : nk) * H) + (is_q ? h : h - nq) * H;
+        std::vector<uint8_t> &hit = is_q ? hq : hk;
+        for (int64_t o : offs)
+          for (int64_t e = 0; e < V; ++e) {
+            const int64_t col = o + e;
+            CHECK(rot == (col < rd), "column %lld on the wrong side of rotaryDim",
+                  (long long)col);
+            const size_t oi = size_t(out_row + col);
+            CHECK(hit[oi] == 0, "wave output %zu written twice", oi);
+            hit[oi] = 1;
+            if (rot) {
+              const int64_t pair = neox ? (col < half ? col : col - half) : col / 2;
+              const int64_t cs = i0 + (neox ? e : e / 2);
+              CHECK(pair == cs, "column %lld reads cos %lld, wants %lld", (long long)col,
+                    (long long)cs, (long long)pair);
+            }
+          }
+        ++items_checked;
+      }
+    }
+  }
+  for (size_t i = 0; i < hq.size(); ++i) CHECK(hq[i] == 1, "wave q output %zu unwritten", i);
+  for (size_t i = 0; i < hk.size(); ++i) CHECK(hk[i] == 1, "wave k output %zu unwritten", i);
+  return true;
+}
+
+static int wave_plans = 0;
+
 static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, int64_t H,
-                 int64_t rd, std::vector<int64_t> sec, int64_t cache_mode, int64_t q_pad) {
+                 int64_t rd, std::vector<int64_t> sec, int64_t cache_mode, int64_t q_pad,
+                 uintptr_t pos_offset = 0) {
   const int64_t m = sec.empty() ? 0 : int64_t(sec.size());
   rope_tensor pos{};
-  pos.data = reinterpret_cast<void *>(uintptr_t(0x20000000));
+  pos.data = reinterpret_cast<void *>(uintptr_t(0x20000000) + pos_offset);
   pos.dtype = ROPE_I64;
   if (m) {
     pos.ndim = 2;
@@ -207,6 +318,14 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
   for (size_t t = 0; t < tok_seen.size(); ++t) CHECK(tok_seen[t] == 1, "token %zu in no tile", t);
   for (size_t i = 0; i < hq.size(); ++i) CHECK(hq[i] == 1, "q output %zu unwritten", i);
   for (size_t i = 0; i < hk.size(); ++i) CHECK(hk[i] == 1, "k output %zu unwritten", i);
+  // the wavefront path: taken exactly when its conditions hold (16-byte access everywhere,
+  // at most 64 units per head, aligned positions); then walked as the kernel walks it
+  const bool wave_ok = p.vector_io && p.cache_vec && p.units <= 64 && pos_offset % 8 == 0;
+  CHECK(p.wave == wave_ok, "wave path %d, conditions say %d", int(p.wave), int(wave_ok));
+  if (p.wave) {
+    ++wave_plans;
+    return walk_waves(p, neox, T, nq, nk, H, rd, sec, cache_mode, qs);
+  }
   return true;
 }
 
@@ -236,6 +355,26 @@ int main() {
                 }
         }
   }
-  std::printf("ok %d %llu\n", plans, (unsigned long long)items_checked);
+  // plans the wavefront path does not take: heads of more than 64 units, positions not
+  // 8-byte aligned
+  for (rope_dtype dt : {ROPE_F32, ROPE_BF16})
+    for (bool neox : {true, false}) {
+      const int64_t v = dt == ROPE_F32 ? 4 : 8;
+      const int64_t H = (neox ? 2 : 1) * v * 72;  // 72 units per head
+      for (int64_t T : {int64_t(1), int64_t(9)}) {
+        if (!walk(dt, neox, T, 3, 2, H, H / 2, {}, 0, 0)) return 1;
+        if (!walk(dt, neox, T, 2, 1, H, H, {}, 0, 0, 4)) return 1;
+        plans += 2;
+      }
+      if (!walk(dt, neox, 5, 3, 1, 128, 128, {16, 24, 24}, 0, 0, 2)) return 1;
+      ++plans;
+    }
+  if (wave_plans == 0 || wave_plans == plans) {
+    std::printf("FAIL: %d of %d plans take the wavefront path; both paths must be covered\n",
+                wave_plans, plans);
+    return 1;
+  }
+  std::printf("ok %d %llu (%d on the wavefront path)\n", plans,
+              (unsigned long long)items_checked, wave_plans);
   return 0;
 }
