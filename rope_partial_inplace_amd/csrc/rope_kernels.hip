@@ -880,7 +880,13 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
   if constexpr (MULTI) multi_rows<C>(p, uint32_t(i0), rows);
   else if (p.mrope) sec = mrope_section_of(p, i0);
   const_i64 *pos_s = reinterpret_cast<const_i64 *>(reinterpret_cast<uintptr_t>(p.positions));
+  // offsets of position rows 0..3 (rows past the last one repeat it): four unconditional
+  // loads, which the compiler keeps in flight across the q/k loads (loads under a branch
+  // were waited for before the q/k loads went out)
   const int nrows = p.mrope ? p.nsec : 1;
+  int64_t roff[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) roff[r] = int64_t(r < nrows ? r : nrows - 1) * p.pos_stride_row;
   constexpr uint32_t kWpb = kWaveBlock / 64;
   for (uint32_t gw = __builtin_amdgcn_readfirstlane(blockIdx.x * kWpb + threadIdx.x / 64);
        gw < uint32_t(p.waves); gw += gridDim.x * kWpb) {
@@ -889,10 +895,8 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
     const int64_t hbase = int64_t(gw - t32 * p.wave_wpt) * p.wave_heads + hs;
     // the token's position rows (wave-uniform scalar loads), issued first
     int64_t prow[4];
-    prow[0] = pos_s[t * p.pos_stride_tok];
 #pragma unroll
-    for (int r = 1; r < 4; ++r)
-      prow[r] = r < nrows ? pos_s[r * p.pos_stride_row + t * p.pos_stride_tok] : prow[0];
+    for (int r = 0; r < 4; ++r) prow[r] = pos_s[roff[r] + t * p.pos_stride_tok];
     // q/k loads of every item (a lane past the last head loads the last head again and
     // stores nothing)
     RawN<T, V, true> v[K][NV];
@@ -906,6 +910,9 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
       load_raw<T, V, true, true>(in, in_row + off_a, v[k][0]);
       if constexpr (NV == 2) load_raw<T, V, true, true>(in, in_row + off_b, v[k][NV - 1]);
     }
+    // All four positions are needed here, after the q/k loads went out: otherwise the compiler
+    // moves each scalar load under the per-lane row choice below and waits for them in turn.
+    asm volatile("" ::"s"(prow[0]), "s"(prow[1]), "s"(prow[2]), "s"(prow[3]));
     // the lane's cos and sin chunks: gather, split, stitch
     CsChunk<T, CB> cw, sw;
     if constexpr (MULTI) {

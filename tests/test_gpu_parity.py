@@ -538,6 +538,55 @@ def test_cache_max_tokens_and_large_rotary_dim():
                   4096, True, qo.cpu(), ko.cpu(), "rd=2048")
 
 
+@pytest.mark.parametrize("H,neox", [(1024, True), (1056, True), (512, False), (544, False)],
+                         ids=["neox64units", "neox66units", "gptj64units", "gptj68units"])
+def test_cache_units_per_head_either_side_of_64(H, neox):
+    """bf16 heads of exactly 64 units (one row of lanes per head on the wavefront path) and
+    just above (the tile path): 5 + 3 heads, half of each head rotated, 300 tokens."""
+    rd = H // 2 if (H // 2) % 32 == 0 else H - 32
+    case = W.cache_case("units", 300, 5, 3, H, rd, torch.bfloat16, neox, 700, seed=H,
+                        device=DEV)
+    qo, ko = run_cache_case(case)
+    compare_cache_case(case, qo, ko, f"H{H} rd{rd} neox={neox}")
+
+
+@pytest.mark.parametrize("neox", [True, False], ids=["neox", "gptj"])
+@pytest.mark.parametrize("sec,cache_mode", [(None, None), ([16, 24, 24], 0), ([24, 20, 20], 1),
+                                            ([11, 11, 10], 0)],
+                         ids=["rope", "mrope", "interleaved", "split_sections"])
+def test_cache_idle_lanes_with_pass_through(sec, cache_mode, neox):
+    """Heads whose units do not divide a row of 64 lanes (bf16 H = 192: 12 NeoX units, 5 heads
+    per row and 4 idle lanes; 24 GPT-J units, 2 heads per row and 16 idle lanes), with a
+    pass-through part (rd 128 of 192; 64 for [11,11,10]), 7 + 3 heads, in rope mode and every
+    stitching form."""
+    H, rd = 192, 2 * sum(sec) if sec else 128
+    m = len(sec) if sec else 0
+    pos = W.mrope_positions(150, 2, 9, 7, m=m) if m else None
+    case = W.cache_case("idle", 276 if not m else pos.shape[1], 7, 3, H, rd, torch.bfloat16,
+                        neox, 400, seed=77, mrope_section=sec, positions=pos, device=DEV,
+                        cache_mode=cache_mode)
+    qo, ko = run_cache_case(case)
+    compare_cache_case(case, qo, ko, f"idle lanes {sec} mode {cache_mode} neox={neox}")
+
+
+def test_cache_more_waves_than_one_grid():
+    """4.5M tokens of one q and one k head (bf16, H = rd = 32, GPT-J): one wavefront per
+    token, more wavefronts than the largest grid holds, so the kernel's grid-stride loop runs.
+    Every output's rotation is checked on the GPU against the oracle's at seeded sample tokens,
+    the first 2048 and the last 2048 tokens (the last ones come from the loop's later
+    trips)."""
+    T, H = 4_500_000, 32
+    case = W.cache_case("grid", T, 1, 1, H, H, torch.bfloat16, False, 5000, seed=4500,
+                        device=DEV)
+    qo, ko = run_cache_case(case)
+    g = torch.Generator().manual_seed(45)
+    idx = torch.cat([torch.arange(2048), torch.randperm(T, generator=g)[:4096],
+                     torch.arange(T - 2048, T)]).unique().sort().values
+    gi = idx.to(DEV)
+    compare_cache(case.positions[gi].cpu(), case.query[gi].cpu(), case.key[gi].cpu(),
+                  case.cache.cpu(), None, H, False, qo[gi].cpu(), ko[gi].cpu(), case.name)
+
+
 def test_cache_deterministic():
     case = W.cache_mrope(DEV)
     a = run_cache_case(case)
