@@ -875,10 +875,18 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
   } else {
     off_a = int64_t(u) * V;
   }
-  int rows[C];  // MULTI: the position row of each element of the chunk
-  int sec = 0;  // otherwise: the one row of the whole chunk
-  if constexpr (MULTI) multi_rows<C>(p, uint32_t(i0), rows);
-  else if (p.mrope) sec = mrope_section_of(p, i0);
+  // MULTI: the position row of element j of the chunk in bits 2j, 2j+1 (one register instead
+  // of C); otherwise the one row of the whole chunk
+  uint32_t rmask = 0;
+  int sec = 0;
+  if constexpr (MULTI) {
+    int rows[C];
+    multi_rows<C>(p, uint32_t(i0), rows);
+#pragma unroll
+    for (int j = 0; j < C; ++j) rmask |= uint32_t(rows[j]) << (2 * j);
+  } else if (p.mrope) {
+    sec = mrope_section_of(p, i0);
+  }
   const_i64 *pos_s = reinterpret_cast<const_i64 *>(reinterpret_cast<uintptr_t>(p.positions));
   // offsets of position rows 0..3 (rows past the last one repeat it): four unconditional
   // loads, which the compiler keeps in flight across the q/k loads (loads under a branch
@@ -925,8 +933,9 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
       }
 #pragma unroll
       for (int j = 0; j < C; ++j) {
-        cw.e[j] = rows[j] == 0 ? cr[0].e[j] : rows[j] == 1 ? cr[1].e[j] : cr[2].e[j];
-        sw.e[j] = rows[j] == 0 ? sr[0].e[j] : rows[j] == 1 ? sr[1].e[j] : sr[2].e[j];
+        const uint32_t r = (rmask >> (2 * j)) & 3u;
+        cw.e[j] = r == 0 ? cr[0].e[j] : r == 1 ? cr[1].e[j] : cr[2].e[j];
+        sw.e[j] = r == 0 ? sr[0].e[j] : r == 1 ? sr[1].e[j] : sr[2].e[j];
       }
     } else {
       const int64_t pos = sec == 0 ? prow[0] : sec == 1 ? prow[1] : sec == 2 ? prow[2] : prow[3];
