@@ -177,7 +177,18 @@ def describe_case(name, case):
 
 
 def kernel_name(case) -> str:
-    return "inplace_rope_kernel" if hasattr(case, "x") else "cos_sin_cache_kernel"
+    """The kernel a workload's launches run.  The cache op takes its wavefront kernel when q/k
+    and the cache rows allow 16-byte access, a head holds at most 64 units (NeoX: two
+    16-byte vectors each, GPT-J: one) and the positions are 8-byte aligned; the profile
+    summaries under profiles/ record the symbol each workload's dispatches actually had."""
+    if hasattr(case, "x"):
+        return "inplace_rope_kernel"
+    es = case.query.element_size()
+    units = case.head_size * es // (32 if case.is_neox else 16)
+    aligned = all(t.data_ptr() % 16 == 0 and (t.stride(0) * es) % 16 == 0
+                  for t in (case.query, case.key, case.cache))
+    wave = aligned and units <= 64 and case.positions.data_ptr() % 8 == 0
+    return "cos_sin_cache_wave_kernel" if wave else "cos_sin_cache_kernel"
 
 
 def traffic_for(workload: str):
@@ -203,7 +214,7 @@ def size_sweep(torch, ra, W, dev, cyc):
              lambda m=m: W.inplace_case("sweep", 8 * m, 4096, 1, 576, torch.bfloat16,
                                         torch.float32, [512, 576], seed=1100 + m, device=dev))
             for m in (1, 2, 4, 8, 16)],
-        "cos_sin_cache_kernel": [
+        "cos_sin_cache_wave_kernel": [
             (f"rope NeoX bf16 T={8192 * m} q 32x128 k 8x128", m,
              lambda m=m: W.cache_case("sweep", 8192 * m, 32, 8, 128, 128, torch.bfloat16, True,
                                       32768, seed=1200 + m, device=dev))
