@@ -4,7 +4,8 @@ so a failure names a reproducible configuration.
 
 In-place op: dtype pair, D, slice (even or odd start, any even length), B/S/N, cos/sin layout,
 rotary mode and direction.  Cache op: dtype, style, rope / mrope (every whitelisted list) and
-cacheMode, headSize and rotaryDim, head counts, token count, cache length, positions and
+cacheMode, headSize and rotaryDim (including heads of 8 to 34 64-byte blocks, either side of
+64 units per head), head counts (up to 48 + 16), token count, cache length, positions and
 row strides.
 """
 import numpy as np
@@ -78,6 +79,14 @@ def cache_fuzz(seed):
     H = rd + align * int(rng.integers(0, 3))
     nq, nk = int(rng.integers(1, 9)), int(rng.integers(1, 9))
     T = int(rng.integers(1, 1500))
+    wide = rng.random()
+    if wide < 0.15:  # many heads: several wavefronts per token, a partly empty last row
+        nq, nk = int(rng.integers(9, 49)), int(rng.integers(1, 17))
+        T = int(rng.integers(1, 400))
+    elif wide < 0.25 and kind == 0:  # wide heads either side of 64 units per head
+        H = align * int(rng.choice([8, 16, 17, 32, 33, 34]))
+        rd = align * int(rng.integers(1, H // align + 1))
+        T = int(rng.integers(1, 200))
     max_seq = int(rng.integers(1, 3000))
     modes = [None, 0] + ([1] if sec is not None and len(sec) == 3 else [])
     cache_mode = modes[int(rng.integers(len(modes)))]
