@@ -21,6 +21,7 @@
 // Prints "ok <plans> <items>" or the first failure; exit status 1 on failure.
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 #include <vector>
 
@@ -183,10 +184,15 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
 }
 
 static int wave_plans = 0;
+// Every g_stride-th plan is walked (1: all of them); runs under the sanitizers use a sparser
+// sample of the same plans.
+static int g_stride = 1, g_seen = 0, g_walked = 0;
 
 static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, int64_t H,
                  int64_t rd, std::vector<int64_t> sec, int64_t cache_mode, int64_t q_pad,
                  uintptr_t pos_offset = 0) {
+  if (g_seen++ % g_stride != 0) return true;
+  ++g_walked;
   const int64_t m = sec.empty() ? 0 : int64_t(sec.size());
   rope_tensor pos{};
   pos.data = reinterpret_cast<void *>(uintptr_t(0x20000000) + pos_offset);
@@ -329,7 +335,8 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
   return true;
 }
 
-int main() {
+int main(int argc, char **argv) {
+  if (argc > 1 && std::atoi(argv[1]) > 1) g_stride = std::atoi(argv[1]);
   int plans = 0;
   const std::vector<std::vector<int64_t>> mlists = {
       {}, {16, 24, 24}, {8, 12, 12}, {24, 20, 20}, {11, 11, 10}, {16, 16, 16, 16}};
@@ -369,12 +376,12 @@ int main() {
       if (!walk(dt, neox, 5, 3, 1, 128, 128, {16, 24, 24}, 0, 0, 2)) return 1;
       ++plans;
     }
-  if (wave_plans == 0 || wave_plans == plans) {
+  if (wave_plans == 0 || wave_plans == g_walked) {
     std::printf("FAIL: %d of %d plans take the wavefront path; both paths must be covered\n",
-                wave_plans, plans);
+                wave_plans, g_walked);
     return 1;
   }
-  std::printf("ok %d %llu (%d on the wavefront path)\n", plans,
-              (unsigned long long)items_checked, wave_plans);
+  std::printf("ok %d %llu (%d walked, %d on the wavefront path)\n", plans,
+              (unsigned long long)items_checked, g_walked, wave_plans);
   return 0;
 }
