@@ -21,6 +21,7 @@ import json
 import math
 import os
 import platform
+import re
 import sys
 import time
 
@@ -38,9 +39,13 @@ def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_code_hash() -> str:
+    """sha256[:16] of rope_kernels.hip with its // comments, trailing blanks and blank lines
+    removed: it changes when the kernels' code does, not when a comment is edited, so a
+    traffic figure stays attached to the code it was measured on."""
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        lines = [re.sub(r"//.*$", "", line).rstrip() for line in f.read().splitlines()]
+    return hashlib.sha256("\n".join(x for x in lines if x).encode()).hexdigest()[:16]
 
 
 # ------------------------------------------------------------------------------------------
@@ -199,7 +204,7 @@ def traffic_for(workload: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_code_sha256_16") != kernel_code_hash():
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -239,7 +244,7 @@ def size_sweep(torch, ra, W, dev, cyc):
         slope, fixed = np.polyfit(b, t, 1)
         out[kern] = {"points": pts, "fit_fixed_us": round(float(fixed), 3),
                      "fit_marginal_gbs": round(float(1e-3 / slope), 1)}
-    return {"sweep": out, "kernel_source_sha256_16": kernel_source_hash()}
+    return {"sweep": out, "kernel_code_sha256_16": kernel_code_hash()}
 
 
 # ------------------------------------------------------------------------------------------
@@ -416,7 +421,7 @@ def main() -> int:
         "kernels": {k: v for k, v in results.items() if k != head},
         "copy_ceiling_gbs": round(ceiling, 1),
         "copy_same_bytes": same,
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_code_sha256_16": kernel_code_hash(),
     }
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_budget_s:.0f} s")

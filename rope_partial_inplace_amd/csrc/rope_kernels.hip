@@ -834,7 +834,7 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
 // u*V...; GPT-J: the V/2 pair indices u*V/2...) is the same for all of its items and is read
 // straight from the token's cache row; the lanes of one unit read the same bytes, which the
 // caches serve.  The token's positions are wave-uniform and are read through the scalar
-// cache, so waiting for them does not wait for the q/k loads issued after them.
+// cache, so waiting for them does not wait for the q/k loads in flight.
 // ============================================================================================
 typedef const __attribute__((address_space(4))) int64_t const_i64;
 
@@ -901,7 +901,8 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
     const uint32_t t32 = fdiv(p.div_wpt, gw);
     const int64_t t = t32;
     const int64_t hbase = int64_t(gw - t32 * p.wave_wpt) * p.wave_heads + hs;
-    // the token's position rows (wave-uniform scalar loads), issued first
+    // the token's position rows (wave-uniform scalar loads; they go out with the q/k loads
+    // below and are waited for only after those, see the asm statement)
     int64_t prow[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) prow[r] = pos_s[roff[r] + t * p.pos_stride_tok];
