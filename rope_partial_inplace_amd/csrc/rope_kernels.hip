@@ -845,25 +845,49 @@ union CsChunk {
   typename Io<T>::raw e[CB / int(sizeof(T))];
 };
 
-template <typename T, bool NEOX, bool MULTI>
+// XCH (NeoX with rotaryDim <= headSize/2): lane u's first access takes vector u of the head
+// and its second vector units + u, so each access instruction covers whole lines of the heads
+// (with the two-vector units, a partial rotaryDim left every access half or a quarter of each
+// line it touched).  All rotated vectors are then in the first access, lanes 0 .. 2R-1
+// (R = rotated units); the pair partner of vector u is vector u + R or u - R, which its own
+// lane holds, and is read from there with ds_bpermute.  Each lane rotates its own vector.
+// LIN (NeoX): a unit is one vector, as in GPT-J, so a head's vectors lie on consecutive lanes
+// and each access covers whole heads; the pair partner (R vectors away, R = rotaryDim/(2V))
+// is read from its lane with ds_bpermute, as in XCH.
+template <typename T, bool NEOX, bool MULTI, bool XCH, bool LIN>
 __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePlan p) {
+  static_assert(!(XCH || LIN) || NEOX, "the lane exchange is a NeoX layout");
+  static_assert(!(XCH && LIN), "one layout at a time");
+  constexpr bool EXCH = XCH || LIN;  // rotated vectors pair across lanes
   constexpr int V = Io<T>::kPer16;
-  constexpr int NV = NEOX ? 2 : 1;   // vectors per unit
+  constexpr int NV = NEOX && !LIN ? 2 : 1;  // vectors per unit
   constexpr int K = kWaveItemsPerLane;
   constexpr int C = NEOX ? V : V / 2;  // cos (and sin) elements of the lane's chunk
   constexpr int CB = C * int(sizeof(T));  // 16 bytes (NeoX) or 8 (GPT-J)
   constexpr int PW = Io<T>::kPerWord;
   const uint32_t lane = __lane_id();
-  const uint32_t hsub = lane / p.units;
-  const uint32_t u = lane - hsub * p.units;
+  const uint32_t lanes_per_head = LIN ? 2 * p.units : p.units;
+  const uint32_t hsub = lane / lanes_per_head;
+  const uint32_t u = lane - hsub * lanes_per_head;
   const bool lane_on = hsub < p.wave_hpw;  // lanes past the last whole head are idle
   const uint32_t hs = lane_on ? hsub : 0;   // (idle lanes load like the first head row)
-  const bool rot = u < p.rot_units;
+  const uint32_t R = p.rot_units;
+  // rot: the lane's (first) vector is rotated; cu: the cos|sin chunk it uses
+  const bool rot = EXCH ? u < 2 * R : u < R;
+  const uint32_t cu = !rot ? 0 : (EXCH && u >= R) ? u - R : u;
   const int64_t rd = p.rd, half = rd / 2, nh = p.nq + p.nk;
-  const int64_t i0 = int64_t(rot ? u : 0) * C;  // first cos element of the lane's chunk
+  const int64_t i0 = int64_t(cu) * C;  // first cos element of the lane's chunk
+  // XCH: the lane holding the pair partners of this lane's first vector (ds_bpermute address)
+  const int xaddr =
+      int(((EXCH && rot && lane_on) ? lane - u + (u < R ? u + R : u - R) : lane) << 2);
   // element offsets of the lane's vectors inside a head, the same for each of its items
   int64_t off_a, off_b = 0;
-  if constexpr (NEOX) {
+  if constexpr (XCH) {
+    off_a = int64_t(u) * V;
+    off_b = p.H / 2 + int64_t(u) * V;
+  } else if constexpr (LIN) {
+    off_a = int64_t(u) * V;
+  } else if constexpr (NEOX) {
     if (rot) {
       off_a = int64_t(u) * V;
       off_b = half + int64_t(u) * V;
@@ -947,11 +971,53 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
     // rotate the first rd of every head, copy the rest as raw bits
 #pragma unroll
     for (int k = 0; k < K; ++k) {
+      // XCH: every lane takes part in the exchange before any lane branches off
+      RawN<T, V, true> xp;
+      if constexpr (EXCH) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w = word_of(v[k][0].v[0], q);
+          const uint32_t r = uint32_t(__builtin_amdgcn_ds_bpermute(xaddr, int(w)));
+          if (q == 0) xp.v[0].x = r;
+          else if (q == 1) xp.v[0].y = r;
+          else if (q == 2) xp.v[0].z = r;
+          else xp.v[0].w = r;
+        }
+      }
       const int64_t h = hbase + int64_t(k) * p.wave_hpw;
       if (!lane_on || h >= nh) continue;
       const bool is_q = h < p.nq;
       const int64_t out_row = t * ((is_q ? p.nq : p.nk) * p.H) + (is_q ? h : h - p.nq) * p.H;
       void *out = is_q ? p.q_out : p.k_out;
+      if constexpr (EXCH) {
+        if constexpr (XCH) store_raw<T, V, true, true>(out, out_row + off_b, v[k][NV - 1]);
+        if (!rot) {
+          store_raw<T, V, true, true>(out, out_row + off_a, v[k][0]);
+          continue;
+        }
+        // [RSCC §rotate_half（GPT-NeoX style）旋转模式]: the x1 lane (u < R) writes
+        // x1*cos - x2*sin, the x2 lane x2*cos + x1*sin; "a" is the lane's own element, "b" its
+        // partner's
+        const bool x1_lane = u < R;
+        RawN<T, V, true> oa;
+#pragma unroll
+        for (int q = 0; q < V / PW; ++q) {
+          float a[PW], b[PW], y[PW], cv[PW], sv[PW];
+          raw_word_to_float<T, V, true>(v[k][0], q, a);
+          raw_word_to_float<T, V, true>(xp, q, b);
+          Io<T>::word_to_floats(cw.w.w[q], cv);
+          Io<T>::word_to_floats(sw.w.w[q], sv);
+#pragma unroll
+          for (int e = 0; e < PW; ++e) {
+            const float pr = a[e] * cv[e];
+            const float qr = b[e] * sv[e];
+            y[e] = x1_lane ? pr - qr : pr + qr;
+          }
+          float_to_raw_word<T, V, true>(y, q, oa);
+        }
+        store_raw<T, V, true, true>(out, out_row + off_a, oa);
+        continue;
+      }
       if (!rot) {
         store_raw<T, V, true, true>(out, out_row + off_a, v[k][0]);
         if constexpr (NV == 2) store_raw<T, V, true, true>(out, out_row + off_b, v[k][NV - 1]);
@@ -1062,9 +1128,15 @@ const void *pick_cache_rows(bool neox, bool vec) {
 template <typename T>
 const void *pick_cache(const CachePlan &p) {
   if (p.wave) {
-#define ROPE_K2W(NX, MU) reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, MU>)
-    if (p.neox) return p.multi_row ? ROPE_K2W(true, true) : ROPE_K2W(true, false);
-    return p.multi_row ? ROPE_K2W(false, true) : ROPE_K2W(false, false);
+#define ROPE_K2W(NX, MU, XC, LI) \
+  reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, MU, XC, LI>)
+    if (p.neox && p.wave_lin)
+      return p.multi_row ? ROPE_K2W(true, true, false, true) : ROPE_K2W(true, false, false, true);
+    if (p.neox && p.wave_xch)
+      return p.multi_row ? ROPE_K2W(true, true, true, false) : ROPE_K2W(true, false, true, false);
+    if (p.neox)
+      return p.multi_row ? ROPE_K2W(true, true, false, false) : ROPE_K2W(true, false, false, false);
+    return p.multi_row ? ROPE_K2W(false, true, false, false) : ROPE_K2W(false, false, false, false);
 #undef ROPE_K2W
   }
   return p.multi_row ? pick_cache_rows<T, true>(p.neox, p.vector_io)

@@ -473,9 +473,23 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
   // The wavefront path needs 16-byte q/k and cache access, a head of at most 64 units (one
   // row of lanes), positions readable as aligned 8-byte words (they go through the scalar
   // cache), and a wave count that fits its 32-bit index.
-  if (p.vector_io && p.cache_vec && p.units >= 1 && p.units <= 64 &&
+  // NeoX layouts.  Each access instruction should cover whole 128-byte lines of the heads:
+  //  - pair units (two vectors, i and i + rd/2, per lane) span rd/2 elements of a head per
+  //    access: taken when that is a whole number of lines;
+  //  - otherwise, with rd <= H/2, the exchange layout (accesses span H/2) when that is whole
+  //    lines;
+  //  - otherwise one-vector units (accesses span whole heads).
+  // Measured with bf16 q/k: rd 64 or 32 of H 128 36.7-43.2 -> 29.8-30.0 us with the exchange
+  // layout; rd 96 of H 128 43.0 -> 33.1 us and H = rd = 64 36.2 -> 31.4 us with one-vector
+  // units, which are 5-12% slower than pair units on whole-line shapes.
+  const int64_t line = 128;
+  const bool pair_lines = (rd / 2 * es) % line == 0;
+  const bool xch = p.neox && !pair_lines && 2 * rd <= head_size && (head_size / 2 * es) % line == 0;
+  const bool lin = p.neox && !pair_lines && !xch && 2 * p.units <= 64;
+  const uint32_t lanes = lin ? 2 * p.units : p.units;  // lanes per head
+  if (p.vector_io && p.cache_vec && lanes >= 1 && lanes <= 64 &&
       (reinterpret_cast<uintptr_t>(p.positions) & 7u) == 0) {
-    const uint32_t hpw = 64u / p.units;
+    const uint32_t hpw = 64u / lanes;
     const uint32_t heads = uint32_t(kWaveItemsPerLane) * hpw;
     const int64_t wpt = (p.nq + p.nk + heads - 1) / heads;
     if (wpt <= int64_t(0x7fffffff) && T <= kMaxWaves / wpt) {
@@ -485,6 +499,8 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
       p.wave_wpt = uint32_t(wpt);
       p.waves = T * wpt;
       p.div_wpt = make_fastdiv(p.wave_wpt);
+      p.wave_lin = lin;
+      p.wave_xch = xch;
     }
   }
   return ROPE_OK;

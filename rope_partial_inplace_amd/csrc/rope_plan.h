@@ -113,6 +113,13 @@ struct CachePlan {
   uint32_t wave_wpt = 0;        // wavefronts per token: ceil((nq + nk) / wave_heads)
   int64_t waves = 0;            // T * wave_wpt (< 2^31)
   FastDiv div_wpt;
+  // NeoX with rotaryDim <= headSize / 2: a lane's two accesses take vectors u and units + u of
+  // the head (whole lines per access); a rotated vector's pair partner comes from another
+  // lane of the same head (cross-lane read)
+  bool wave_xch = false;
+  // NeoX with one-vector units (a head's vectors on consecutive lanes, 2 * units lanes per
+  // head); rotated pairs are completed by the same cross-lane read
+  bool wave_lin = false;
 };
 
 int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor *sin,

@@ -97,8 +97,10 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
                        int64_t cache_mode, int64_t qs) {
   const int64_t V = p.vec, half = rd / 2, nh = nq + nk;
   const int64_t C = neox ? V : V / 2;
-  CHECK(p.units >= 1 && p.units <= 64 && p.wave_hpw == 64 / p.units, "wave plan units %u hpw %u",
-        p.units, p.wave_hpw);
+  const uint32_t lanes = p.wave_lin ? 2 * p.units : p.units;  // lanes per head
+  CHECK(!p.wave_lin || (neox && !p.wave_xch), "one-vector NeoX units on a GPT-J or exchange plan");
+  CHECK(lanes >= 1 && lanes <= 64 && p.wave_hpw == 64 / lanes, "wave plan lanes %u hpw %u",
+        lanes, p.wave_hpw);
   CHECK(p.wave_heads == uint32_t(kWaveItemsPerLane) * p.wave_hpw, "wave heads %u", p.wave_heads);
   CHECK(int64_t(p.wave_wpt) * p.wave_heads >= nh &&
             int64_t(p.wave_wpt - 1) * p.wave_heads < nh, "waves per token %u", p.wave_wpt);
@@ -110,12 +112,25 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
     CHECK(t32 == uint32_t(gw / p.wave_wpt), "wave %lld decodes to token %u", (long long)gw, t32);
     const int64_t t = t32;
     const int64_t hbase0 = int64_t(uint32_t(gw) - t32 * p.wave_wpt) * p.wave_heads;
+    const bool xch = p.wave_xch, lin = p.wave_lin, exch = xch || lin;
+    const uint32_t R = p.rot_units;
     for (uint32_t lane = 0; lane < 64; ++lane) {
-      const uint32_t hsub = lane / p.units, u = lane - hsub * p.units;
+      const uint32_t hsub = lane / lanes, u = lane - hsub * lanes;
       const bool on = hsub < p.wave_hpw;
       const int64_t hbase = hbase0 + (on ? hsub : 0);
-      const bool rot = u < p.rot_units;
-      const int64_t i0 = int64_t(rot ? u : 0) * C;
+      const bool rot = exch ? u < 2 * R : u < R;
+      const uint32_t cu = !rot ? 0 : (exch && u >= R) ? u - R : u;
+      const int64_t i0 = int64_t(cu) * C;
+      if (exch && rot && on) {
+        // the partner lane: same head row, unit u + R or u - R, whose first vector holds the
+        // pair partners (column +- rd/2) of this lane's first vector
+        const uint32_t pu = u < R ? u + R : u - R;
+        const uint32_t pl = lane - u + pu;
+        CHECK(pl < 64 && pl / lanes == hsub && pu < 2 * R, "lane %u partner lane %u", lane, pl);
+        const int64_t mine = int64_t(u) * V, theirs = int64_t(pu) * V;
+        CHECK(theirs - mine == (u < R ? half : -half), "lane %u partner at %lld, own %lld", lane,
+              (long long)theirs, (long long)mine);
+      }
       CHECK(i0 + C <= half, "cos chunk [%lld, %lld) beyond rd/2", (long long)i0,
             (long long)(i0 + C));
       // rows of the chunk's elements: one row (the section of i0) unless multi-row
@@ -137,7 +152,13 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
         CHECK(got < (p.mrope ? p.nsec : 1), "row %d beyond the position rows", got);
       }
       std::vector<int64_t> offs;
-      if (neox) {
+      if (xch) {
+        CHECK(neox && 2 * rd <= H, "exchange layout on a plan with rd %lld, H %lld",
+              (long long)rd, (long long)H);
+        offs = {int64_t(u) * V, H / 2 + int64_t(u) * V};
+      } else if (lin) {
+        offs = {int64_t(u) * V};
+      } else if (neox) {
         if (rot) {
           offs = {int64_t(u) * V, half + int64_t(u) * V};
         } else {
@@ -159,15 +180,17 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
         const bool is_q = h < nq;
         const int64_t out_row = t * ((is_q ? nq : nk) * H) + (is_q ? h : h - nq) * H;
         std::vector<uint8_t> &hit = is_q ? hq : hk;
-        for (int64_t o : offs)
+        for (size_t a = 0; a < offs.size(); ++a)
           for (int64_t e = 0; e < V; ++e) {
-            const int64_t col = o + e;
-            CHECK(rot == (col < rd), "column %lld on the wrong side of rotaryDim",
+            const int64_t col = offs[a] + e;
+            // the exchange layout rotates only the first access of a rotated lane
+            const bool rotated = exch ? (rot && a == 0) : rot;
+            CHECK(rotated == (col < rd), "column %lld on the wrong side of rotaryDim",
                   (long long)col);
             const size_t oi = size_t(out_row + col);
             CHECK(hit[oi] == 0, "wave output %zu written twice", oi);
             hit[oi] = 1;
-            if (rot) {
+            if (rotated) {
               const int64_t pair = neox ? (col < half ? col : col - half) : col / 2;
               const int64_t cs = i0 + (neox ? e : e / 2);
               CHECK(pair == cs, "column %lld reads cos %lld, wants %lld", (long long)col,
@@ -183,7 +206,7 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
   return true;
 }
 
-static int wave_plans = 0;
+static int wave_plans = 0, xch_plans = 0, lin_plans = 0;
 // Every g_stride-th plan is walked (1: all of them); runs under the sanitizers use a sparser
 // sample of the same plans.
 static int g_stride = 1, g_seen = 0, g_walked = 0;
@@ -326,10 +349,18 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
   for (size_t i = 0; i < hk.size(); ++i) CHECK(hk[i] == 1, "k output %zu unwritten", i);
   // the wavefront path: taken exactly when its conditions hold (16-byte access everywhere,
   // at most 64 units per head, aligned positions); then walked as the kernel walks it
-  const bool wave_ok = p.vector_io && p.cache_vec && p.units <= 64 && pos_offset % 8 == 0;
+  const uint32_t lanes = p.wave_lin ? 2 * p.units : p.units;
+  const bool wave_ok = p.vector_io && p.cache_vec && lanes <= 64 && pos_offset % 8 == 0;
   CHECK(p.wave == wave_ok, "wave path %d, conditions say %d", int(p.wave), int(wave_ok));
+  // the NeoX layout is a speed choice; each is walked below, and the exchange layout needs
+  // rd <= H/2 (all rotated vectors in the first access)
+  CHECK(!p.wave_xch || (wave_ok && neox && !p.wave_lin && 2 * rd <= H),
+        "exchange layout %d for neox=%d rd %lld H %lld", int(p.wave_xch), int(neox),
+        (long long)rd, (long long)H);
   if (p.wave) {
     ++wave_plans;
+    xch_plans += p.wave_xch ? 1 : 0;
+    lin_plans += p.wave_lin ? 1 : 0;
     return walk_waves(p, neox, T, nq, nk, H, rd, sec, cache_mode, qs);
   }
   return true;
@@ -376,12 +407,14 @@ int main(int argc, char **argv) {
       if (!walk(dt, neox, 5, 3, 1, 128, 128, {16, 24, 24}, 0, 0, 2)) return 1;
       ++plans;
     }
-  if (wave_plans == 0 || wave_plans == g_walked) {
-    std::printf("FAIL: %d of %d plans take the wavefront path; both paths must be covered\n",
-                wave_plans, g_walked);
+  if (wave_plans == 0 || wave_plans == g_walked || xch_plans == 0 || lin_plans == 0) {
+    std::printf("FAIL: %d of %d plans take the wavefront path (%d exchange, %d one-vector "
+                "NeoX); every path and layout must be covered\n",
+                wave_plans, g_walked, xch_plans, lin_plans);
     return 1;
   }
-  std::printf("ok %d %llu (%d walked, %d on the wavefront path)\n", plans,
-              (unsigned long long)items_checked, g_walked, wave_plans);
+  std::printf("ok %d %llu (%d walked, %d on the wavefront path: %d exchange, %d one-vector "
+              "NeoX)\n", plans, (unsigned long long)items_checked, g_walked, wave_plans,
+              xch_plans, lin_plans);
   return 0;
 }

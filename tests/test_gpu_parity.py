@@ -569,6 +569,53 @@ def test_cache_idle_lanes_with_pass_through(sec, cache_mode, neox):
     compare_cache_case(case, qo, ko, f"idle lanes {sec} mode {cache_mode} neox={neox}")
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16, torch.float32],
+                         ids=lambda d: str(d).split(".")[-1])
+@pytest.mark.parametrize("H,rd,sec,cache_mode", [(128, 32, None, None), (128, 64, None, None),
+                                                  (256, 128, None, None),
+                                                  (128, 64, [11, 11, 10], 1),
+                                                  (256, 128, [16, 24, 24], 0)],
+                         ids=["rd_quarter", "rd_half", "rd_half_H256", "mrope_interleaved",
+                              "mrope_sections"])
+def test_cache_neox_partial_lane_exchange(H, rd, sec, cache_mode, dt):
+    """NeoX with rotaryDim <= headSize/2 (the wavefront kernel's lane-exchange layout: a
+    rotated vector's pair partner is read from another lane of the same head): 28 + 4 heads,
+    777 tokens or the mrope text + image positions, every dtype."""
+    es = torch.empty(0, dtype=dt).element_size()
+    if rd * es % 64:
+        pytest.skip("rotaryDim must be a 64-byte multiple")
+    pos = W.mrope_positions(300, 2, 12, 10, m=3) if sec else None
+    T = pos.shape[1] if sec else 777
+    case = W.cache_case("xch", T, 28, 4, H, rd, dt, True, 900, seed=H + rd + es,
+                        mrope_section=sec, positions=pos, device=DEV, cache_mode=cache_mode)
+    qo, ko = run_cache_case(case)
+    compare_cache_case(case, qo, ko, f"NeoX H{H} rd{rd} {sec} mode {cache_mode} {dt}")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16, torch.float32],
+                         ids=lambda d: str(d).split(".")[-1])
+@pytest.mark.parametrize("H,rd,sec,cache_mode", [(128, 96, None, None), (64, 64, None, None),
+                                                  (96, 96, None, None), (64, 32, None, None),
+                                                  (64, 64, [11, 11, 10], 1),
+                                                  (64, 64, [8, 12, 12], 0)],
+                         ids=["rd96_H128", "H64", "H96", "rd32_H64", "mrope_interleaved",
+                              "mrope_split_sections"])
+def test_cache_neox_one_vector_units(H, rd, sec, cache_mode, dt):
+    """NeoX shapes whose pair units would leave each access part of every line (half of the
+    rotated part not a whole number of 128-byte lines, and no whole-line exchange layout):
+    the wavefront kernel then gives a unit one vector and completes each pair from another
+    lane.  28 + 4 heads, 777 tokens or the mrope text + image positions, every dtype."""
+    es = torch.empty(0, dtype=dt).element_size()
+    if rd * es % 64 or H * es % 64:
+        pytest.skip("headSize and rotaryDim must be 64-byte multiples")
+    pos = W.mrope_positions(300, 2, 12, 10, m=3) if sec else None
+    T = pos.shape[1] if sec else 777
+    case = W.cache_case("lin", T, 28, 4, H, rd, dt, True, 900, seed=H + 3 * rd + es,
+                        mrope_section=sec, positions=pos, device=DEV, cache_mode=cache_mode)
+    qo, ko = run_cache_case(case)
+    compare_cache_case(case, qo, ko, f"NeoX H{H} rd{rd} {sec} mode {cache_mode} {dt}")
+
+
 def test_cache_more_waves_than_one_grid():
     """4.5M tokens of one q and one k head (bf16, H = rd = 32, GPT-J): one wavefront per
     token, more wavefronts than the largest grid holds, so the kernel's grid-stride loop runs.
