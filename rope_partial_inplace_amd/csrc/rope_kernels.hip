@@ -511,17 +511,19 @@ __global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
 }
 
 // ============================================================================================
-// K2: RoPE with a cos/sin cache ([RSCC §设计动机], rope and mrope modes, NeoX and GPT-J).
+// K2: RoPE with a cos/sin cache ([RSCC §设计动机], rope and mrope modes, NeoX and GPT-J), tile
+// form.  It serves the plans the wavefront form further below does not take: element-wise
+// access (unaligned data), heads of more than 64 lanes' units, unaligned positions.
 // A workgroup owns a tile of tokens.  Stage: its lanes gather each token's cos|sin row from
 // the cache (mrope: element i from the position row that the stitching assigns it) and keep
 // it in LDS in the cache's own element type (raised to float32 at use), so it is read from
 // HBM once per token and reused by every q/k head.  Then lanes walk (token, head, unit)
 // items.  NeoX: a unit is two V-element vectors, u and u + rd/(2V) of the rotated part (its
 // pairs lie across the halves), or the same two-vector shape over [rd, H) copied as raw bits.
-// GPT-J: a unit is one vector (its pairs lie inside it), rotated below rd and copied above.  The units of one head are adjacent
-// lanes, so each wavefront load/store covers whole runs of 128-byte lines.  q/k are
-// streamed (non-temporal loads and stores); the first pass's loads are issued before the LDS
-// staging so that their latency overlaps the position -> cache gather.
+// GPT-J: a unit is one vector (its pairs lie inside it), rotated below rd and copied above.
+// The units of one head are adjacent lanes.  q/k are streamed (non-temporal loads and
+// stores); the first pass's loads are issued before the LDS staging so that their latency
+// overlaps the position -> cache gather.
 // ============================================================================================
 // mrope: the position row whose section holds element i of cos/sin
 // ([RSCC §mrope 模式：多模态位置编码]).
@@ -827,9 +829,9 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
 }
 
 // ============================================================================================
-// K2, wavefront form (the plans it covers: 16-byte q/k and cache access, at most 64 units per
-// head).  The same operation as cos_sin_cache_kernel, with one wavefront per (token, group of
-// heads) and no LDS and no barrier.  Lane l owns unit u = l % units of head l / units in each
+// K2, wavefront form (the plans it covers: 16-byte q/k and cache access, a head's units on at
+// most 64 lanes, 8-byte aligned positions).  The same operation as cos_sin_cache_kernel, with
+// one wavefront per (token, group of heads) and no LDS and no barrier.  Lane l owns unit u = l % units of head l / units in each
 // of kWaveItemsPerLane rows of wave_hpw heads, so its cos|sin chunk (NeoX: the V elements
 // u*V...; GPT-J: the V/2 pair indices u*V/2...) is the same for all of its items and is read
 // straight from the token's cache row; the lanes of one unit read the same bytes, which the
