@@ -634,6 +634,29 @@ def test_cache_more_waves_than_one_grid():
                   case.cache.cpu(), None, H, False, qo[gi].cpu(), ko[gi].cpu(), case.name)
 
 
+def test_cache_positions_rewritten_between_calls():
+    """The wavefront kernel reads positions through the scalar cache.  Positions rewritten in
+    place on the GPU between two launches (by a torch kernel on the same stream) must be the
+    ones the second launch uses: both launches are checked against the oracle, for rope and
+    mrope positions."""
+    for sec in (None, [16, 24, 24]):
+        m = 3 if sec else 0
+        pos = W.mrope_positions(64, 1, 8, 8, m=3) if sec else None
+        case = W.cache_case("rewrite", 128 if not sec else pos.shape[1], 6, 2, 128, 128,
+                            torch.bfloat16, True, 1000, seed=77, mrope_section=sec,
+                            positions=pos, device=DEV)
+        first = [t.cpu() for t in run_cache_case(case)]
+        before = case.positions.cpu()
+        case.positions.mul_(3).add_(1).remainder_(1000)   # in place, same stream
+        second = [t.cpu() for t in run_cache_case(case)]
+        after = case.positions.cpu()
+        assert not torch.equal(before, after)
+        compare_cache(before, case.query.cpu(), case.key.cpu(), case.cache.cpu(), sec, 128,
+                      True, first[0], first[1], f"positions before rewrite, m={m}")
+        compare_cache(after, case.query.cpu(), case.key.cpu(), case.cache.cpu(), sec, 128,
+                      True, second[0], second[1], f"positions after rewrite, m={m}")
+
+
 def test_cache_deterministic():
     case = W.cache_mrope(DEV)
     a = run_cache_case(case)
