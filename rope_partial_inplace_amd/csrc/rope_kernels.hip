@@ -358,9 +358,10 @@ __device__ inline void rotate_pair(float a, float b, float c0, float c1, float s
 // slice.  HALF (rotary_mode 0, [IPRM §参数说明]; x1, x2 the two halves of the slice,
 // x_rotate = cat(-x2, x1)): a lane owns chunk u of the first half and chunk u of the second,
 // so every pair (i, i + L/2) is lane-local and both halves are read as contiguous runs.
-// XCH (half mode, 1..16 chunks per half, a power of two): a lane owns one chunk of one half
-// and reads its pair partners from lane (lane ^ chunks per half) with ds_bpermute, so the
-// launch has as many lanes, and each lane as few loads, as in interleave mode.
+// XCH (half mode, 1..16 chunks per half): a lane owns one chunk of one half and reads its
+// pair partners from lane (lane ^ xch) with ds_bpermute, xch being the chunk count of a half
+// rounded up to a power of two (PAD when that rounds up: the extra lanes carry no chunk), so
+// the launch has about as many lanes, and each lane as few loads, as in interleave mode.
 // NHL = 2 or 4 (cos/sin broadcast over the heads): the lane owns its chunk in NHL consecutive
 // heads of one (b, s) and loads the cos/sin chunk once for all of them.  Elements outside
 // [start, end) are never touched.  cos/sin rows are addressed with zero strides on broadcast
@@ -371,7 +372,8 @@ __device__ inline void rotate_pair(float a, float b, float c0, float c1, float s
 // ============================================================================================
 // One lane item: chunk `chunk` of the NHL x rows starting at row r * NHL, whose cos/sin row
 // is that of (b, s, head g * NHL).
-template <typename XT, typename CT, bool VEC, int NHL, bool CNT, bool BWD, bool HALF, bool XCH>
+template <typename XT, typename CT, bool VEC, int NHL, bool CNT, bool BWD, bool HALF, bool XCH,
+          bool PAD>
 __device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, uint64_t chunk,
                                              uint64_t b, uint64_t s, uint64_t g) {
   // one 16-byte access per lane for the wider of x and cos/sin, 8 bytes for the narrower;
@@ -381,8 +383,18 @@ __device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, u
   constexpr int NH = HALF && !XCH ? 2 : 1;  // chunks per head: one, or one in each half
   const int64_t hoff = HALF ? p.L / 2 : 0;  // offset of the second half
   const int64_t crow = int64_t(b) * p.cb + int64_t(s) * p.cs + int64_t(g) * NHL * p.cn;
-  const int64_t coff = crow * p.L + int64_t(chunk) * V;
-  const int64_t x0 = int64_t(r) * NHL * p.D + p.start + int64_t(chunk) * V;
+  // element offset of the chunk in the slice.  PAD (XCH with a half's chunk count below the
+  // power of two xch): chunk c of the first half or of the second (chunk >= xch), the lanes
+  // past a half's last chunk loading that chunk and storing nothing
+  int64_t elem = int64_t(chunk) * V;
+  bool owns = true;
+  if constexpr (XCH && PAD) {
+    const uint32_t c = uint32_t(chunk) & (p.xch - 1);
+    owns = c < p.xch_cph;
+    elem = (chunk >= p.xch ? p.L / 2 : 0) + int64_t(owns ? c : p.xch_cph - 1) * V;
+  }
+  const int64_t coff = crow * p.L + elem;
+  const int64_t x0 = int64_t(r) * NHL * p.D + p.start + elem;
   float xv[NHL][NH][V], cv[NH][V], sv[NH][V];
   float xpv[XCH ? NHL : 1][V], spv[XCH && BWD ? V : 1];  // XCH: the partner lane's x, sin
   if constexpr (VEC) {
@@ -454,7 +466,7 @@ __device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, u
         const float qr = xpv[j][e] * (BWD ? spv[e] : sv[0][e]);
         y[e] = (second == BWD) ? pr - qr : pr + qr;
       }
-      store_n<XT, V, VEC, true>(p.x, x0 + j * p.D, y);
+      if (owns) store_n<XT, V, VEC, true>(p.x, x0 + j * p.D, y);
     }
     return;
   }
@@ -479,7 +491,8 @@ __device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, u
   }
 }
 
-template <typename XT, typename CT, bool VEC, int NHL, bool CNT, bool BWD, bool HALF, bool XCH>
+template <typename XT, typename CT, bool VEC, int NHL, bool CNT, bool BWD, bool HALF, bool XCH,
+          bool PAD>
 __global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
   // item it -> (row group r = (b, s, head group g), chunk).  Two loops: 32-bit indices with
   // multiply-high division (the usual case), and plain 64-bit division for huge tensors, kept
@@ -493,7 +506,7 @@ __global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
       const uint32_t g = r - bs * ng;
       const uint32_t b = fdiv(p.div_s, bs);
       const uint32_t s = bs - b * uint32_t(p.S);
-      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF, XCH>(p, r, chunk, b, s, g);
+      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF, XCH, PAD>(p, r, chunk, b, s, g);
     }
   } else {
     const uint64_t items = uint64_t(p.items), ng = uint64_t(p.N) / NHL;
@@ -505,7 +518,7 @@ __global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
       const uint64_t g = r - bs * ng;
       const uint64_t b = bs / uint64_t(p.S);
       const uint64_t s = bs - b * uint64_t(p.S);
-      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF, XCH>(p, r, chunk, b, s, g);
+      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF, XCH, PAD>(p, r, chunk, b, s, g);
     }
   }
 }
@@ -1080,10 +1093,11 @@ int launch(const void *fn, int64_t blocks, int threads, size_t lds, void *stream
   return ROPE_OK;
 }
 
-template <typename XT, typename CT, bool BWD, bool HALF, bool XCH>
+template <typename XT, typename CT, bool BWD, bool HALF, bool XCH, bool PAD>
 const void *pick_inplace_vec(const InplacePlan &p) {
 #define ROPE_K1(NHL, CNT) \
-  reinterpret_cast<const void *>(&inplace_rope_kernel<XT, CT, true, NHL, CNT, BWD, HALF, XCH>)
+  reinterpret_cast<const void *>(                                                       \
+      &inplace_rope_kernel<XT, CT, true, NHL, CNT, BWD, HALF, XCH, PAD>)
   // Only the heads-per-lane counts a plan can choose are built: a lane's x bytes stay at 32
   // or less (x bytes per head: V elements, twice that when a lane owns both halves).
   constexpr int kV = 16 / int(sizeof(XT) > sizeof(CT) ? sizeof(XT) : sizeof(CT));
@@ -1101,10 +1115,12 @@ template <typename XT, typename CT, bool BWD, bool HALF>
 const void *pick_inplace(const InplacePlan &p) {
   if (!p.vector_io)
     return reinterpret_cast<const void *>(
-        &inplace_rope_kernel<XT, CT, false, 1, false, BWD, HALF, false>);
+        &inplace_rope_kernel<XT, CT, false, 1, false, BWD, HALF, false, false>);
   if constexpr (HALF)
-    if (p.xch != 0) return pick_inplace_vec<XT, CT, BWD, true, true>(p);
-  return pick_inplace_vec<XT, CT, BWD, HALF, false>(p);
+    if (p.xch != 0)
+      return p.xch_cph == p.xch ? pick_inplace_vec<XT, CT, BWD, true, true, false>(p)
+                                : pick_inplace_vec<XT, CT, BWD, true, true, true>(p);
+  return pick_inplace_vec<XT, CT, BWD, HALF, false, false>(p);
 }
 
 template <bool BWD, bool HALF>

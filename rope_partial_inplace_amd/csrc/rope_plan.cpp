@@ -215,12 +215,18 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
   p.vector_io = aligned;
   p.vec = aligned ? uint32_t(v) : (p.half ? 1u : 2u);
   p.chunks_per_row = uint32_t(span / p.vec);
-  // Half mode, vector path, 1..16 chunks per half (a power of two): one chunk per lane, the
-  // pair partner in lane (lane ^ chunks per half) -- twice the lanes, half the loads each.
+  // Half mode, vector path, 1..16 chunks per half: one chunk per lane, the pair partner in
+  // lane (lane ^ P) with P the chunk count of a half rounded up to a power of two; the lanes
+  // of a row past a half's last chunk carry none.  Each access then covers a row's slice as
+  // one contiguous run, where a lane owning a chunk of both halves covered each half apart:
+  // bf16 x [4,4096,32,96] (12 chunks per half) measured 44.4 us that way.
   const uint32_t cph = p.chunks_per_row;
-  if (p.half && aligned && cph <= 16 && (cph & (cph - 1)) == 0) {
-    p.xch = cph;
-    p.chunks_per_row = 2 * cph;
+  uint32_t pw = 1;
+  while (pw < cph) pw <<= 1;
+  if (p.half && aligned && cph >= 1 && pw <= 16) {
+    p.xch = pw;
+    p.xch_cph = cph;
+    p.chunks_per_row = 2 * pw;
   }
   // Heads per lane: with cos/sin broadcast over N, a lane rotates its chunk in nhl consecutive
   // heads with one cos/sin load: the larger of 4, 2 that divides N and keeps a lane's x

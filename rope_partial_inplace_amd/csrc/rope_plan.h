@@ -47,9 +47,12 @@ struct InplacePlan {
   bool half = false;  // rotary_mode 0
   // Half mode with pairs split across lanes: each lane owns one chunk of one half, and its
   // partner chunk (same position in the other half) belongs to lane (lane ^ xch), fetched by a
-  // cross-lane read.  Taken when the chunks of a half, xch, are a power of two up to 16, so a
-  // row's 2 * xch lanes never straddle a wavefront.  0 = the lane owns both chunks.
+  // cross-lane read.  xch is the chunk count of a half rounded up to a power of two, at most
+  // 16, so a row's 2 * xch lanes never straddle a wavefront.  0 = the lane owns both chunks.
   uint32_t xch = 0;
+  // chunks of one half (<= xch; xch is the next power of two): a row's lanes u with
+  // u % xch >= xch_cph carry no chunk (they load the half's last chunk and store nothing)
+  uint32_t xch_cph = 0;
   uint32_t nhl = 1;   // heads per lane (1, 2 or 4); > 1 only when cos/sin broadcast over N
   rope_dtype xdt = ROPE_F32, cdt = ROPE_F32;
   bool vector_io = false;  // 16-byte x accesses (else one element at a time)

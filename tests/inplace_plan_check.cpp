@@ -75,6 +75,7 @@ static Decoded decode(const InplacePlan &p, uint64_t it) {
 
 static int fails = 0;
 static uint64_t items_checked = 0;
+static int padded_plans = 0;
 
 #define CHECK(cond, ...)                                  \
   do {                                                    \
@@ -102,12 +103,14 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
   const int st = plan_inplace(&x, &c, &sn, mode, sl, 2, &p, &err);
   CHECK(st == ROPE_OK, "plan rejected: %s", err.c_str());
   if (p.noop) return true;
+  if (p.xch && p.xch_cph < p.xch) ++padded_plans;
   const int64_t V = p.vec, NHL = p.nhl, NH = (p.half && !p.xch) ? 2 : 1;
   const int64_t hoff = p.half ? L / 2 : 0;
   CHECK(p.xch == 0 || (p.half && p.vector_io && (p.xch & (p.xch - 1)) == 0 && p.xch <= 16 &&
-                       p.chunks_per_row == 2 * p.xch && int64_t(p.xch) * V == L / 2),
-        "lane exchange with xch %u, chunks %u, V %lld, L %lld", p.xch, p.chunks_per_row,
-        (long long)V, (long long)L);
+                       p.xch_cph <= p.xch && 2 * p.xch_cph > p.xch &&
+                       p.chunks_per_row == 2 * p.xch && int64_t(p.xch_cph) * V == L / 2),
+        "lane exchange with xch %u (%u chunks per half), chunks %u, V %lld, L %lld", p.xch,
+        p.xch_cph, p.chunks_per_row, (long long)V, (long long)L);
   CHECK(!p.idx32 || uint64_t(p.items) - 1 + uint64_t(kMaxGrid) * p.block < (uint64_t(1) << 32),
         "32-bit item index can wrap: items %lld, block %u", (long long)p.items, p.block);
   {
@@ -124,7 +127,10 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
         (long long)NHL, (long long)(NH * V * esize(xdt)));
   CHECK(NHL == 1 || (Nc == 1 && N % NHL == 0), "heads per lane %lld with Nc %lld N %lld",
         (long long)NHL, (long long)Nc, (long long)N);
-  CHECK(uint64_t(p.items) * NHL * NH * V == uint64_t(B * S * N * L),
+  // items carrying a chunk (all of them, except the lanes past a half's last chunk in XCH)
+  const uint64_t owning = p.xch ? uint64_t(p.items) / (2 * p.xch) * (2 * p.xch_cph)
+                                : uint64_t(p.items);
+  CHECK(owning * NHL * NH * V == uint64_t(B * S * N * L),
         "items %lld do not tile the slices", (long long)p.items);
   std::vector<uint8_t> hit(size_t(B * S * N * D), 0);
   for (uint64_t it = 0; it < uint64_t(p.items); ++it) {
@@ -133,15 +139,31 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
               d.chunk < p.chunks_per_row,
           "item %llu decodes out of range", (unsigned long long)it);
     const int64_t crow = int64_t(d.b) * p.cb + int64_t(d.s) * p.cs + int64_t(d.g) * NHL * p.cn;
-    const int64_t coff = crow * L + int64_t(d.chunk) * V;
-    const int64_t x0 = int64_t(d.r) * NHL * D + start + int64_t(d.chunk) * V;
+    // the kernel's element offset of a chunk (XCH: half, then chunk of the half; a lane past
+    // a half's last chunk loads that chunk and stores nothing)
+    auto elem_of = [&](uint64_t chunk, bool *owns) {
+      if (!p.xch) {
+        *owns = true;
+        return int64_t(chunk) * V;
+      }
+      const uint32_t c = uint32_t(chunk) & (p.xch - 1);
+      *owns = c < p.xch_cph;
+      return (chunk >= p.xch ? L / 2 : 0) + int64_t(*owns ? c : p.xch_cph - 1) * V;
+    };
+    bool owns;
+    const int64_t elem = elem_of(d.chunk, &owns);
+    const int64_t coff = crow * L + elem;
+    const int64_t x0 = int64_t(d.r) * NHL * D + start + elem;
     if (p.xch) {
       const Decoded q = decode(p, it ^ p.xch);
       CHECK(q.r == d.r && q.chunk == (d.chunk ^ p.xch) && (it & 63) / (2 * p.xch) ==
                                                               ((it ^ p.xch) & 63) / (2 * p.xch),
             "item %llu and its partner lane are not the pair chunks of one row",
             (unsigned long long)it);
-      const int64_t xq = int64_t(q.r) * NHL * D + start + int64_t(q.chunk) * V;
+      bool q_owns;
+      const int64_t xq = int64_t(q.r) * NHL * D + start + elem_of(q.chunk, &q_owns);
+      CHECK(q_owns == owns, "item %llu and its partner lane disagree on carrying a chunk",
+            (unsigned long long)it);
       CHECK(xq - x0 == (d.chunk < p.xch ? hoff : -hoff), "partner chunk not L/2 away");
     }
     for (int64_t j = 0; j < NHL; ++j)
@@ -159,6 +181,7 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
                 (long long)b, (long long)s, (long long)n, (long long)col, (long long)ci,
                 (long long)want);
           CHECK(ci < Bc * Sc * Nc * L, "cos index out of bounds");
+          if (!owns) continue;  // loads only
           CHECK(hit[size_t(xi)] == 0, "x index %lld touched twice", (long long)xi);
           hit[size_t(xi)] = 1;
         }
@@ -228,7 +251,10 @@ int main() {
   const Shape shapes[] = {{2, 5, 8, 64, 0, 64},   {3, 4, 12, 96, 32, 96}, {2, 3, 6, 48, 16, 48},
                           {1, 7, 5, 40, 8, 40},   {2, 3, 2, 40, 1, 37},   {2, 2, 16, 24, 0, 16},
                           {1, 2, 40, 128, 64, 128}, {2, 3, 4, 10, 4, 6},  {1, 2, 3, 1024, 0, 1024},
-                          {2, 3, 4, 48, 8, 20}};
+                          {2, 3, 4, 48, 8, 20},
+                          // half mode with chunk counts per half that are not powers of two
+                          {2, 3, 4, 96, 0, 96},   {1, 3, 6, 128, 8, 104}, {2, 2, 3, 80, 0, 80},
+                          {2, 3, 2, 64, 24, 64},  {3, 2, 2, 24, 0, 24}};
   for (const auto &sh : shapes)
     for (const auto &pr : pairs)
       for (int mode = 0; mode < 2; ++mode)
@@ -245,6 +271,11 @@ int main() {
             ++plans;
           }
   if (!limits() || !huge()) return 1;
-  std::printf("ok %d %llu\n", plans, (unsigned long long)items_checked);
+  if (padded_plans == 0) {
+    std::printf("FAIL: no half-mode plan pads its lane pairs\n");
+    return 1;
+  }
+  std::printf("ok %d %llu (%d half-mode plans with padded lane pairs)\n", plans,
+              (unsigned long long)items_checked, padded_plans);
   return 0;
 }

@@ -799,6 +799,38 @@ def test_inplace_past_one_round_of_lanes(xdt, cdt, layout, mode, direction):
         check_backward(before, g, case.cos, case.sin, None, what, mode=mode)
 
 
+@pytest.mark.parametrize("direction", ["forward", "backward"])
+@pytest.mark.parametrize("xdt,cdt", DTYPE_PAIRS, ids=lambda d: str(d).split(".")[-1])
+@pytest.mark.parametrize("layout", ["BSND", "BS1D"])
+@pytest.mark.parametrize("cph", [3, 5, 6, 7, 10, 12])
+def test_half_mode_padded_lane_pairs(cph, layout, xdt, cdt, direction):
+    """Half mode whose halves split into a chunk count that is not a power of two: a row's
+    lanes are padded to twice the next power of two and the padding lanes store nothing.
+    The slice is 2 * cph chunks of the vector width, placed at an aligned inner offset of a
+    wider D; 3 x 37 x 4 rows (ragged against the workgroups), cos/sin per head or shared by
+    the heads (heads per lane)."""
+    xs, cs = torch.empty(0, dtype=xdt).element_size(), torch.empty(0, dtype=cdt).element_size()
+    V = 16 // max(xs, cs)
+    L = 2 * cph * V
+    start = V
+    D = L + 2 * V
+    B, S, N = 3, 37, 4
+    sl = [start, start + L]
+    cshape = LAYOUTS[layout](B, S, N) + (L,)
+    case = W.inplace_case("half_pad", B, S, N, D, xdt, cdt, sl, cos_shape=cshape,
+                          seed=cph * 7 + xs + cs, table="randn", device=DEV, rotary_mode=0)
+    what = f"padded half {direction} cph={cph} {layout} {xdt}/{cdt}"
+    if direction == "forward":
+        before, x = run_inplace(case)
+        check_inplace(before, x, case.cos, case.sin, sl, what, mode=0)
+    else:
+        g = case.x
+        before = g.cpu()
+        ra.rope_partial_inplace_backward(g, case.cos, case.sin, 0, sl)
+        torch.cuda.synchronize()
+        check_backward(before, g, case.cos, case.sin, sl, what, mode=0)
+
+
 def test_half_mode_backward_full_and_autograd():
     case = W.inplace_half_bf16_slice(DEV)
     g = case.x
