@@ -92,6 +92,43 @@ def time_launches(torch, calls, steps: int, warmup: int, cyc_per_ms: float):
     return start.elapsed_time(end) / steps
 
 
+def graph_replay_us(torch, ra, case, n_sets: int, reps: int = 3) -> float:
+    """Per-launch time of the in-place op when its launches over the n_sets buffer sets are
+    captured in one HIP graph and the graph is replayed back to back (inputs rotated as in
+    the stream timing).  Reported beside the stream-launch figure: a serving loop that
+    replays a captured graph pays this per-launch cost instead."""
+    xs = [case.x] + [case.x.clone() for _ in range(n_sets - 1)]
+    cs = [case.cos] + [case.cos.clone() for _ in range(n_sets - 1)]
+    ss = [case.sin] + [case.sin.clone() for _ in range(n_sets - 1)]
+    fn = ra.rope_partial_inplace_backward if case.backward else ra.rope_partial_inplace
+
+    def launches():
+        for x, c, sn in zip(xs, cs, ss):
+            fn(x, c, sn, case.rotary_mode, case.partial_slice)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the capture, as capture requires
+        launches()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launches()
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / (reps * n_sets)
+    del g, xs, cs, ss
+    torch.cuda.empty_cache()
+    return ms * 1e3
+
+
 def copy_ceiling_gbs(torch, nbytes=1 << 30) -> float:
     """Device-to-device copy bandwidth (read + write bytes) at a footprint well above the
     Infinity Cache: the attainable-bandwidth context for the kernels."""
@@ -394,6 +431,11 @@ def main() -> int:
 
     head = names[0]
     hr = results[head]
+    if hasattr(cases[head], "x") and head != "inplace_f32_1x16x2x64":
+        gus = graph_replay_us(torch, ra, cases[head], hr["buffer_sets"])
+        hr["graph_replay"] = {"us_per_launch": round(gus, 3),
+                              "gbs": round(cases[head].algo_bytes / gus / 1e3, 1)}
+        log(f"{head} replayed from one HIP graph: {gus:.3f} us/launch")
     ceiling = copy_ceiling_gbs(torch)
     same = copy_same_bytes(torch, hr["algo_bytes_per_launch"], cyc)
     log(f"copy of the headline's bytes: {same['us']} us, {same['gbs']} GB/s")
@@ -418,6 +460,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": hr["gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": hr["frac_of_hbm_peak"],
                      "traffic": traffic_for(head), "kernel": hr["kernel"]},
+        "graph_replay": hr.get("graph_replay"),
         "kernels": {k: v for k, v in results.items() if k != head},
         "copy_ceiling_gbs": round(ceiling, 1),
         "copy_same_bytes": same,
