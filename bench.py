@@ -129,6 +129,15 @@ def graph_replay_us(torch, ra, case, n_sets: int, reps: int = 3) -> float:
     return ms * 1e3
 
 
+def launch_floor_us(torch, ra, W, dev, cyc) -> float:
+    """Per-launch time of the smallest in-place launch (one row of 64 fp32 elements, one
+    workgroup) issued back to back: the cost of a launch itself on this GPU and runtime."""
+    case = W.inplace_case("floor", 1, 1, 1, 64, torch.float32, torch.float32, [0, 64], seed=7,
+                          device=dev)
+    calls = inplace_calls(ra, case, 1)
+    return time_launches(torch, calls, 200, 20, cyc) * 1e3
+
+
 def copy_ceiling_gbs(torch, nbytes=1 << 30) -> float:
     """Device-to-device copy bandwidth (read + write bytes) at a footprint well above the
     Infinity Cache: the attainable-bandwidth context for the kernels."""
@@ -436,6 +445,10 @@ def main() -> int:
         hr["graph_replay"] = {"us_per_launch": round(gus, 3),
                               "gbs": round(cases[head].algo_bytes / gus / 1e3, 1)}
         log(f"{head} replayed from one HIP graph: {gus:.3f} us/launch")
+    floor_us = launch_floor_us(torch, ra, W, dev, cyc)
+    ideal_us = hr["algo_bytes_per_launch"] / (HBM_PEAK_GBS * 1e3)
+    log(f"launch floor {floor_us:.3f} us: the headline could reach at most "
+        f"{100 * ideal_us / (floor_us + ideal_us):.1f}% of peak per launch")
     ceiling = copy_ceiling_gbs(torch)
     same = copy_same_bytes(torch, hr["algo_bytes_per_launch"], cyc)
     log(f"copy of the headline's bytes: {same['us']} us, {same['gbs']} GB/s")
@@ -461,6 +474,10 @@ def main() -> int:
                      "unit": "GB/s", "frac": hr["frac_of_hbm_peak"],
                      "traffic": traffic_for(head), "kernel": hr["kernel"]},
         "graph_replay": hr.get("graph_replay"),
+        # the cost of one launch (a one-row launch back to back) and what it leaves of the peak
+        # for the headline's bytes: floor + bytes at the full 8 TB/s
+        "launch_floor": {"us": round(floor_us, 3),
+                         "headline_frac_ceiling": round(ideal_us / (floor_us + ideal_us), 4)},
         "kernels": {k: v for k, v in results.items() if k != head},
         "copy_ceiling_gbs": round(ceiling, 1),
         "copy_same_bytes": same,
