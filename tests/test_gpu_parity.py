@@ -657,6 +657,28 @@ def test_cache_positions_rewritten_between_calls():
                       True, second[0], second[1], f"positions after rewrite, m={m}")
 
 
+def test_cache_query_beyond_2e31_elements():
+    """A query of more than 2^31 elements (2^21 + 7 tokens of 8 heads of 128, bf16, 4.3 GB):
+    row offsets past 32 bits on the wavefront kernel.  The rotated outputs of the last 1024
+    tokens and of 3072 seeded sample tokens are compared with the oracle."""
+    T, nq, nk, H = (1 << 21) + 7, 8, 1, 128
+    assert T * nq * H > (1 << 31)
+    g = W.generator(2031, DEV)
+    q = W.randn((T, nq * H), torch.bfloat16, g)
+    k = W.randn((T, nk * H), torch.bfloat16, g)
+    cache = W.cos_sin_cache(4096, H, torch.bfloat16).to(DEV)
+    pos = torch.randint(0, 4096, (T,), generator=g, device=DEV)
+    qo, ko = ra.rope_with_cos_sin_cache(pos, q, k, cache, None, H, True)
+    torch.cuda.synchronize()
+    idx = torch.cat([torch.randperm(T - 1024, generator=torch.Generator().manual_seed(31))[:3072],
+                     torch.arange(T - 1024, T)]).sort().values
+    gi = idx.to(DEV)
+    compare_cache(pos[gi].cpu(), q[gi].cpu(), k[gi].cpu(), cache.cpu(), None, H, True,
+                  qo[gi].cpu(), ko[gi].cpu(), "query beyond 2^31 elements")
+    del q, k, qo, ko
+    torch.cuda.empty_cache()
+
+
 def test_cache_deterministic():
     case = W.cache_mrope(DEV)
     a = run_cache_case(case)
