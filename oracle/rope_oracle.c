@@ -47,6 +47,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* Status values printed in [IPRM §返回值与错误码] (error-code table). */
@@ -55,6 +56,8 @@
 #define ORO_ERR_PARAM_INVALID 161002
 /* Oracle-only: the call is outside the contract (a position outside the cache). */
 #define ORO_ERR_OUTSIDE_CONTRACT (-1)
+/* Oracle-only: the host could not give the oracle its per-call row buffers. */
+#define ORO_ERR_OUT_OF_MEMORY (-2)
 
 /* dtype codes of the descriptor (the same numbering as the library's interface, since the
  * harness hands the same descriptions to both). */
@@ -636,8 +639,16 @@ static int cos_sin_cache(const oro_tensor *positions, const oro_tensor *query_in
 
   const int64_t half = rd / 2;
   const int64_t nq = query_in->shape[1] / head_size, nk = key_in->shape[1] / head_size;
-  float cs_cos[4096], cs_sin[4096]; /* rd/2 <= headSize/2; headSize is bounded below */
-  if (half > 4096) return fail(ORO_ERR_PARAM_INVALID, "oracle limit: rotaryDim above 8192");
+  /* one token's gathered cos and sin (rotaryDim/2 each) and one head's rotated inputs
+   * (rotaryDim): the pages bound rotaryDim only by headSize, so these are sized per call */
+  float *cs_cos = malloc((size_t)rd * sizeof(float));
+  float *vin = malloc((size_t)rd * sizeof(float));
+  if (!cs_cos || !vin) {
+    free(cs_cos);
+    free(vin);
+    return fail(ORO_ERR_OUT_OF_MEMORY, "oracle: no host memory for one row of rotaryDim");
+  }
+  float *cs_sin = cs_cos + half;
 
   for (int64_t t = 0; t < T; ++t) {
     /* gather the cache row(s) and split into cos | sin; mrope stitches the
@@ -675,7 +686,6 @@ static int cos_sin_cache(const oro_tensor *positions, const oro_tensor *query_in
         int64_t ob = t * (nh * head_size) + h * head_size;   /* output head base  */
         /* the rotated part: read every input of the head first, since an exactly aliased
          * output may overwrite it */
-        float vin[8192];
         for (int64_t j = 0; j < rd; ++j) vin[j] = load_f32(in, ib + j);
         for (int64_t i = 0; i < half; ++i) {
           int64_t ja, jb;
@@ -699,6 +709,8 @@ static int cos_sin_cache(const oro_tensor *positions, const oro_tensor *query_in
       }
     }
   }
+  free(cs_cos);
+  free(vin);
   return ORO_OK;
 }
 

@@ -9,6 +9,7 @@ disabled (so the compiler never emits packed fp32 adds/multiplies).
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 
@@ -20,6 +21,11 @@ LIB_PATH = os.path.join(HERE, "librope_amd.so")
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, "rope_plan.cpp"), os.path.join(CSRC, "rope_kernels.hip")]
+# Everything the library is built from; its digest is written beside the library (STAMP_PATH)
+# so that a library older than its sources is noticed before it is tested.
+BUILD_INPUTS = SOURCES + [os.path.join(CSRC, "rope_plan.h"), os.path.join(INCLUDE, "rope.h"),
+                          os.path.abspath(__file__)]
+STAMP_PATH = LIB_PATH + ".sources"
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC",
@@ -53,6 +59,24 @@ def bundled_targets(path: str) -> list[str]:
     return out
 
 
+def source_digest() -> str:
+    """sha256 of the library's build inputs (names and contents)."""
+    h = hashlib.sha256()
+    for path in BUILD_INPUTS:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def up_to_date() -> bool:
+    """The library exists and was built from the sources as they are now."""
+    if not (os.path.exists(LIB_PATH) and os.path.exists(STAMP_PATH)):
+        return False
+    with open(STAMP_PATH) as f:
+        return f.read().strip() == source_digest()
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd))
@@ -77,7 +101,10 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     devices = [t for t in bundled_targets(tmp) if not t.startswith("host-")]
     if devices != [f"hipv4-amdgcn-amd-amdhsa--{ARCH}"]:
         raise RuntimeError(f"built library carries device code for {devices}, expected {ARCH}")
+    digest = source_digest()
     os.replace(tmp, LIB_PATH)
+    with open(STAMP_PATH, "w") as f:
+        f.write(digest + "\n")
     return LIB_PATH
 
 

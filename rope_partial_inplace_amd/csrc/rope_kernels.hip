@@ -637,7 +637,27 @@ __device__ inline void cache_load_pass(const CachePlan &p, int64_t t0, uint32_t 
   }
 }
 
-template <typename T, bool NEOX, int V, bool VEC, int K, int NV>
+// DIRECT: BYTES bytes of a token's cos or sin straight from its cache row (16-byte aligned
+// rows: one load; otherwise element by element).
+template <typename T, int BYTES>
+__device__ inline Words<BYTES> cache_row_words(const T *row, bool vec) {
+  Words<BYTES> r;
+  if (vec) {
+    load_words<BYTES, false>(row, r);
+  } else {
+    union {
+      Words<BYTES> w;
+      typename Io<T>::raw e[BYTES / int(sizeof(T))];
+    } u;
+    const typename Io<T>::raw *q = reinterpret_cast<const typename Io<T>::raw *>(row);
+#pragma unroll
+    for (int j = 0; j < BYTES / int(sizeof(T)); ++j) u.e[j] = q[j];
+    r = u.w;
+  }
+  return r;
+}
+
+template <typename T, bool NEOX, int V, bool VEC, int K, int NV, bool DIRECT>
 __device__ inline void cache_store_pass(const CachePlan &p, int64_t t0, const T *cs_tile,
                                         const CacheItems<T, V, VEC, K, NV> &w) {
   const int64_t rd = p.rd, half = rd / 2;
@@ -651,15 +671,29 @@ __device__ inline void cache_store_pass(const CachePlan &p, int64_t t0, const T 
       if constexpr (NV == 2) store_raw<T, V, VEC, true>(out, c.out_row + c.off_b, w.v[k][NV - 1]);
       continue;
     }
-    // the token's cos|sin row, kept in LDS in the cache's own element type
-    const T *cs = cs_tile + int64_t(c.tl) * rd;
+    // the token's cos|sin row: kept in LDS in the cache's own element type, or (DIRECT, rope
+    // mode) read from the cache row of the token's position
+    const T *cs;
+    if constexpr (DIRECT)
+      cs = static_cast<const T *>(p.cache) +
+           clamp_position(p, p.positions[(t0 + c.tl) * p.pos_stride_tok]) * p.cache_stride;
+    else
+      cs = cs_tile + int64_t(c.tl) * rd;
     constexpr int PW = Io<T>::kPerWord;
     if constexpr (NEOX) {
       // [RSCC §rotate_half（GPT-NeoX style）旋转模式]: x1 = a (first half), x2 = b.  Worked one
       // 32-bit word (1 or 2 elements) of each vector at a time to keep few values live.
       const int64_t ci = int64_t(c.u) * V;
-      const u32x4 cw = *reinterpret_cast<const u32x4 *>(cs + ci);
-      const u32x4 sw = *reinterpret_cast<const u32x4 *>(cs + half + ci);
+      u32x4 cw, sw;
+      if constexpr (DIRECT) {
+        const Words<16> cr = cache_row_words<T, 16>(cs + ci, p.cache_vec);
+        const Words<16> sr = cache_row_words<T, 16>(cs + half + ci, p.cache_vec);
+        cw = u32x4{cr.w[0], cr.w[1], cr.w[2], cr.w[3]};
+        sw = u32x4{sr.w[0], sr.w[1], sr.w[2], sr.w[3]};
+      } else {
+        cw = *reinterpret_cast<const u32x4 *>(cs + ci);
+        sw = *reinterpret_cast<const u32x4 *>(cs + half + ci);
+      }
       RawN<T, V, VEC> oa, ob;
 #pragma unroll
       for (int q = 0; q < V / PW; ++q) {
@@ -684,8 +718,16 @@ __device__ inline void cache_store_pass(const CachePlan &p, int64_t t0, const T 
       float a[V], ya[V], cv[V / 2], sv[V / 2];
       raw_to_float<T, V, VEC>(w.v[k][0], a);
       const int64_t ca = int64_t(c.u) * (V / 2);
-      const u32x2 cw = *reinterpret_cast<const u32x2 *>(cs + ca);
-      const u32x2 sw = *reinterpret_cast<const u32x2 *>(cs + half + ca);
+      u32x2 cw, sw;
+      if constexpr (DIRECT) {
+        const Words<8> cr = cache_row_words<T, 8>(cs + ca, p.cache_vec);
+        const Words<8> sr = cache_row_words<T, 8>(cs + half + ca, p.cache_vec);
+        cw = u32x2{cr.w[0], cr.w[1]};
+        sw = u32x2{sr.w[0], sr.w[1]};
+      } else {
+        cw = *reinterpret_cast<const u32x2 *>(cs + ca);
+        sw = *reinterpret_cast<const u32x2 *>(cs + half + ca);
+      }
       Io<T>::word_to_floats(cw.x, cv);
       Io<T>::word_to_floats(cw.y, cv + PW);
       Io<T>::word_to_floats(sw.x, sv);
@@ -717,9 +759,12 @@ __device__ inline void multi_rows(const CachePlan &p, uint32_t i0, int *row) {
 }
 
 // MULTI: the plan's stitched cos/sin has chunks drawing on several position rows
-// (CachePlan::multi_row); otherwise every staging chunk comes from one row.
-template <typename T, bool NEOX, bool VEC, int K, bool MULTI>
+// (CachePlan::multi_row); otherwise every staging chunk comes from one row.  DIRECT (rope mode
+// with a cos|sin row too long for the LDS tile, CachePlan::cs_direct): nothing is staged; each
+// item reads its cos/sin chunk from the cache row of its token's position.
+template <typename T, bool NEOX, bool VEC, int K, bool MULTI, bool DIRECT>
 __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p) {
+  static_assert(!(DIRECT && MULTI), "direct cos/sin reads are a rope-mode path");
   // [tile_tokens][rd] elements of T: the gathered cos (rd/2) then sin (rd/2) of each token
   extern __shared__ u32x4 cs_lds[];
   T *cs_tile = reinterpret_cast<T *>(cs_lds);
@@ -746,7 +791,7 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
     // (Multi-row chunks load their positions at staging time: holding three positions
     // across the q/k loads costs more registers than the early load saves.)
     int64_t first_pos = 0;
-    if (!MULTI && threadIdx.x < stage_items) {
+    if (!MULTI && !DIRECT && threadIdx.x < stage_items) {
       const uint32_t tl = fdiv(p.div_stage, threadIdx.x);
       const uint32_t i0 = (threadIdx.x - tl * p.stage_chunks) * uint32_t(V);
       const int sec = p.mrope ? mrope_section_of(p, i0) : 0;
@@ -764,7 +809,7 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
     // loads the row of the chunk's first element instead (lines already being fetched) and
     // writes nothing.  Loads are unconditional: loads under divergent branches make the
     // compiler wait for every outstanding load at each join.
-    bool staged = false;
+    bool staged = DIRECT;
     if constexpr (MULTI) {
       if (p.cache_vec) {
         staged = true;
@@ -828,16 +873,16 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
         *reinterpret_cast<u32x4 *>(dst + half) = ld16<false>(src + half);
       }
     }
-    __syncthreads();
+    if constexpr (!DIRECT) __syncthreads();
 
     // ---- rotate the first rd of every q head then k head, copy the rest ----
     for (uint32_t pbase = 0;;) {
-      cache_store_pass<T, NEOX, V, VEC, K, NV>(p, t0, cs_tile, w);
+      cache_store_pass<T, NEOX, V, VEC, K, NV, DIRECT>(p, t0, cs_tile, w);
       pbase += pass;
       if (pbase >= tile_items) break;
       cache_load_pass<T, NEOX, V, VEC, K, NV>(p, t0, tile_items, pbase, w);
     }
-    __syncthreads();  // the LDS tile is rewritten by the next tile
+    if constexpr (!DIRECT) __syncthreads();  // the LDS tile is rewritten by the next tile
   }
 }
 
@@ -1133,14 +1178,14 @@ const void *pick_inplace_dtype(const InplacePlan &p) {
                            : pick_inplace<__bf16, __bf16, BWD, HALF>(p);
 }
 
-template <typename T, bool MULTI>
+template <typename T, bool MULTI, bool DIRECT>
 const void *pick_cache_rows(bool neox, bool vec) {
   constexpr int KN = kNeoxItemsPerLane, KJ = kGptjItemsPerLane;
-  if (neox)
-    return vec ? reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, true, true, KN, MULTI>)
-               : reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, true, false, KN, MULTI>);
-  return vec ? reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, false, true, KJ, MULTI>)
-             : reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, false, false, KJ, MULTI>);
+#define ROPE_K2(NX, VE, KK) \
+  reinterpret_cast<const void *>(&cos_sin_cache_kernel<T, NX, VE, KK, MULTI, DIRECT>)
+  if (neox) return vec ? ROPE_K2(true, true, KN) : ROPE_K2(true, false, KN);
+  return vec ? ROPE_K2(false, true, KJ) : ROPE_K2(false, false, KJ);
+#undef ROPE_K2
 }
 
 template <typename T>
@@ -1157,8 +1202,9 @@ const void *pick_cache(const CachePlan &p) {
     return p.multi_row ? ROPE_K2W(false, true, false, false) : ROPE_K2W(false, false, false, false);
 #undef ROPE_K2W
   }
-  return p.multi_row ? pick_cache_rows<T, true>(p.neox, p.vector_io)
-                     : pick_cache_rows<T, false>(p.neox, p.vector_io);
+  if (p.cs_direct) return pick_cache_rows<T, false, true>(p.neox, p.vector_io);
+  return p.multi_row ? pick_cache_rows<T, true, false>(p.neox, p.vector_io)
+                     : pick_cache_rows<T, false, false>(p.neox, p.vector_io);
 }
 
 }  // namespace
@@ -1236,7 +1282,7 @@ ROPE_API int rope_with_cos_sin_cache_v2(const rope_tensor *positions, const rope
     return launch(fn, (plan.waves + kWaveBlock / 64 - 1) / (kWaveBlock / 64), kWaveBlock, 0,
                   stream, &plan);
   const size_t esize = plan.dt == ROPE_F32 ? 4 : 2;
-  const size_t lds = size_t(plan.tile_tokens) * size_t(plan.rd) * esize;
+  const size_t lds = plan.cs_direct ? 0 : size_t(plan.tile_tokens) * size_t(plan.rd) * esize;
   return launch(fn, plan.tiles, kCacheBlock, lds, stream, &plan);
 }
 

@@ -445,8 +445,12 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
   }
   tt = std::min<int64_t>(tt, T);
   if (T <= kOneRoundCacheTiles) tt = 1;
-  if (rd * 4 * tt > 64 * 1024)
-    return reject(err, ROPE_ERR_PARAM_INVALID, "rotaryDim too large for the LDS tile (max 16384)");
+  // A token's cos|sin row of more than 16384 elements does not fit the 64 KiB LDS tile: such
+  // plans stage nothing and read each item's cos/sin from the cache row directly.  Only rope
+  // mode gets there (every mrope list has rotaryDim = 2 * sum <= 128).
+  p.cs_direct = rd * 4 * tt > 64 * 1024;
+  if (p.cs_direct && mrope)
+    return reject(err, ROPE_ERR_PARAM_INVALID, "internal: mrope plan with a direct cos/sin read");
   p.tile_tokens = uint32_t(tt);
   p.tiles = (T + tt - 1) / tt;
   // Tapered end: a workgroup lives for a few loaded round trips, and the last round drains

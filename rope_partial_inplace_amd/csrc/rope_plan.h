@@ -104,6 +104,9 @@ struct CachePlan {
   // every later tile holds one token, so the workgroups of the last round are short.
   int64_t big_tiles = 0, big_tokens = 0;
   bool cache_vec = false;       // cache rows can be read with 16-byte loads
+  // rope mode with rotaryDim > 16384 (a cos|sin row beyond the 64 KiB LDS tile): no staging;
+  // every item reads its cos/sin chunk from its token's cache row
+  bool cs_direct = false;
   uint32_t stage_chunks = 0;    // (rd/2) / vec: vector chunks of one cos (or sin) half-row
   FastDiv div_units, div_ipt, div_stage;
   // Wavefront path (cos_sin_cache_wave_kernel): one wavefront per (token, group of heads), no

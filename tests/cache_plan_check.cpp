@@ -234,7 +234,7 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
   const int64_t qs = nq * H + q_pad;
   const rope_tensor q = t2(0x30000000, dt, T, nq * H, qs);
   const rope_tensor k = t2(0x50000000, dt, T, nk * H, nk * H);
-  const rope_tensor c = t2(0x70000000, dt, 4096, rd, rd);
+  const rope_tensor c = t2(0x70000000, dt, 1024, rd, rd);  // below 0x80000000 up to rd 65536
   const rope_tensor qo = t2(0x80000000, dt, T, nq * H, nq * H);
   const rope_tensor ko = t2(0xA0000000, dt, T, nk * H, nk * H);
   CachePlan p;
@@ -265,10 +265,16 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
       CHECK(tok_seen[size_t(t)] == 0, "token %lld in two tiles", (long long)t);
       tok_seen[size_t(t)] = 1;
     }
+    // direct plans (rope mode, a cos|sin row of more than 16384 elements): nothing is staged,
+    // each item reads its pair indices from the cache row (checked with the items below)
+    CHECK(p.cs_direct == (rd > 16384), "direct cos/sin reads %d for rotaryDim %lld",
+          int(p.cs_direct), (long long)rd);
+    CHECK(!p.cs_direct || (m == 0 && p.tile_tokens == 1 && !p.wave),
+          "direct plan with %lld position rows, %u-token tiles", (long long)m, p.tile_tokens);
     // staging: one lane per chunk, or for multi-row plans (16-byte cache rows) one lane per
     // (chunk, row of rows 0..2) writing only the elements assigned to its row
-    std::vector<uint8_t> lds(size_t(lds_elems), 0);
-    const uint32_t stage_items = uint32_t(ntok) * p.stage_chunks;
+    std::vector<uint8_t> lds(size_t(p.cs_direct ? 0 : lds_elems), 0);
+    const uint32_t stage_items = p.cs_direct ? 0u : uint32_t(ntok) * p.stage_chunks;
     const bool per_row = p.multi_row && p.cache_vec;
     CHECK(!p.multi_row || m == 3, "multi-row plan with %lld position rows", (long long)m);
     for (uint32_t idx = 0; idx < stage_items * (per_row ? 3u : 1u); ++idx) {
@@ -294,7 +300,8 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
         }
       }
     }
-    for (int64_t i = 0; i < ntok * rd; ++i) CHECK(lds[size_t(i)] == 1, "LDS %lld unset", (long long)i);
+    for (int64_t i = 0; !p.cs_direct && i < ntok * rd; ++i)
+      CHECK(lds[size_t(i)] == 1, "LDS %lld unset", (long long)i);
     // items
     const uint32_t tile_items = uint32_t(ntok) * p.items_per_token;
     for (uint32_t it = 0; it < tile_items; ++it) {
@@ -406,6 +413,13 @@ int main(int argc, char **argv) {
       }
       if (!walk(dt, neox, 5, 3, 1, 128, 128, {16, 24, 24}, 0, 0, 2)) return 1;
       ++plans;
+      // rotaryDim at the LDS tile's limit (16384) and past it (direct cos/sin reads)
+      const int64_t align = dt == ROPE_F32 ? 16 : 32;
+      for (int64_t rd : {int64_t(16384), 16384 + align, int64_t(24576)})
+        for (int64_t extra : {int64_t(0), align}) {
+          if (!walk(dt, neox, 3, 2, 1, rd + extra, rd, {}, 0, 0)) return 1;
+          ++plans;
+        }
     }
   if (wave_plans == 0 || wave_plans == g_walked || xch_plans == 0 || lin_plans == 0) {
     std::printf("FAIL: %d of %d plans take the wavefront path (%d exchange, %d one-vector "

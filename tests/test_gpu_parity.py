@@ -64,21 +64,24 @@ def test_inplace_configs_full(cfg):
                   case.rotary_mode)
 
 
-def test_inplace_f32_scaled_sampled_rows_and_pair_norms():
-    """The 768 MiB fp32 workload [1,524288,2,64]: 4096 seeded sample positions (both heads)
-    compared with the oracle, and for every pair of the whole launch the norm kept: the
-    tables hold cos and sin of one angle per pair, so |(y0, y1)|^2 = |(x0, x1)|^2 up to the
-    fp32 roundings of the tables and the four products (about 11 units of 2^-24 in all)."""
+def test_inplace_f32_scaled_full_and_pair_norms():
+    """The 768 MiB fp32 workload [1,524288,2,64], the launch the benchmark times: every
+    element compared with the oracle (bit for bit, and within the fp32 bound of the oracle's
+    float64 twin), and for every pair the norm kept: the tables hold cos and sin of one angle
+    per pair, so |(y0, y1)|^2 = |(x0, x1)|^2 up to the fp32 roundings of the tables and the
+    four products (about 11 units of 2^-24 in all)."""
     case = W.CONFIGS["inplace_f32_1x524288x2x64"](DEV)
     x = case.x
     before = x.clone()
     ra.rope_partial_inplace(x, case.cos, case.sin, 1, case.partial_slice)
     torch.cuda.synchronize()
     S = x.shape[1]
-    idx = torch.randperm(S, generator=torch.Generator().manual_seed(45))[:4096].sort().values
-    gi = idx.to(DEV)
-    check_inplace(before[:, gi].cpu(), x[:, gi], case.cos[:, gi], case.sin[:, gi],
-                  case.partial_slice, case.name + " sampled positions")
+    ref = before.cpu()
+    assert oracle.rope_partial_inplace(ref, case.cos.cpu(), case.sin.cpu(), 1,
+                                       case.partial_slice)[0] == 0
+    check_bits_equal(x.cpu(), ref, case.name + " all positions")
+    check_inplace(before.cpu(), x, case.cos, case.sin, case.partial_slice,
+                  case.name + " all positions")
     for h in range(0, S, 1 << 17):  # fp64 norms in slices of the sequence
         a = before[:, h:h + (1 << 17)].double().view(-1, 2)
         y = x[:, h:h + (1 << 17)].double().view(-1, 2)
@@ -221,7 +224,8 @@ def test_cache_subnormal_inputs(dt):
 @pytest.mark.parametrize("cfg", ["inplace_bf16_8x4096x1x576_s512", "inplace_f32_1x16x2x64",
                                  "inplace_half_bf16_8x4096x1x576_s512",
                                  "inplace_heads_bf16_4x2048x32x192_s128_bs1d",
-                                 "cache_rope_neox_bf16_t8192", "cache_mrope_neox_bf16_t16384",
+                                 "cache_rope_neox_bf16_t8192", "cache_rope_gptj_f16_t32768_rd64",
+                                 "cache_mrope_neox_bf16_t16384",
                                  "cache_mrope_interleaved_neox_bf16_t16384"])
 def test_configs_bit_identical_to_oracle(cfg):
     """Beyond the tolerances: the kernels perform the oracle's float32 operations in the
@@ -310,7 +314,8 @@ def compare_cache_case(case, qo, ko, what=None):
                   what or case.name, case.cache_mode)
 
 
-@pytest.mark.parametrize("cfg", ["cache_rope_neox_bf16_t8192", "cache_mrope_neox_bf16_t16384",
+@pytest.mark.parametrize("cfg", ["cache_rope_neox_bf16_t8192", "cache_rope_gptj_f16_t32768_rd64",
+                                 "cache_mrope_neox_bf16_t16384",
                                  "cache_mrope_interleaved_neox_bf16_t16384"])
 def test_cache_configs_full(cfg):
     case = W.CONFIGS[cfg](DEV)
@@ -341,20 +346,40 @@ def test_cache_long_launch_many_tiles(dt, neox, mrope):
                   f"long launch {dt} neox={neox} mrope={mrope}")
 
 
-def test_cache_config_c4_sampled_tokens():
-    """The 1 GiB GPT-J workload: every token's pass-through half is checked on the GPU; the
-    rotated half is compared with the oracle on 4096 seeded sample tokens."""
-    case = W.cache_rope_gptj_partial(DEV)
+@pytest.mark.parametrize("neox", [True, False], ids=["neox", "gptj"])
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=lambda d: str(d).split(".")[-1])
+@pytest.mark.parametrize("rd,extra", [(16384, 0), (16384, 64), ("past", 0), (24576, 32)],
+                         ids=["lds_limit", "lds_limit_tail", "direct", "direct_tail"])
+def test_cache_rotary_dim_at_and_past_the_lds_tile(rd, extra, dt, neox):
+    """[RSCC §约束说明] bounds rotaryDim only by headSize and 64-byte alignment.  16384 is the
+    longest cos|sin row the tile kernel stages in LDS (64 KiB for float32); one 64-byte step
+    past it, and at 24576, each item reads its cos/sin straight from the cache row.  Heads with
+    and without a pass-through tail, every token against the oracle."""
+    align = 64 // torch.tensor([], dtype=dt).element_size()
+    rd = 16384 + align if rd == "past" else rd
+    H = rd + extra
+    case = W.cache_case("longrd", 9, 2, 1, H, rd, dt, neox, 40, seed=rd + extra, device=DEV)
     qo, ko = run_cache_case(case)
-    rd, H = case.cache.shape[1], case.head_size
-    T = case.tokens
-    for got, inp in ((qo, case.query), (ko, case.key)):
-        assert torch.equal(got.view(T, -1, H)[..., rd:].view(torch.int16),
-                           inp.view(T, -1, H)[..., rd:].view(torch.int16))
-    idx = torch.randperm(T, generator=torch.Generator().manual_seed(44))[:4096].sort().values
-    gi = idx.to(DEV)
-    compare_cache(case.positions[gi].cpu(), case.query[gi].cpu(), case.key[gi].cpu(),
-                  case.cache.cpu(), None, H, False, qo[gi].cpu(), ko[gi].cpu(), case.name)
+    compare_cache_case(case, qo, ko, f"rd {rd} H {H} {dt} neox={neox}")
+
+
+def test_cache_long_rotary_dim_unaligned_rows():
+    """The direct cos/sin reads on rows that are not 16-byte aligned (cache and query one
+    element off): element-wise loads of the cache row and of q."""
+    rd, H, T = 16416, 16448, 5
+    g = W.generator(31, DEV)
+    cbuf = W.cos_sin_cache(12, rd, torch.bfloat16).to(DEV).reshape(-1)
+    cache = torch.cat([cbuf[:1], cbuf]).narrow(0, 1, cbuf.numel()).view(12, rd)
+    qbuf = W.randn((T * 2 * H + 1,), torch.bfloat16, g)
+    q = qbuf.narrow(0, 1, T * 2 * H).view(T, 2 * H)
+    k = W.randn((T, H), torch.bfloat16, g)
+    pos = torch.tensor([11, 0, 5, 5, 3], device=DEV)
+    assert cache.data_ptr() % 16 and q.data_ptr() % 16
+    for neox in (True, False):
+        qo, ko = ra.rope_with_cos_sin_cache(pos, q, k, cache, None, H, neox)
+        torch.cuda.synchronize()
+        compare_cache(pos.cpu(), q.cpu(), k.cpu(), cache.cpu(), None, H, neox, qo.cpu(),
+                      ko.cpu(), f"unaligned rd {rd} neox={neox}")
 
 
 HEADS = [(torch.bfloat16, 32, 32), (torch.bfloat16, 64, 32), (torch.bfloat16, 96, 96),

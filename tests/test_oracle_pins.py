@@ -304,6 +304,53 @@ def test_cache_matches_complex_multiplication(neox, mrope):
         np.testing.assert_allclose(got.reshape(T, -1, H), exp, rtol=1e-13, atol=1e-13)
 
 
+@pytest.mark.parametrize("neox", [True, False])
+@pytest.mark.parametrize("rd,extra", [(16384, 0), (16416, 32), (24576, 0)])
+def test_cache_long_rotary_dim_matches_complex_multiplication(neox, rd, extra):
+    """[RSCC §约束说明] bounds rotaryDim only by headSize and 64-byte alignment, so the oracle
+    evaluates any length: rotaryDim of 16384 and beyond, checked as above against NumPy complex
+    multiplication of every pair (float64 twin), the float32 outputs within the error bound
+    of their twin, and the head's tail copied bit for bit."""
+    T, nq, nk = 3, 2, 1
+    H = rd + extra
+    g = torch.Generator().manual_seed(rd + extra + int(neox))
+    q = torch.randn(T, nq * H, generator=g)
+    k = torch.randn(T, nk * H, generator=g)
+    cache = torch.randn(7, rd, generator=g)
+    pos = torch.tensor([6, 0, 3])
+    qo, ko, q64, k64 = run_cache(pos, q, k, cache, None, H, neox, twin=True)
+    C = f64(cache)
+    w = C[pos.numpy(), : rd // 2] + 1j * C[pos.numpy(), rd // 2:]
+    for inp, out, got in ((q, qo, q64), (k, ko, k64)):
+        X = f64(inp).reshape(T, -1, H)
+        rot = X[..., :rd]
+        z = (rot[..., : rd // 2] + 1j * rot[..., rd // 2:]) if neox else \
+            (rot[..., 0::2] + 1j * rot[..., 1::2])
+        r = z * w[:, None, :]
+        exp = X.copy()
+        if neox:
+            exp[..., : rd // 2], exp[..., rd // 2: rd] = r.real, r.imag
+        else:
+            exp[..., 0:rd:2], exp[..., 1:rd:2] = r.real, r.imag
+        np.testing.assert_allclose(got.reshape(T, -1, H), exp, rtol=1e-13, atol=1e-13)
+        o = f64(out).reshape(T, -1, H)
+        # each output is two float32 products and one sum: within 2 ulp of the term sizes
+        # (|x1*c| + |x2*s|, the same for both outputs of a pair)
+        if neox:
+            terms = np.abs(rot[..., : rd // 2]) * np.abs(w.real)[:, None] + \
+                np.abs(rot[..., rd // 2:]) * np.abs(w.imag)[:, None]
+            terms = np.concatenate([terms, np.abs(rot[..., : rd // 2]) * np.abs(w.imag)[:, None]
+                                    + np.abs(rot[..., rd // 2:]) * np.abs(w.real)[:, None]], -1)
+        else:
+            a, b = np.abs(rot[..., 0::2]), np.abs(rot[..., 1::2])
+            terms = np.empty_like(rot)
+            terms[..., 0::2] = a * np.abs(w.real)[:, None] + b * np.abs(w.imag)[:, None]
+            terms[..., 1::2] = b * np.abs(w.real)[:, None] + a * np.abs(w.imag)[:, None]
+        assert np.all(np.abs(o[..., :rd] - exp[..., :rd]) <= 2.0 ** -22 * terms + 1e-45)
+        assert np.array_equal(raw_bits(out).reshape(T, -1, H)[..., rd:],
+                              raw_bits(inp).reshape(T, -1, H)[..., rd:])
+
+
 def test_relative_position_property():
     """RoPE's defining property: <R(p) q, R(p') k> depends on p - p' only.  Tables hold
     exact-angle values rounded to float32, so equality holds to float32-table accuracy."""
