@@ -2,26 +2,38 @@
 """Benchmark of the RoPE apply path on one MI355X: achieved HBM GB/s (and fraction of the
 8 TB/s peak) and tokens/s.
 
-One step is one pass of the in-place partial interleave op over one batch of the headline
-workload: bf16 x [8,4096,1,576], slice [512,576), fp32 cos/sin [8,4096,1,64] (32768 tokens).
-The cos/sin-cache kernel is timed the same way on its three workloads (rope NeoX bf16, rope
-GPT-J fp16 with a pass-through half, mrope bf16) and reported in `kernels`.
+One step is one launch of the headline workload, the largest single-GPU configuration: the
+cos/sin-cache op in GPT-J style, fp16, 32768 tokens, q and k [32768, 32*128], rotaryDim 64 of
+headSize 128 (the other 64 dims copied through), cache [65536, 64] (1078 MB per launch).  The
+other configurations (the in-place op on fp32 [1,16,2,64] and on bf16 [8,4096,1,576] with a
+[512,576) slice; the cache op in rope NeoX bf16 and mrope [16,24,24] bf16) and extra workloads
+(the in-place gradient, half mode, the multi-head in-place shape, interleaved mrope stitching,
+a 768 MiB fp32 in-place launch) are timed the same way and reported under `kernels`.
 
 Timing: inputs are resident in HBM; launches cycle over enough copies of the inputs that
-every pass touches >= 2 GiB before a buffer is reused, so that MI355X's 256 MB Infinity
-Cache holds none of a buffer set's lines when it comes round again; the host queues the timed launches behind a short GPU spin so
-that they run back to back, and two HIP events on the launch stream bracket exactly `steps`
-launches.  Rank 0 prints one JSON line on stdout; progress goes to stderr.
+every pass touches >= 2 GiB before a buffer is reused, so that MI355X's 256 MB Infinity Cache
+holds none of a buffer set's lines when it comes round again; the host queues the timed
+launches behind a short GPU spin so that they run back to back, and two HIP events on the
+launch stream bracket exactly `steps` launches.
+
+Beside each kernel: per-launch percentiles (each launch between its own pair of events, in a
+separate pass), the per-launch time of the same launches replayed from one captured HIP graph
+(in-place workloads), a measured ceiling that does the same memory traffic with no arithmetic
+(bench_ceiling.hip: the in-place access pattern, or a dense copy of the cache op's bytes), and
+the CPU oracle's rate on the same workload at 1 thread and on all usable host cores.  One
+JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
 import os
 import platform
 import re
+import subprocess
 import sys
 import time
 
@@ -33,6 +45,16 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 # larger rotations start to add TLB misses of their own.
 MALL_DEFEAT_BYTES = 2 << 30
 KERNEL_SRC = os.path.join(ROOT, "rope_partial_inplace_amd", "csrc", "rope_kernels.hip")
+CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
+CEILING_LIB = os.path.join(ROOT, "libbench_ceiling.so")
+HEADLINE = "cache_rope_gptj_f16_t32768_rd64"
+WORKLOADS = [HEADLINE, "inplace_bf16_8x4096x1x576_s512", "inplace_f32_1x16x2x64",
+             "cache_rope_neox_bf16_t8192", "cache_mrope_neox_bf16_t16384",
+             "inplace_backward_bf16_8x4096x1x576_s512", "cache_mrope_interleaved_neox_bf16_t16384",
+             "inplace_half_bf16_8x4096x1x576_s512", "inplace_heads_bf16_4x2048x32x192_s128_bs1d",
+             "inplace_f32_1x524288x2x64"]
+# copy sizes (bytes read = bytes written) run by --calibrate for scaling the byte counters
+CALIBRATION_BYTES = [12 << 10, 12 << 20, 36 << 20, 128 << 20, 512 << 20]
 
 
 def log(msg: str):
@@ -46,6 +68,43 @@ def kernel_code_hash() -> str:
     with open(KERNEL_SRC, encoding="utf-8") as f:
         lines = [re.sub(r"//.*$", "", line).rstrip() for line in f.read().splitlines()]
     return hashlib.sha256("\n".join(x for x in lines if x).encode()).hexdigest()[:16]
+
+
+def build_ceiling(verbose: bool = False) -> str:
+    """Compile bench_ceiling.hip (gfx950) into libbench_ceiling.so beside this file."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = [os.path.join(rocm, "bin", "hipcc"), "--offload-arch=gfx950", "-mcode-object-version=5",
+           "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall",
+           CEILING_SRC, "-o", CEILING_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(CEILING_LIB + ".tmp", CEILING_LIB)
+    return CEILING_LIB
+
+
+def load_ceiling():
+    if not os.path.exists(CEILING_LIB):
+        raise SystemExit(f"{CEILING_LIB} is missing: build it first (python __graft_entry__.py)")
+    lib = ctypes.CDLL(CEILING_LIB)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.ceiling_copy.argtypes = [vp, vp, i64, vp]
+    lib.ceiling_copy.restype = ctypes.c_int
+    lib.ceiling_rows.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, i64, i64, ctypes.c_int, vp]
+    lib.ceiling_rows.restype = ctypes.c_int
+    return lib
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 # ------------------------------------------------------------------------------------------
@@ -62,18 +121,22 @@ def spin_cycles_per_ms(torch) -> float:
     return 2_000_000 / max(a.elapsed_time(b), 1e-3)
 
 
+def _host_ms_per_launch(torch, calls, n):
+    t0 = time.perf_counter()
+    for i in range(n):
+        calls[i % len(calls)]()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    torch.cuda.synchronize()
+    return ms
+
+
 def time_launches(torch, calls, steps: int, warmup: int, cyc_per_ms: float):
     """Mean GPU time per launch (ms) over `steps` back-to-back launches cycling over calls."""
     n = len(calls)
     for i in range(warmup):
         calls[i % n]()
     torch.cuda.synchronize()
-    # host enqueue cost per launch, to size the spin that hides it
-    t0 = time.perf_counter()
-    for i in range(min(steps, 20)):
-        calls[i % n]()
-    host_ms = (time.perf_counter() - t0) * 1e3 / min(steps, 20)
-    torch.cuda.synchronize()
+    host_ms = _host_ms_per_launch(torch, calls, min(steps, 20))  # sizes the spin
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for attempt in range(3):
         spin_ms = 1.0 + 1.5 * host_ms * steps * (1 + attempt)
@@ -92,18 +155,35 @@ def time_launches(torch, calls, steps: int, warmup: int, cyc_per_ms: float):
     return start.elapsed_time(end) / steps
 
 
-def graph_replay_us(torch, ra, case, n_sets: int, reps: int = 3) -> float:
-    """Per-launch time of the in-place op when its launches over the n_sets buffer sets are
-    captured in one HIP graph and the graph is replayed back to back (inputs rotated as in
-    the stream timing).  Reported beside the stream-launch figure: a serving loop that
-    replays a captured graph pays this per-launch cost instead."""
-    xs = [case.x] + [case.x.clone() for _ in range(n_sets - 1)]
-    cs = [case.cos] + [case.cos.clone() for _ in range(n_sets - 1)]
-    ss = [case.sin] + [case.sin.clone() for _ in range(n_sets - 1)]
+def launch_percentiles(torch, calls, steps: int, cyc_per_ms: float) -> dict:
+    """p10 / median / p90 of single launches, each between its own pair of events (queued
+    behind a spin so they run back to back; the events add a little to short launches)."""
+    n = len(calls)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    host_ms = _host_ms_per_launch(torch, calls, min(steps, 20))
+    torch.cuda._sleep(int((1.0 + 2.0 * host_ms * steps) * cyc_per_ms))
+    ev[0].record()
+    for i in range(steps):
+        calls[i % n]()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    d = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps))
+
+    def q(p):
+        return round(d[min(len(d) - 1, int(p * (len(d) - 1) + 0.5))], 3)
+    return {"p10_us": q(0.1), "median_us": q(0.5), "p90_us": q(0.9), "launches": steps}
+
+
+def graph_replay_us(torch, ra, case, sets, reps: int = 3) -> float:
+    """Per-launch time of the in-place op when its launches over the buffer sets (at least 32
+    launches, cycling over the sets) are captured in one HIP graph and the graph is replayed
+    back to back.  A serving loop that replays a captured graph pays this per-launch cost
+    instead of the stream-launch one."""
     fn = ra.rope_partial_inplace_backward if case.backward else ra.rope_partial_inplace
+    order = [sets[i % len(sets)] for i in range(max(len(sets), 32))]  # >= 32 launches a graph
 
     def launches():
-        for x, c, sn in zip(xs, cs, ss):
+        for x, c, sn in order:
             fn(x, c, sn, case.rotary_mode, case.partial_slice)
 
     side = torch.cuda.Stream()
@@ -123,8 +203,8 @@ def graph_replay_us(torch, ra, case, n_sets: int, reps: int = 3) -> float:
         g.replay()
     end.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / (reps * n_sets)
-    del g, xs, cs, ss
+    ms = start.elapsed_time(end) / (reps * len(order))
+    del g
     torch.cuda.empty_cache()
     return ms * 1e3
 
@@ -138,38 +218,30 @@ def launch_floor_us(torch, ra, W, dev, cyc) -> float:
     return time_launches(torch, calls, 200, 20, cyc) * 1e3
 
 
-def copy_ceiling_gbs(torch, nbytes=1 << 30) -> float:
-    """Device-to-device copy bandwidth (read + write bytes) at a footprint well above the
-    Infinity Cache: the attainable-bandwidth context for the kernels."""
-    a = torch.empty(nbytes // 2, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(10):
-        b.copy_(a)
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / 10
-    return 2 * a.numel() / (ms * 1e-3) / 1e9
-
-
-def copy_same_bytes(torch, moved: int, cyc: float, steps: int = 100) -> dict:
-    """A device-to-device copy (torch's copy_) that reads and writes `moved` bytes in all,
-    timed like the kernels (buffer pairs rotated over MALL_DEFEAT_BYTES, launches back to
-    back): what a plain copy of the headline's bytes achieves at the same footprint."""
-    half = moved // 2
-    n_sets = max(1, math.ceil(MALL_DEFEAT_BYTES / moved))
+def copy_calls(torch, lib, moved: int):
+    """Dense copies (bench_ceiling's copy kernel) that read and write `moved` bytes in all,
+    over enough buffer pairs to rotate through MALL_DEFEAT_BYTES."""
+    half = max(16, (moved // 2) // 16 * 16)
+    n_sets = max(1, math.ceil(MALL_DEFEAT_BYTES / (2 * half)))
     pairs = [(torch.empty(half, dtype=torch.uint8, device="cuda"),
               torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(n_sets)]
-    calls = [(lambda a=a, b=b: b.copy_(a)) for a, b in pairs]
-    ms = time_launches(torch, calls, steps, 10, cyc)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def one(a, b):
+        st = lib.ceiling_copy(b.data_ptr(), a.data_ptr(), half, stream)
+        if st != 0:
+            raise RuntimeError(f"ceiling_copy failed ({st})")
+    return [(lambda a=a, b=b: one(a, b)) for a, b in pairs], pairs, 2 * half
+
+
+def copy_ceiling(torch, lib, moved: int, cyc: float, steps: int = 50) -> dict:
+    calls, pairs, nbytes = copy_calls(torch, lib, moved)
+    ms = time_launches(torch, calls, steps, 5, cyc)
+    out = {"bytes": nbytes, "us": round(ms * 1e3, 3), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "buffer_sets": len(pairs)}
     del calls, pairs
     torch.cuda.empty_cache()
-    return {"bytes": 2 * half, "us": round(ms * 1e3, 3),
-            "gbs": round(2 * half / (ms * 1e-3) / 1e9, 1), "buffer_sets": n_sets}
+    return out
 
 
 # ------------------------------------------------------------------------------------------
@@ -186,15 +258,21 @@ def n_sets_for(algo_bytes: int) -> int:
     return max(1, math.ceil(MALL_DEFEAT_BYTES / algo_bytes))
 
 
-def inplace_calls(ra, case, n_sets):
-    calls = []
+def inplace_sets(case, n_sets):
+    """(x, cos, sin) per buffer set; set 0 is the case's own tensors."""
+    sets = []
     for i in range(n_sets):
-        x = case.x if i == 0 else case.x.clone()
-        c = case.cos if i == 0 else case.cos.clone()
-        s = case.sin if i == 0 else case.sin.clone()
-        calls.append(ra.prepare_partial_inplace(x, c, s, case.rotary_mode, case.partial_slice,
-                                                backward=case.backward))
-    return calls
+        if i == 0:
+            sets.append((case.x, case.cos, case.sin))
+        else:
+            sets.append((case.x.clone(), case.cos.clone(), case.sin.clone()))
+    return sets
+
+
+def inplace_calls(ra, case, n_sets, sets=None):
+    sets = sets or inplace_sets(case, n_sets)
+    return [ra.prepare_partial_inplace(x, c, s, case.rotary_mode, case.partial_slice,
+                                       backward=case.backward) for x, c, s in sets]
 
 
 def cache_calls(ra, torch, case, n_sets):
@@ -208,6 +286,34 @@ def cache_calls(ra, torch, case, n_sets):
                                                    case.head_size, case.is_neox, qo, ko,
                                                    cache_mode=case.cache_mode))
     return calls
+
+
+def inplace_pattern(case) -> dict:
+    """The in-place kernel's memory traffic as bench_ceiling's row pattern: the slice of each
+    x row in lanes of the kernel's x width (16 bytes for the wider of x and cos/sin, so 8 bytes
+    of bf16/f16 x beside float32 cos/sin), and one cos and one sin row per (b, s) (BS1D)."""
+    B, S, N, D = case.x.shape
+    xs, cs = case.x.element_size(), case.cos.element_size()
+    start, end = case.partial_slice if case.partial_slice else (0, D)
+    L = end - start
+    assert tuple(case.cos.shape[:2]) == (B, S) and case.cos.shape[2] in (1, N)
+    per_head = case.cos.shape[2] == N
+    return {"rows": B * S * N, "row_bytes": D * xs, "off": start * xs, "len": L * xs,
+            "lane_bytes": (16 // max(xs, cs)) * xs, "side_bytes": L * cs,
+            "rows_per_side": 1 if per_head else N, "side_stream": int(per_head or N == 1)}
+
+
+def pattern_calls(torch, lib, case, sets):
+    pat = inplace_pattern(case)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def one(x, c, s):
+        st = lib.ceiling_rows(x.data_ptr(), pat["rows"], pat["row_bytes"], pat["off"], pat["len"],
+                              pat["lane_bytes"], c.data_ptr(), s.data_ptr(), pat["side_bytes"],
+                              pat["rows_per_side"], pat["side_stream"], stream)
+        if st != 0:
+            raise RuntimeError(f"ceiling_rows rejected {pat} ({st})")
+    return [(lambda x=x, c=c, s=s: one(x, c, s)) for x, c, s in sets]
 
 
 def describe_case(name, case):
@@ -297,31 +403,52 @@ def size_sweep(torch, ra, W, dev, cyc):
 # CPU baseline: the oracle, as it stands, on the host
 # ------------------------------------------------------------------------------------------
 
-def _oracle_rate(case, threads: int, budget_s: float):
-    """Run the oracle (unchanged, single-threaded C) over the headline batch for ~budget_s
-    from `threads` host threads at once, each on its own block of rows: the batch is viewed
-    as [B*S, 1, N, D] rows (cos/sin alike, which keeps each row's cos/sin row), and thread k
-    rotates rows [k*R/threads, (k+1)*R/threads) again and again.  ctypes releases the GIL
-    during each call.  Returns (bytes/s, tokens/s, passes over the whole batch)."""
-    import threading
+def _host_copies(case):
+    """Host copies of a workload's inputs (outside any timed region) and the function that
+    runs the oracle, unchanged, over token block [lo, hi) of them."""
+    import torch
     import oracle
-    B, S, N, D = case.x.shape
-    x = case.x.cpu().reshape(B * S, 1, N, D).contiguous()
-    c = case.cos.cpu().reshape(B * S, 1, case.cos.shape[2], case.cos.shape[3]).contiguous()
-    sn = case.sin.cpu().reshape(B * S, 1, case.sin.shape[2], case.sin.shape[3]).contiguous()
-    assert case.cos.shape[:2] == (B, S), "the CPU baseline needs per-(b, s) cos/sin rows"
-    rows = B * S
-    edges = [rows * k // threads for k in range(threads + 1)]
+    if hasattr(case, "x"):
+        B, S, N, D = case.x.shape
+        assert tuple(case.cos.shape[:2]) == (B, S), "the CPU baseline needs per-(b, s) cos/sin"
+        x = case.x.cpu().reshape(B * S, 1, N, D).contiguous()
+        c = case.cos.cpu().reshape(B * S, 1, case.cos.shape[2], case.cos.shape[3]).contiguous()
+        s = case.sin.cpu().reshape(B * S, 1, case.sin.shape[2], case.sin.shape[3]).contiguous()
+        fn = oracle.rope_partial_inplace_backward if case.backward else \
+            oracle.rope_partial_inplace
+
+        def run(lo, hi):
+            st, _ = fn(x[lo:hi], c[lo:hi], s[lo:hi], case.rotary_mode, case.partial_slice)
+            assert st == 0, oracle.last_error()
+        return B * S, run
+    pos = case.positions.cpu()
+    q, k, cache = case.query.cpu(), case.key.cpu(), case.cache.cpu()
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+
+    def run(lo, hi):
+        p = pos[lo:hi] if pos.dim() == 1 else pos[:, lo:hi]
+        st, _, _ = oracle.rope_with_cos_sin_cache(p, q[lo:hi], k[lo:hi], cache,
+                                                  case.mrope_section, case.head_size,
+                                                  case.is_neox, qo[lo:hi], ko[lo:hi],
+                                                  cache_mode=case.cache_mode)
+        assert st == 0, oracle.last_error()
+    return case.tokens, run
+
+
+def _oracle_rate(tokens, run, algo_bytes, threads: int, budget_s: float):
+    """Run the oracle (single-threaded C) over the whole batch again and again for about
+    budget_s from `threads` host threads at once, each on its own block of tokens; ctypes
+    releases the GIL during each call.  Returns (bytes/s, tokens/s, passes, seconds)."""
+    import threading
+    edges = [tokens * k // threads for k in range(threads + 1)]
     done = [0.0] * threads
     stop = threading.Event()
 
     def work(k):
         lo, hi = edges[k], edges[k + 1]
-        xs, cs, ss = x[lo:hi], c[lo:hi], sn[lo:hi]
-        while not stop.is_set():
-            st, _ = oracle.rope_partial_inplace(xs, cs, ss, case.rotary_mode, case.partial_slice)
-            assert st == 0, oracle.last_error()
-            done[k] += (hi - lo) / rows
+        while not stop.is_set() and hi > lo:
+            run(lo, hi)
+            done[k] += (hi - lo) / tokens
 
     pool = [threading.Thread(target=work, args=(k,)) for k in range(threads)]
     t0 = time.perf_counter()
@@ -333,57 +460,64 @@ def _oracle_rate(case, threads: int, budget_s: float):
         t.join()
     el = time.perf_counter() - t0
     passes = sum(done)
-    return case.algo_bytes * passes / el, case.tokens * passes / el, passes, el
+    return algo_bytes * passes / el, tokens * passes / el, passes, el
 
 
-def cpu_baseline(case, budget_s: float):
+def cpu_baseline(case, budget_s: float, budget1_s: float) -> dict:
     """The oracle as it stands on the host: on all the cores this process may use (up to 16,
-    the host share of one GPU), plus the single-thread figure."""
+    the host share of one GPU), and on one thread."""
     cores = min(16, len(os.sched_getaffinity(0)))
-    bps, tps, passes, el = _oracle_rate(case, cores, budget_s)
-    bps1, tps1, passes1, el1 = _oracle_rate(case, 1, max(2.0, budget_s / 3))
+    tokens, run = _host_copies(case)
+    bps, tps, passes, el = _oracle_rate(tokens, run, case.algo_bytes, cores, budget_s)
+    bps1, tps1, passes1, el1 = _oracle_rate(tokens, run, case.algo_bytes, 1, budget1_s)
     return {
         "value": round(bps / 1e9, 4),
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"the full headline batch ({case.tokens} tokens) rotated {passes:.1f} times in "
-                   f"{el:.1f} s by the single-threaded C oracle run from {cores} host threads at "
-                   f"once, each on its own block of rows"),
+        "sample": (f"the whole batch ({tokens} tokens) passed {passes:.2f} times in {el:.1f} s "
+                   f"through the single-threaded C oracle, run from {cores} host threads at "
+                   f"once, each on its own block of tokens"),
         "tokens_per_s": round(tps, 1),
         "single_thread": {"value": round(bps1 / 1e9, 4), "unit": "GB/s", "cores": 1,
                           "tokens_per_s": round(tps1, 1),
-                          "sample": f"{passes1:.1f} passes over the batch in {el1:.1f} s"},
-        "host_cpu": platform.processor() or platform.machine(),
-        "host_cores_visible": len(os.sched_getaffinity(0)),
+                          "sample": f"{passes1:.2f} passes over the batch in {el1:.1f} s"},
     }
 
 
 # ------------------------------------------------------------------------------------------
 
+def calibrate(torch, lib, cyc):
+    """Dense copies of known size (CALIBRATION_BYTES read and as many written), 20 each, for
+    scaling the HBM byte counters of a profiled run; prints one JSON line."""
+    out = []
+    for nbytes in CALIBRATION_BYTES:
+        r = copy_ceiling(torch, lib, 2 * nbytes, cyc, steps=20)
+        r["read_bytes"] = r["bytes"] // 2
+        out.append(r)
+        log(f"copy {nbytes} B: {r['us']} us")
+    print(json.dumps({"calibration_copies": out}), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workloads", default=",".join(
-                        ["inplace_bf16_8x4096x1x576_s512", "inplace_f32_1x16x2x64",
-                         "cache_rope_neox_bf16_t8192", "cache_rope_gptj_f16_t32768_rd64",
-                         "cache_mrope_neox_bf16_t16384",
-                         "inplace_backward_bf16_8x4096x1x576_s512",
-                         "cache_mrope_interleaved_neox_bf16_t16384",
-                         "inplace_half_bf16_8x4096x1x576_s512",
-                         "inplace_heads_bf16_4x2048x32x192_s128_bs1d",
-                         "inplace_f32_1x524288x2x64"]),
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workloads", default=",".join(WORKLOADS),
                     help="first is the headline; the rest are reported under `kernels`")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=10.0)
-    ap.add_argument("--resident", action="store_true",
-                    help="also time without buffer rotation (Infinity-Cache-resident)")
+    ap.add_argument("--cpu-budget-s", type=float, default=10.0,
+                    help="oracle time on all cores for the headline (others: a third of it)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the launches only (no percentiles, graph replay or ceilings)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line, time the headline in-place shape and "
                          "the rope NeoX cache shape at 1..16x their tokens and fit fixed cost "
                          "+ bytes / marginal bandwidth (one JSON line)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="instead of the benchmark line, run dense copies of known sizes (for "
+                         "scaling the HBM byte counters of a profiled run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -398,6 +532,7 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    lib = load_ceiling()
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), "
@@ -406,15 +541,18 @@ def main() -> int:
     if args.sweep:
         print(json.dumps(size_sweep(torch, ra, W, dev, cyc)), flush=True)
         return 0
+    if args.calibrate:
+        calibrate(torch, lib, cyc)
+        return 0
     names = [w.strip() for w in args.workloads.split(",") if w.strip()]
-    results = {}
-    cases = {}
+    results, head_case = {}, None
     for wi, name in enumerate(names):
         case = W.CONFIGS[name](dev)
-        cases[name] = case
+        inplace = hasattr(case, "x")
         n_sets = 1 if name == "inplace_f32_1x16x2x64" else n_sets_for(case.algo_bytes)
-        calls = (inplace_calls(ra, case, n_sets) if hasattr(case, "x")
-                 else cache_calls(ra, torch, case, n_sets))
+        sets = inplace_sets(case, n_sets) if inplace else None
+        calls = inplace_calls(ra, case, n_sets, sets) if inplace else \
+            cache_calls(ra, torch, case, n_sets)
         steps = args.steps if wi == 0 else max(20, min(args.steps, 100))
         ms = time_launches(torch, calls, steps, args.warmup, cyc)
         gbs = case.algo_bytes / (ms * 1e-3) / 1e9
@@ -426,33 +564,49 @@ def main() -> int:
              "traffic": traffic_for(name)}
         if name in EXTRA:
             r["extra"] = EXTRA[name]
-        if args.resident:
-            ms_r = time_launches(torch, calls[:1], steps, args.warmup, cyc)
-            r["resident_us_per_launch"] = round(ms_r * 1e3, 3)
-            r["resident_gbs"] = round(case.algo_bytes / (ms_r * 1e-3) / 1e9, 1)
+        if not args.no_extras:
+            r["per_launch"] = launch_percentiles(torch, calls, steps, cyc)
+            if inplace:
+                gus = graph_replay_us(torch, ra, case, sets)
+                r["graph_replay"] = {"us_per_launch": round(gus, 3),
+                                     "gbs": round(case.algo_bytes / gus / 1e3, 1)}
+                pms = time_launches(torch, pattern_calls(torch, lib, case, sets), steps,
+                                    args.warmup, cyc)
+                r["ceiling"] = {"what": "the same x slice and cos/sin traffic with no "
+                                        "arithmetic (bench_ceiling.hip ceiling_rows)",
+                                "us_per_launch": round(pms * 1e3, 3),
+                                "gbs": round(case.algo_bytes / (pms * 1e-3) / 1e9, 1)}
+            else:
+                cc = copy_ceiling(torch, lib, case.algo_bytes, cyc, steps=min(steps, 50))
+                r["ceiling"] = {"what": "a dense copy of the same number of bytes "
+                                        "(bench_ceiling.hip ceiling_copy)",
+                                "us_per_launch": cc["us"], "gbs": cc["gbs"]}
+            r["ceiling"]["kernel_over_ceiling"] = round(r["ceiling"]["us_per_launch"] /
+                                                        r["us_per_launch"], 4)
         results[name] = r
         log(f"{name}: {r['us_per_launch']} us/launch, {r['gbs']} GB/s "
-            f"({100 * r['frac_of_hbm_peak']:.1f}% of peak), {n_sets} buffer sets")
-        del calls
-        if wi > 0:
-            del cases[name]
+            f"({100 * r['frac_of_hbm_peak']:.1f}% of peak), {n_sets} buffer sets"
+            + (f"; ceiling {r['ceiling']['us_per_launch']} us" if "ceiling" in r else ""))
+        del calls, sets
+        torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            budget = args.cpu_budget_s if wi == 0 else args.cpu_budget_s / 3
+            log(f"{name}: timing the CPU oracle for ~{budget + max(2.0, budget / 3):.0f} s")
+            r["cpu_baseline"] = cpu_baseline(case, budget, max(2.0, budget / 3))
+        if wi == 0:
+            head_case = case
+        else:
+            del case
         torch.cuda.empty_cache()
 
     head = names[0]
     hr = results[head]
-    if hasattr(cases[head], "x") and head != "inplace_f32_1x16x2x64":
-        gus = graph_replay_us(torch, ra, cases[head], hr["buffer_sets"])
-        hr["graph_replay"] = {"us_per_launch": round(gus, 3),
-                              "gbs": round(cases[head].algo_bytes / gus / 1e3, 1)}
-        log(f"{head} replayed from one HIP graph: {gus:.3f} us/launch")
     floor_us = launch_floor_us(torch, ra, W, dev, cyc)
     ideal_us = hr["algo_bytes_per_launch"] / (HBM_PEAK_GBS * 1e3)
     log(f"launch floor {floor_us:.3f} us: the headline could reach at most "
         f"{100 * ideal_us / (floor_us + ideal_us):.1f}% of peak per launch")
-    ceiling = copy_ceiling_gbs(torch)
-    same = copy_same_bytes(torch, hr["algo_bytes_per_launch"], cyc)
-    log(f"copy of the headline's bytes: {same['us']} us, {same['gbs']} GB/s")
-    log(f"device-to-device copy: {ceiling:.0f} GB/s")
+    ceiling = copy_ceiling(torch, lib, 1 << 30, cyc, steps=20)
+    log(f"dense copy of 1 GiB: {ceiling['gbs']} GB/s")
     out = {
         "metric": "achieved HBM GB/s (and % of peak) + tokens/sec for RoPE apply on one MI355X",
         "value": hr["gbs"],
@@ -466,28 +620,29 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded N(0,1) activations, RoPE angle tables theta=10000)",
-        "config": {"workload": hr["workload"], "tokens": cases[head].tokens,
+        "config": {"workload": hr["workload"], "name": head, "tokens": head_case.tokens,
                    "algo_bytes_per_step": hr["algo_bytes_per_launch"],
-                   "buffer_sets": hr["buffer_sets"], "name": head},
+                   "buffer_sets": hr["buffer_sets"]},
         "tokens_per_s": hr["tokens_per_s"],
         "roofline": {"bound": "hbm", "achieved": hr["gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": hr["frac_of_hbm_peak"],
-                     "traffic": traffic_for(head), "kernel": hr["kernel"]},
-        "graph_replay": hr.get("graph_replay"),
+                     "traffic": hr["traffic"], "kernel": hr["kernel"]},
+        "per_launch": hr.get("per_launch"),
+        "ceiling": hr.get("ceiling"),
         # the cost of one launch (a one-row launch back to back) and what it leaves of the peak
         # for the headline's bytes: floor + bytes at the full 8 TB/s
         "launch_floor": {"us": round(floor_us, 3),
                          "headline_frac_ceiling": round(ideal_us / (floor_us + ideal_us), 4)},
         "kernels": {k: v for k, v in results.items() if k != head},
-        "copy_ceiling_gbs": round(ceiling, 1),
-        "copy_same_bytes": same,
+        "copy_ceiling_1gib": ceiling,
         "kernel_code_sha256_16": kernel_code_hash(),
+        "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle for ~{args.cpu_budget_s:.0f} s")
-        out["cpu_baseline"] = cpu_baseline(cases[head], args.cpu_budget_s)
-    else:
-        out["cpu_baseline"] = None
+    if "cpu_baseline" in hr:
+        cb = dict(hr["cpu_baseline"])
+        cb["host_cpu"] = host_cpu_model()
+        cb["host_cores_visible"] = len(os.sched_getaffinity(0))
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
     return 0
 

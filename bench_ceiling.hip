@@ -1,0 +1,116 @@
+// bench_ceiling.hip -- measurement kernels for bench.py (not part of the RoPE library).
+//
+// Two reference streams that do no arithmetic, built in the way the RoPE kernels stream
+// (16-byte lanes, one item per lane, non-temporal loads and stores), to put a measured
+// ceiling beside each kernel's time:
+//   ceiling_copy   a dense copy of `bytes` bytes: the attainable rate of a mixed read/write
+//                  stream, and a copy of known size for scaling the HBM byte counters;
+//   ceiling_rows   an in-place pass over a strided slice of each row (read `len` bytes at
+//                  `off` of each `row_bytes`-byte row in lanes of `lane_bytes` (8 or 16), write
+//                  them back unchanged) plus dense side reads per row (`side_bytes` from each of
+//                  two arrays, row r using side row r / rows_per_side, split evenly over the
+//                  row's lanes in 16-byte loads): the access pattern of the in-place RoPE kernel
+//                  on a [rows, D] slice with its cos/sin rows, with the rotation taken out.
+// Both return 0, or -1 for arguments outside their documented form and -2 if the launch
+// fails.  Everything is enqueued on `stream` (a hipStream_t, NULL = the null stream).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 512;
+constexpr int64_t kMaxGrid = int64_t(1) << 20;
+
+__global__ __launch_bounds__(kBlock) void copy_kernel(u32x4 *dst, const u32x4 *src, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * kBlock)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+// One lane: W bytes (8 or 16) of one row's slice, and its share of the row's side bytes
+// (side_lanes loads of 16 bytes from each side array, SW = side bytes per lane / 16).  `flip`
+// is zero at run time; folding it into the data keeps every word of the store live.
+template <int W>
+__global__ __launch_bounds__(kBlock) void rows_kernel(char *x, int64_t rows, int64_t row_bytes,
+                                                      int64_t off, int64_t lanes_per_row,
+                                                      const char *side_a, const char *side_b,
+                                                      int64_t side_bytes, int64_t rows_per_side,
+                                                      uint32_t flip, bool side_stream) {
+  using V = typename std::conditional<W == 16, u32x4, u32x2>::type;
+  const int64_t per_lane = side_bytes / lanes_per_row;  // a multiple of 16 (host-checked)
+  for (int64_t it = int64_t(blockIdx.x) * kBlock + threadIdx.x; it < rows * lanes_per_row;
+       it += int64_t(gridDim.x) * kBlock) {
+    const int64_t r = it / lanes_per_row, c = it - r * lanes_per_row;
+    V *p = reinterpret_cast<V *>(x + r * row_bytes + off + c * W);
+    V v = __builtin_nontemporal_load(p);
+    uint32_t acc = 0;
+    const int64_t so = (r / rows_per_side) * side_bytes + c * per_lane;
+    for (int64_t k = 0; k < per_lane; k += 16) {
+      const u32x4 *qa = reinterpret_cast<const u32x4 *>(side_a + so + k);
+      const u32x4 *qb = reinterpret_cast<const u32x4 *>(side_b + so + k);
+      const u32x4 a = side_stream ? __builtin_nontemporal_load(qa) : *qa;
+      const u32x4 b = side_stream ? __builtin_nontemporal_load(qb) : *qb;
+      acc |= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
+    }
+    const uint32_t m = flip & acc;
+    v.x ^= m;
+    v.y ^= m;
+    if constexpr (W == 16) {
+      v.z ^= m;
+      v.w ^= m;
+    }
+    __builtin_nontemporal_store(v, p);
+  }
+}
+
+int64_t grid_for(int64_t lanes) {
+  const int64_t g = (lanes + kBlock - 1) / kBlock;
+  return g < 1 ? 1 : (g > kMaxGrid ? kMaxGrid : g);
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" __attribute__((visibility("default"))) int ceiling_copy(void *dst, const void *src,
+                                                                   int64_t bytes, void *stream) {
+  if (!dst || !src || bytes <= 0 || bytes % 16 || !aligned(dst, 16) || !aligned(src, 16))
+    return -1;
+  const int64_t n = bytes / 16;
+  hipLaunchKernelGGL(copy_kernel, dim3(uint32_t(grid_for(n))), dim3(kBlock), 0,
+                     static_cast<hipStream_t>(stream), static_cast<u32x4 *>(dst),
+                     static_cast<const u32x4 *>(src), n);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+extern "C" __attribute__((visibility("default"))) int ceiling_rows(
+    void *x, int64_t rows, int64_t row_bytes, int64_t off, int64_t len, int64_t lane_bytes,
+    const void *side_a, const void *side_b, int64_t side_bytes, int64_t rows_per_side,
+    int side_stream, void *stream) {
+  const int64_t w = lane_bytes;
+  if (!x || (w != 8 && w != 16) || rows <= 0 || len <= 0 || len % w || off % w ||
+      row_bytes % w || off + len > row_bytes || !aligned(x, uintptr_t(w)) || rows_per_side <= 0 ||
+      side_bytes < 0)
+    return -1;
+  const int64_t lanes_per_row = len / w;
+  if (side_bytes % (16 * lanes_per_row) != 0) return -1;
+  if (side_bytes > 0 && (!side_a || !side_b || !aligned(side_a, 16) || !aligned(side_b, 16)))
+    return -1;
+  const int64_t lanes = rows * lanes_per_row;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char *a = static_cast<const char *>(side_a), *b = static_cast<const char *>(side_b);
+  if (w == 16)
+    hipLaunchKernelGGL(rows_kernel<16>, dim3(uint32_t(grid_for(lanes))), dim3(kBlock), 0, s,
+                       static_cast<char *>(x), rows, row_bytes, off, lanes_per_row, a, b,
+                       side_bytes, rows_per_side, 0u, side_stream != 0);
+  else
+    hipLaunchKernelGGL(rows_kernel<8>, dim3(uint32_t(grid_for(lanes))), dim3(kBlock), 0, s,
+                       static_cast<char *>(x), rows, row_bytes, off, lanes_per_row, a, b,
+                       side_bytes, rows_per_side, 0u, side_stream != 0);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}

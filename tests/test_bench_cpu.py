@@ -65,3 +65,48 @@ def test_inplace_kernel_name_and_rotation():
     assert bench.n_sets_for(bench.MALL_DEFEAT_BYTES) == 1
     assert bench.n_sets_for(bench.MALL_DEFEAT_BYTES - 1) == 2
     assert bench.n_sets_for(25_165_824) == 86   # the headline launch: 86 buffer sets
+
+
+def test_headline_is_the_largest_configuration():
+    """The headline is the configuration with the most algorithmic bytes per launch (the
+    1 GiB GPT-J fp16 one); every other workload is reported under `kernels`."""
+    sizes = {
+        "inplace_f32_1x16x2x64": 16 * (2 * 64 * 4 * 2 + 2 * 64 * 4),
+        "inplace_bf16_8x4096x1x576_s512": 32768 * (64 * 2 * 2 + 2 * 64 * 4),
+        "cache_rope_neox_bf16_t8192": W.cache_algo_bytes(8192, 32, 8, 128, 128, 2, 1),
+        "cache_rope_gptj_f16_t32768_rd64": W.cache_algo_bytes(32768, 32, 32, 128, 64, 2, 1),
+        "cache_mrope_neox_bf16_t16384": W.cache_algo_bytes(16384, 28, 4, 128, 128, 2, 3),
+    }
+    assert bench.WORKLOADS[0] == bench.HEADLINE == max(sizes, key=sizes.get)
+    assert set(sizes) <= set(bench.WORKLOADS)
+    assert len(set(bench.WORKLOADS)) == len(bench.WORKLOADS)
+    assert all(w in W.CONFIGS for w in bench.WORKLOADS)
+
+
+@pytest.mark.parametrize("shape,sl,xdt,cdt,want", [
+    # bf16 x beside f32 cos/sin: 8-byte x lanes, one cos/sin row per row (N = 1), streamed
+    ((2, 5, 1, 576), [512, 576], torch.bfloat16, torch.float32,
+     dict(rows=10, row_bytes=1152, off=1024, len=128, lane_bytes=8, side_bytes=256,
+          rows_per_side=1, side_stream=1)),
+    # 32 heads sharing each (b, s) cos/sin row
+    ((2, 3, 32, 192), [128, 192], torch.bfloat16, torch.float32,
+     dict(rows=192, row_bytes=384, off=256, len=128, lane_bytes=8, side_bytes=256,
+          rows_per_side=32, side_stream=0)),
+    # fp32 throughout: 16-byte lanes
+    ((1, 16, 2, 64), [0, 64], torch.float32, torch.float32,
+     dict(rows=32, row_bytes=256, off=0, len=256, lane_bytes=16, side_bytes=256,
+          rows_per_side=2, side_stream=0)),
+])
+def test_inplace_access_pattern_matches_the_kernel(shape, sl, xdt, cdt, want):
+    B, S, N, D = shape
+    case = W.inplace_case("pat", B, S, N, D, xdt, cdt, sl, seed=1)
+    assert bench.inplace_pattern(case) == want
+    # the pattern moves the workload's algorithmic bytes: slice read + write, cos + sin rows
+    moved = want["rows"] * want["len"] * 2 + 2 * (want["rows"] // want["rows_per_side"]) * \
+        want["side_bytes"]
+    assert moved == case.algo_bytes
+
+
+def test_host_cpu_model_is_named():
+    name = bench.host_cpu_model()
+    assert name and name != "x86_64" or not os.path.exists("/proc/cpuinfo")
