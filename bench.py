@@ -53,8 +53,6 @@ WORKLOADS = [HEADLINE, "inplace_bf16_8x4096x1x576_s512", "inplace_f32_1x16x2x64"
              "inplace_backward_bf16_8x4096x1x576_s512", "cache_mrope_interleaved_neox_bf16_t16384",
              "inplace_half_bf16_8x4096x1x576_s512", "inplace_heads_bf16_4x2048x32x192_s128_bs1d",
              "inplace_f32_1x524288x2x64"]
-# copy sizes (bytes read = bytes written) run by --calibrate for scaling the byte counters
-CALIBRATION_BYTES = [12 << 10, 12 << 20, 36 << 20, 128 << 20, 512 << 20]
 
 
 def log(msg: str):
@@ -218,11 +216,11 @@ def launch_floor_us(torch, ra, W, dev, cyc) -> float:
     return time_launches(torch, calls, 200, 20, cyc) * 1e3
 
 
-def copy_calls(torch, lib, moved: int):
+def copy_calls(torch, lib, moved: int, max_sets: int = 1 << 16):
     """Dense copies (bench_ceiling's copy kernel) that read and write `moved` bytes in all,
-    over enough buffer pairs to rotate through MALL_DEFEAT_BYTES."""
+    over enough buffer pairs to rotate through MALL_DEFEAT_BYTES (at most max_sets pairs)."""
     half = max(16, (moved // 2) // 16 * 16)
-    n_sets = max(1, math.ceil(MALL_DEFEAT_BYTES / (2 * half)))
+    n_sets = min(max_sets, max(1, math.ceil(MALL_DEFEAT_BYTES / (2 * half))))
     pairs = [(torch.empty(half, dtype=torch.uint8, device="cuda"),
               torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(n_sets)]
     stream = torch.cuda.current_stream().cuda_stream
@@ -234,8 +232,9 @@ def copy_calls(torch, lib, moved: int):
     return [(lambda a=a, b=b: one(a, b)) for a, b in pairs], pairs, 2 * half
 
 
-def copy_ceiling(torch, lib, moved: int, cyc: float, steps: int = 50) -> dict:
-    calls, pairs, nbytes = copy_calls(torch, lib, moved)
+def copy_ceiling(torch, lib, moved: int, cyc: float, steps: int = 50,
+                 max_sets: int = 1 << 16) -> dict:
+    calls, pairs, nbytes = copy_calls(torch, lib, moved, max_sets)
     ms = time_launches(torch, calls, steps, 5, cyc)
     out = {"bytes": nbytes, "us": round(ms * 1e3, 3), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "buffer_sets": len(pairs)}
@@ -487,15 +486,34 @@ def cpu_baseline(case, budget_s: float, budget1_s: float) -> dict:
 
 # ------------------------------------------------------------------------------------------
 
-def calibrate(torch, lib, cyc):
-    """Dense copies of known size (CALIBRATION_BYTES read and as many written), 20 each, for
-    scaling the HBM byte counters of a profiled run; prints one JSON line."""
+def read_write_bytes(case) -> tuple[int, int]:
+    """Algorithmic bytes a launch reads and writes: the in-place op writes its slice back,
+    the cache op writes whole q/k rows; everything else is read."""
+    if hasattr(case, "x"):
+        B, S, N, D = case.x.shape
+        start, end = case.partial_slice if case.partial_slice else (0, D)
+        written = B * S * N * (end - start) * case.x.element_size()
+    else:
+        written = (case.query.numel() + case.key.numel()) * case.query.element_size()
+    return case.algo_bytes - written, written
+
+
+def calibrate(torch, lib, W, dev, cyc, names):
+    """For each workload, a dense copy (bench_ceiling's copy kernel) that reads as many bytes
+    as the workload's launch does (and writes as many), 20 launches each, in workload order:
+    what FETCH_SIZE and WRITE_SIZE read for a copy of known size at that size scales the
+    workload's own readings.  Prints one JSON line."""
     out = []
-    for nbytes in CALIBRATION_BYTES:
-        r = copy_ceiling(torch, lib, 2 * nbytes, cyc, steps=20)
-        r["read_bytes"] = r["bytes"] // 2
+    for name in names:
+        case = W.CONFIGS[name](dev)
+        rd, wr = read_write_bytes(case)
+        del case
+        torch.cuda.empty_cache()
+        r = copy_ceiling(torch, lib, 2 * rd, cyc, steps=20, max_sets=256)
+        r.update(workload=name, read_bytes=r["bytes"] // 2, workload_read_bytes=rd,
+                 workload_write_bytes=wr)
         out.append(r)
-        log(f"copy {nbytes} B: {r['us']} us")
+        log(f"copy for {name}: {r['read_bytes']} B read, {r['us']} us")
     print(json.dumps({"calibration_copies": out}), flush=True)
 
 
@@ -516,8 +534,9 @@ def main() -> int:
                          "the rope NeoX cache shape at 1..16x their tokens and fit fixed cost "
                          "+ bytes / marginal bandwidth (one JSON line)")
     ap.add_argument("--calibrate", action="store_true",
-                    help="instead of the benchmark line, run dense copies of known sizes (for "
-                         "scaling the HBM byte counters of a profiled run)")
+                    help="instead of the benchmark line, run one dense copy per workload that "
+                         "reads as many bytes as the workload (for scaling the HBM byte "
+                         "counters of a profiled run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -541,10 +560,10 @@ def main() -> int:
     if args.sweep:
         print(json.dumps(size_sweep(torch, ra, W, dev, cyc)), flush=True)
         return 0
-    if args.calibrate:
-        calibrate(torch, lib, cyc)
-        return 0
     names = [w.strip() for w in args.workloads.split(",") if w.strip()]
+    if args.calibrate:
+        calibrate(torch, lib, W, dev, cyc, names)
+        return 0
     results, head_case = {}, None
     for wi, name in enumerate(names):
         case = W.CONFIGS[name](dev)

@@ -110,3 +110,12 @@ def test_inplace_access_pattern_matches_the_kernel(shape, sl, xdt, cdt, want):
 def test_host_cpu_model_is_named():
     name = bench.host_cpu_model()
     assert name and name != "x86_64" or not os.path.exists("/proc/cpuinfo")
+
+
+def test_read_write_split_of_the_algorithmic_bytes():
+    inp = W.inplace_case("rw", 2, 5, 3, 96, torch.bfloat16, torch.float32, [32, 96], seed=2)
+    assert bench.read_write_bytes(inp) == (2 * 5 * 3 * 64 * 2 + 2 * 2 * 5 * 64 * 4,
+                                           2 * 5 * 3 * 64 * 2)
+    cc = W.cache_case("rw", 7, 3, 2, 128, 64, torch.float16, False, 50, seed=3)
+    rd, wr = bench.read_write_bytes(cc)
+    assert wr == 7 * 5 * 128 * 2 and rd == wr + 7 * (64 * 2 + 8)
