@@ -89,7 +89,8 @@ def load_ceiling():
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     lib.ceiling_copy.argtypes = [vp, vp, i64, vp]
     lib.ceiling_copy.restype = ctypes.c_int
-    lib.ceiling_rows.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, i64, i64, ctypes.c_int, vp]
+    lib.ceiling_rows.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, vp, i64, i64, ctypes.c_int,
+                                 vp]
     lib.ceiling_rows.restype = ctypes.c_int
     return lib
 
@@ -290,16 +291,23 @@ def cache_calls(ra, torch, case, n_sets):
 def inplace_pattern(case) -> dict:
     """The in-place kernel's memory traffic as bench_ceiling's row pattern: the slice of each
     x row in lanes of the kernel's x width (16 bytes for the wider of x and cos/sin, so 8 bytes
-    of bf16/f16 x beside float32 cos/sin), and one cos and one sin row per (b, s) (BS1D)."""
+    of bf16/f16 x beside float32 cos/sin); with cos/sin shared by the heads of a (b, s), a lane
+    takes its chunk in 4 or 2 consecutive heads (the larger that divides N and keeps a lane's
+    x bytes at 32 or less, the in-place kernel's rule) and loads the cos/sin chunk once; one cos
+    and one sin row per (b, s) (BS1D) or per row (BSND)."""
     B, S, N, D = case.x.shape
     xs, cs = case.x.element_size(), case.cos.element_size()
     start, end = case.partial_slice if case.partial_slice else (0, D)
     L = end - start
     assert tuple(case.cos.shape[:2]) == (B, S) and case.cos.shape[2] in (1, N)
     per_head = case.cos.shape[2] == N
+    lane = (16 // max(xs, cs)) * xs
+    rpl = 1
+    if not per_head and N > 1:
+        rpl = next((c for c in (4, 2) if N % c == 0 and c * lane <= 32), 1)
     return {"rows": B * S * N, "row_bytes": D * xs, "off": start * xs, "len": L * xs,
-            "lane_bytes": (16 // max(xs, cs)) * xs, "side_bytes": L * cs,
-            "rows_per_side": 1 if per_head else N, "side_stream": int(per_head or N == 1)}
+            "lane_bytes": lane, "rows_per_lane": rpl, "side_bytes": L * cs,
+            "rows_per_side": 1 if per_head else N, "side_stream": int(per_head or N == rpl)}
 
 
 def pattern_calls(torch, lib, case, sets):
@@ -308,8 +316,8 @@ def pattern_calls(torch, lib, case, sets):
 
     def one(x, c, s):
         st = lib.ceiling_rows(x.data_ptr(), pat["rows"], pat["row_bytes"], pat["off"], pat["len"],
-                              pat["lane_bytes"], c.data_ptr(), s.data_ptr(), pat["side_bytes"],
-                              pat["rows_per_side"], pat["side_stream"], stream)
+                              pat["lane_bytes"], pat["rows_per_lane"], c.data_ptr(), s.data_ptr(),
+                              pat["side_bytes"], pat["rows_per_side"], pat["side_stream"], stream)
         if st != 0:
             raise RuntimeError(f"ceiling_rows rejected {pat} ({st})")
     return [(lambda x=x, c=c, s=s: one(x, c, s)) for x, c, s in sets]

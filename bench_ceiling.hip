@@ -6,11 +6,13 @@
 //   ceiling_copy   a dense copy of `bytes` bytes: the attainable rate of a mixed read/write
 //                  stream, and a copy of known size for scaling the HBM byte counters;
 //   ceiling_rows   an in-place pass over a strided slice of each row (read `len` bytes at
-//                  `off` of each `row_bytes`-byte row in lanes of `lane_bytes` (8 or 16), write
-//                  them back unchanged) plus dense side reads per row (`side_bytes` from each of
-//                  two arrays, row r using side row r / rows_per_side, split evenly over the
-//                  row's lanes in 16-byte loads): the access pattern of the in-place RoPE kernel
-//                  on a [rows, D] slice with its cos/sin rows, with the rotation taken out.
+//                  `off` of each `row_bytes`-byte row in lanes of `lane_bytes` (8 or 16), a lane
+//                  taking its chunk in `rows_per_lane` consecutive rows (1, 2 or 4), write them
+//                  back unchanged) plus dense side reads per row (`side_bytes` from each of two
+//                  arrays, row r using side row r / rows_per_side, split evenly over the row's
+//                  lanes in 16-byte loads, loaded once per lane): the access pattern of the
+//                  in-place RoPE kernel on a [rows, D] slice with its cos/sin rows, with the
+//                  rotation taken out.
 // Both return 0, or -1 for arguments outside their documented form and -2 if the launch
 // fails.  Everything is enqueued on `stream` (a hipStream_t, NULL = the null stream).
 #include <hip/hip_runtime.h>
@@ -32,24 +34,27 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(u32x4 *dst, const u32x4 *s
     __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
-// One lane: W bytes (8 or 16) of one row's slice, and its share of the row's side bytes
-// (side_lanes loads of 16 bytes from each side array, SW = side bytes per lane / 16).  `flip`
-// is zero at run time; folding it into the data keeps every word of the store live.
-template <int W>
-__global__ __launch_bounds__(kBlock) void rows_kernel(char *x, int64_t rows, int64_t row_bytes,
+// One lane: W bytes (8 or 16) of the slice in each of R consecutive rows (rows that share one
+// side row), and its share of that side row (16-byte loads from each side array, loaded once for
+// the R rows).  `flip` is zero at run time; folding it into the data keeps every word of the
+// stores live.
+template <int W, int R>
+__global__ __launch_bounds__(kBlock) void rows_kernel(char *x, int64_t groups, int64_t row_bytes,
                                                       int64_t off, int64_t lanes_per_row,
                                                       const char *side_a, const char *side_b,
                                                       int64_t side_bytes, int64_t rows_per_side,
                                                       uint32_t flip, bool side_stream) {
   using V = typename std::conditional<W == 16, u32x4, u32x2>::type;
   const int64_t per_lane = side_bytes / lanes_per_row;  // a multiple of 16 (host-checked)
-  for (int64_t it = int64_t(blockIdx.x) * kBlock + threadIdx.x; it < rows * lanes_per_row;
+  for (int64_t it = int64_t(blockIdx.x) * kBlock + threadIdx.x; it < groups * lanes_per_row;
        it += int64_t(gridDim.x) * kBlock) {
-    const int64_t r = it / lanes_per_row, c = it - r * lanes_per_row;
-    V *p = reinterpret_cast<V *>(x + r * row_bytes + off + c * W);
-    V v = __builtin_nontemporal_load(p);
+    const int64_t g = it / lanes_per_row, c = it - g * lanes_per_row;
+    V *p = reinterpret_cast<V *>(x + g * R * row_bytes + off + c * W);
+    V v[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = __builtin_nontemporal_load(p + j * (row_bytes / W));
     uint32_t acc = 0;
-    const int64_t so = (r / rows_per_side) * side_bytes + c * per_lane;
+    const int64_t so = (g * R / rows_per_side) * side_bytes + c * per_lane;
     for (int64_t k = 0; k < per_lane; k += 16) {
       const u32x4 *qa = reinterpret_cast<const u32x4 *>(side_a + so + k);
       const u32x4 *qb = reinterpret_cast<const u32x4 *>(side_b + so + k);
@@ -58,13 +63,16 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(char *x, int64_t rows, int
       acc |= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
     }
     const uint32_t m = flip & acc;
-    v.x ^= m;
-    v.y ^= m;
-    if constexpr (W == 16) {
-      v.z ^= m;
-      v.w ^= m;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      v[j].x ^= m;
+      v[j].y ^= m;
+      if constexpr (W == 16) {
+        v[j].z ^= m;
+        v[j].w ^= m;
+      }
+      __builtin_nontemporal_store(v[j], p + j * (row_bytes / W));
     }
-    __builtin_nontemporal_store(v, p);
   }
 }
 
@@ -90,27 +98,34 @@ extern "C" __attribute__((visibility("default"))) int ceiling_copy(void *dst, co
 
 extern "C" __attribute__((visibility("default"))) int ceiling_rows(
     void *x, int64_t rows, int64_t row_bytes, int64_t off, int64_t len, int64_t lane_bytes,
-    const void *side_a, const void *side_b, int64_t side_bytes, int64_t rows_per_side,
-    int side_stream, void *stream) {
-  const int64_t w = lane_bytes;
-  if (!x || (w != 8 && w != 16) || rows <= 0 || len <= 0 || len % w || off % w ||
-      row_bytes % w || off + len > row_bytes || !aligned(x, uintptr_t(w)) || rows_per_side <= 0 ||
-      side_bytes < 0)
+    int64_t rows_per_lane, const void *side_a, const void *side_b, int64_t side_bytes,
+    int64_t rows_per_side, int side_stream, void *stream) {
+  const int64_t w = lane_bytes, r = rows_per_lane;
+  if (!x || (w != 8 && w != 16) || (r != 1 && r != 2 && r != 4) || rows <= 0 || rows % r ||
+      len <= 0 || len % w || off % w || row_bytes % w || off + len > row_bytes ||
+      !aligned(x, uintptr_t(w)) || rows_per_side <= 0 || rows_per_side % r || side_bytes < 0)
     return -1;
   const int64_t lanes_per_row = len / w;
   if (side_bytes % (16 * lanes_per_row) != 0) return -1;
   if (side_bytes > 0 && (!side_a || !side_b || !aligned(side_a, 16) || !aligned(side_b, 16)))
     return -1;
-  const int64_t lanes = rows * lanes_per_row;
+  const int64_t groups = rows / r, lanes = groups * lanes_per_row;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const char *a = static_cast<const char *>(side_a), *b = static_cast<const char *>(side_b);
-  if (w == 16)
-    hipLaunchKernelGGL(rows_kernel<16>, dim3(uint32_t(grid_for(lanes))), dim3(kBlock), 0, s,
-                       static_cast<char *>(x), rows, row_bytes, off, lanes_per_row, a, b,
-                       side_bytes, rows_per_side, 0u, side_stream != 0);
-  else
-    hipLaunchKernelGGL(rows_kernel<8>, dim3(uint32_t(grid_for(lanes))), dim3(kBlock), 0, s,
-                       static_cast<char *>(x), rows, row_bytes, off, lanes_per_row, a, b,
-                       side_bytes, rows_per_side, 0u, side_stream != 0);
+  const dim3 grid(uint32_t(grid_for(lanes))), block(kBlock);
+  char *xc = static_cast<char *>(x);
+#define ROWS_LAUNCH(W, R)                                                                    \
+  hipLaunchKernelGGL((rows_kernel<W, R>), grid, block, 0, s, xc, groups, row_bytes, off,      \
+                     lanes_per_row, a, b, side_bytes, rows_per_side, 0u, side_stream != 0)
+  if (w == 16) {
+    if (r == 1) ROWS_LAUNCH(16, 1);
+    else if (r == 2) ROWS_LAUNCH(16, 2);
+    else ROWS_LAUNCH(16, 4);
+  } else {
+    if (r == 1) ROWS_LAUNCH(8, 1);
+    else if (r == 2) ROWS_LAUNCH(8, 2);
+    else ROWS_LAUNCH(8, 4);
+  }
+#undef ROWS_LAUNCH
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }

@@ -86,16 +86,20 @@ def test_headline_is_the_largest_configuration():
 @pytest.mark.parametrize("shape,sl,xdt,cdt,want", [
     # bf16 x beside f32 cos/sin: 8-byte x lanes, one cos/sin row per row (N = 1), streamed
     ((2, 5, 1, 576), [512, 576], torch.bfloat16, torch.float32,
-     dict(rows=10, row_bytes=1152, off=1024, len=128, lane_bytes=8, side_bytes=256,
-          rows_per_side=1, side_stream=1)),
-    # 32 heads sharing each (b, s) cos/sin row
+     dict(rows=10, row_bytes=1152, off=1024, len=128, lane_bytes=8, rows_per_lane=1,
+          side_bytes=256, rows_per_side=1, side_stream=1)),
+    # 32 heads sharing each (b, s) cos/sin row: 4 heads per lane of 8-byte chunks
     ((2, 3, 32, 192), [128, 192], torch.bfloat16, torch.float32,
-     dict(rows=192, row_bytes=384, off=256, len=128, lane_bytes=8, side_bytes=256,
-          rows_per_side=32, side_stream=0)),
-    # fp32 throughout: 16-byte lanes
+     dict(rows=192, row_bytes=384, off=256, len=128, lane_bytes=8, rows_per_lane=4,
+          side_bytes=256, rows_per_side=32, side_stream=0)),
+    # fp32 throughout: 16-byte lanes, 2 heads per lane (their one cos/sin row streamed)
     ((1, 16, 2, 64), [0, 64], torch.float32, torch.float32,
-     dict(rows=32, row_bytes=256, off=0, len=256, lane_bytes=16, side_bytes=256,
-          rows_per_side=2, side_stream=0)),
+     dict(rows=32, row_bytes=256, off=0, len=256, lane_bytes=16, rows_per_lane=2,
+          side_bytes=256, rows_per_side=2, side_stream=1)),
+    # 6 heads of 16-byte chunks: 2 per lane
+    ((2, 3, 6, 64), [0, 64], torch.bfloat16, torch.bfloat16,
+     dict(rows=36, row_bytes=128, off=0, len=128, lane_bytes=16, rows_per_lane=2,
+          side_bytes=128, rows_per_side=6, side_stream=0)),
 ])
 def test_inplace_access_pattern_matches_the_kernel(shape, sl, xdt, cdt, want):
     B, S, N, D = shape
