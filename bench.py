@@ -472,9 +472,10 @@ def _oracle_rate(tokens, run, algo_bytes, threads: int, budget_s: float):
 
 def cpu_baseline(case, budget_s: float, budget1_s: float) -> dict:
     """The oracle as it stands on the host: on all the cores this process may use (up to 16,
-    the host share of one GPU), and on one thread."""
-    cores = min(16, len(os.sched_getaffinity(0)))
+    the host share of one GPU; at most one thread per 512 tokens, since a thread with a handful
+    of tokens per call measures the call overhead), and on one thread."""
     tokens, run = _host_copies(case)
+    cores = max(1, min(16, len(os.sched_getaffinity(0)), tokens // 512))
     bps, tps, passes, el = _oracle_rate(tokens, run, case.algo_bytes, cores, budget_s)
     bps1, tps1, passes1, el1 = _oracle_rate(tokens, run, case.algo_bytes, 1, budget1_s)
     return {
