@@ -115,3 +115,38 @@ def test_cache_fuzz(seed):
     torch.cuda.synchronize()
     compare_cache(pos.cpu(), q.cpu(), k.cpu(), cache.cpu(), cfg["sec"], H, cfg["neox"],
                   qo.cpu(), ko.cpu(), f"fuzz {seed}: {cfg}", cfg["cache_mode"])
+
+
+def cache_fuzz_long(seed):
+    """rotaryDim either side of 16384, where a token's cos|sin row no longer fits the tile
+    kernel's LDS and each item reads the cache row directly (an own generator, so the seeds
+    above keep their configurations)."""
+    rng = np.random.default_rng(4000 + seed)
+    dt = [torch.float32, torch.float16, torch.bfloat16][int(rng.integers(3))]
+    align = 64 // torch.empty(0, dtype=dt).element_size()
+    rd = align * int(rng.integers(16384 // align - 3, 24576 // align + 1))
+    H = rd + align * int(rng.integers(0, 3))
+    return dict(dt=dt, neox=bool(rng.integers(0, 2)), rd=rd, H=H, nq=int(rng.integers(1, 4)),
+                nk=int(rng.integers(1, 3)), T=int(rng.integers(1, 24)),
+                max_seq=int(rng.integers(1, 48)),
+                pad_q=int(rng.integers(0, 3)) * align if rng.random() < 0.4 else 0,
+                v2=bool(rng.integers(0, 2)))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_cache_fuzz_long_rotary_dim(seed):
+    cfg = cache_fuzz_long(seed)
+    g = W.generator(5000 + seed, DEV)
+    T, H, rd, dt = cfg["T"], cfg["H"], cfg["rd"], cfg["dt"]
+    qbig = W.randn((T, cfg["nq"] * H + cfg["pad_q"]), dt, g)
+    q = qbig[:, :cfg["nq"] * H]
+    k = W.randn((T, cfg["nk"] * H), dt, g)
+    cache = W.randn((cfg["max_seq"], rd), dt, g)
+    pos = torch.randint(0, cfg["max_seq"], (T,), generator=g, device=DEV)
+    if cfg["v2"]:
+        qo, ko = ra.rope_with_cos_sin_cache_v2(pos, q, k, cache, None, H, cfg["neox"], 0)
+    else:
+        qo, ko = ra.rope_with_cos_sin_cache(pos, q, k, cache, None, H, cfg["neox"])
+    torch.cuda.synchronize()
+    compare_cache(pos.cpu(), q.cpu(), k.cpu(), cache.cpu(), None, H, cfg["neox"], qo.cpu(),
+                  ko.cpu(), f"long-rd fuzz {seed}: {cfg}")
