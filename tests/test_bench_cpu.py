@@ -123,3 +123,35 @@ def test_read_write_split_of_the_algorithmic_bytes():
     cc = W.cache_case("rw", 7, 3, 2, 128, 64, torch.float16, False, 50, seed=3)
     rd, wr = bench.read_write_bytes(cc)
     assert wr == 7 * 5 * 128 * 2 and rd == wr + 7 * (64 * 2 + 8)
+
+
+@pytest.mark.skipif(not os.path.exists(bench.CEILING_LIB), reason="libbench_ceiling.so not built")
+def test_ceiling_kernels_refuse_arguments_outside_their_form():
+    """bench_ceiling's entry points check their arguments before any launch (so these calls
+    run without a GPU): null or misaligned buffers, sizes that are not whole lanes, a slice past
+    the row, lane widths and rows per lane outside {8, 16} and {1, 2, 4}."""
+    lib = bench.load_ceiling()
+    buf = torch.zeros(1 << 16, dtype=torch.uint8)
+    p = buf.data_ptr()
+    assert p % 256 == 0
+    assert lib.ceiling_copy(None, p, 1024, None) == -1
+    assert lib.ceiling_copy(p, p + 8, 1024, None) == -1            # misaligned source
+    assert lib.ceiling_copy(p, p + 4096, 1000, None) == -1         # not whole 16-byte lanes
+    assert lib.ceiling_copy(p, p + 4096, 0, None) == -1
+
+    def rows(**kw):
+        a = dict(x=p, rows=8, row_bytes=384, off=256, len=128, lane=8, rpl=4, sa=p + 8192,
+                 sb=p + 12288, side=256, rps=32, stream_side=0)
+        a.update(kw)
+        return lib.ceiling_rows(a["x"], a["rows"], a["row_bytes"], a["off"], a["len"], a["lane"],
+                                a["rpl"], a["sa"], a["sb"], a["side"], a["rps"], a["stream_side"],
+                                None)
+    assert rows(x=None) == -1
+    assert rows(lane=4) == -1                  # lane width outside {8, 16}
+    assert rows(rpl=3) == -1                   # rows per lane outside {1, 2, 4}
+    assert rows(rows=6) == -1                  # rows not a multiple of rows per lane
+    assert rows(off=320) == -1                 # slice past the end of the row
+    assert rows(len=100) == -1                 # not whole lanes
+    assert rows(side=200) == -1                # side bytes not whole 16-byte loads per lane
+    assert rows(rps=2) == -1                   # rows per lane sharing different side rows
+    assert rows(sa=p + 8) == -1                # misaligned side array
