@@ -9,6 +9,11 @@ streams.  There is no fallback: if the library is not built this import fails.
   rope_partial_inplace_backward(g, cos, sin, rotary_mode=1, partial_slice=None, stream=None)
   InplacePartialRotaryMul.apply(x, cos, sin, partial_slice, rotary_mode)
                                                   (autograd; x must not be a leaf)
+  inplace_partial_rotary_mul(x, r1, r2, *, rotary_mode="interleave", partial_slice=None)
+  inplace_partial_rotary_mul_backward(grad, r1, r2, *, rotary_mode="interleave",
+                                      partial_slice=None)
+                                                  (the pages' Python interface: same calls,
+                                                  autograd when x requires grad)
   rope_with_cos_sin_cache(positions, query_in, key_in, cos_sin_cache, mrope_section,
                           head_size, is_neox_style, query_out=None, key_out=None, stream=None)
   rope_with_cos_sin_cache_v2(..., is_neox_style, cache_mode, query_out=None, ...)
@@ -206,6 +211,40 @@ def __getattr__(name):
         globals()[name] = fn
         return fn
     raise AttributeError(name)
+
+
+_ROTARY_MODES = {"interleave": 1, "half": 0}
+
+
+def _rotary_mode_code(rotary_mode) -> int:
+    if isinstance(rotary_mode, str):
+        if rotary_mode not in _ROTARY_MODES:
+            raise RopeError(ROPE_ERR_PARAM_INVALID,
+                            f"rotary_mode {rotary_mode!r}: 'interleave' or 'half' (or 1 / 0)")
+        return _ROTARY_MODES[rotary_mode]
+    return int(rotary_mode)
+
+
+def inplace_partial_rotary_mul(x, r1, r2, *, rotary_mode="interleave", partial_slice=None):
+    """The Python interface of [IPRM §Python 接口与自动微分]: rotates x in place (r1 = cos,
+    r2 = sin) and returns None.  rotary_mode is "interleave" (1) or "half" (0, reading R21).
+    When autograd records x (x requires grad and grad mode is on), the call goes through
+    InplacePartialRotaryMul, so the gradient of x comes from the backward kernel and r1, r2 get
+    none; x must then not be a leaf (rotate a copy such as ``y = x * 1.0``)."""
+    import torch
+    mode = _rotary_mode_code(rotary_mode)
+    if x.requires_grad and torch.is_grad_enabled():
+        __getattr__("InplacePartialRotaryMul").apply(x, r1, r2, partial_slice, mode)
+    else:
+        rope_partial_inplace(x, r1, r2, mode, partial_slice)
+
+
+def inplace_partial_rotary_mul_backward(grad, r1, r2, *, rotary_mode="interleave",
+                                        partial_slice=None):
+    """The gradient op named by [IPRM §Python 接口与自动微分], in place on ``grad`` (the
+    transpose of each slice pair's rotation; outside the slice the gradient passes through).
+    Returns None."""
+    rope_partial_inplace_backward(grad, r1, r2, _rotary_mode_code(rotary_mode), partial_slice)
 
 
 def _cache_args(positions, query_in, key_in, cos_sin_cache, mrope_section, head_size,

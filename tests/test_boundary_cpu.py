@@ -393,3 +393,19 @@ def test_library_carries_gfx950_code_only():
     from rope_partial_inplace_amd import build
     targets = build.bundled_targets(ra.LIB_PATH)
     assert [t for t in targets if not t.startswith("host-")] == ["hipv4-amdgcn-amd-amdhsa--gfx950"]
+
+
+def test_pages_python_interface_rotary_mode_names():
+    """inplace_partial_rotary_mul takes rotary_mode by name as on [IPRM §Python 接口与自动微分]
+    ("interleave"; "half" for mode 0) or by number; other names are refused before any call,
+    other numbers go to the library, which refuses them."""
+    assert ra._rotary_mode_code("interleave") == 1
+    assert ra._rotary_mode_code("half") == 0
+    assert ra._rotary_mode_code(1) == 1 and ra._rotary_mode_code(0) == 0
+    with pytest.raises(ra.RopeError) as e:
+        ra._rotary_mode_code("quarter")
+    assert e.value.code == ra.ROPE_ERR_PARAM_INVALID
+    x = torch.zeros(1, 2, 1, 8)
+    with pytest.raises(ra.RopeError) as e:   # host tensors are refused before the library
+        ra.inplace_partial_rotary_mul(x, x[..., :8], x[..., :8], partial_slice=[0, 8])
+    assert e.value.code == ra.ROPE_ERR_PARAM_INVALID

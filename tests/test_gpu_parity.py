@@ -786,6 +786,40 @@ def test_autograd_wrapper_gradient():
     check_backward(w.cpu(), x.grad, c, s, sl, "autograd")
 
 
+@pytest.mark.parametrize("mode", ["interleave", "half"])
+def test_pages_python_interface(mode):
+    """inplace_partial_rotary_mul / _backward, the Python interface of [IPRM §Python 接口与自动
+    微分]: returns None and rotates x in place (as rope_partial_inplace does) without autograd;
+    with x requiring grad it records the op, and the gradient of x equals the backward op
+    applied to the incoming gradient; r1, r2 get no gradient."""
+    code = {"interleave": 1, "half": 0}[mode]
+    B, S, N, D, sl = 2, 32, 8, 128, [0, 64]
+    g = W.generator(41 + code, DEV)
+    x = W.randn((B, S, N, D), torch.bfloat16, g)
+    r1 = W.randn((B, S, 1, 64), torch.bfloat16, g)
+    r2 = W.randn((B, S, 1, 64), torch.bfloat16, g)
+    a, b = x.clone(), x.clone()
+    assert ra.inplace_partial_rotary_mul(a, r1, r2, rotary_mode=mode, partial_slice=sl) is None
+    ra.rope_partial_inplace(b, r1, r2, code, sl)
+    torch.cuda.synchronize()
+    check_bits_equal(a, b, f"{mode}: pages' interface vs entry point")
+    # autograd
+    xg = x.float().requires_grad_(True)
+    c32, s32 = r1.float().requires_grad_(True), r2.float().requires_grad_(True)
+    y = xg * 1.0
+    assert ra.inplace_partial_rotary_mul(y, c32, s32, rotary_mode=mode, partial_slice=sl) is None
+    w = W.randn((B, S, N, D), torch.float32, g)
+    (y * w).sum().backward()
+    ref = w.clone()
+    assert ra.inplace_partial_rotary_mul_backward(ref, c32.detach(), s32.detach(),
+                                                  rotary_mode=mode, partial_slice=sl) is None
+    torch.cuda.synchronize()
+    check_bits_equal(xg.grad, ref, f"{mode}: autograd gradient vs the backward op")
+    assert c32.grad is None and s32.grad is None
+    check_backward(w.cpu(), xg.grad, c32.detach(), s32.detach(), sl, f"{mode} autograd",
+                   mode=code)
+
+
 # ------------------------------------------------------------------------------------------
 # half mode, rotary_mode 0 (x1, x2 the two halves of the slice)
 # ------------------------------------------------------------------------------------------
