@@ -8,8 +8,9 @@
  *     start, or empty), B/S/N, broadcast dims of cos/sin, both rotary modes, forward and
  *     gradient, with and without the float64 twin;
  *   - cache op: every dtype, both styles, rope mode and every whitelisted mropeSection with
- *     both cache modes, padded query rows, positions in range (status 0) and one out of
- *     range (the oracle's out-of-contract status);
+ *     both cache modes, padded query rows, rotaryDim either side of 16384 (rope mode),
+ *     positions in range (status 0) and one out of range (the oracle's out-of-contract
+ *     status);
  *   - a few calls that must be refused (NULL data, a bad slice, a bad list).
  * Prints "ok <calls>" or the first failure; exit status 1 on failure.
  */
@@ -133,10 +134,16 @@ static void cache_case(int seed) {
   int kind = (int)pick(0, 5); /* 0: rope, else list kind - 1 */
   const int64_t *sec = kind ? lists[kind - 1] : NULL;
   int64_t nsec = kind == 5 ? 4 : kind ? 3 : 0;
-  int64_t rd = kind ? 2 * (sec[0] + sec[1] + sec[2] + sec[3]) : align * pick(1, 4);
+  /* rope mode, 1 in 12: rotaryDim either side of 16384 (the oracle's row buffers are sized
+   * per call; every buffer here is allocated to its exact size, so the sanitizer sees any
+   * overrun) */
+  int long_rd = !kind && pick(0, 11) == 0;
+  int64_t rd = kind ? 2 * (sec[0] + sec[1] + sec[2] + sec[3])
+                    : long_rd ? align * pick(16384 / align - 2, 24576 / align) : align * pick(1, 4);
   if (rd % align) return; /* [11,11,10] in f32: not a 64-byte multiple */
   int64_t H = rd + align * pick(0, 2);
-  int64_t nq = pick(1, 5), nk = pick(1, 3), T = pick(1, 40), max_seq = pick(1, 70);
+  int64_t nq = pick(1, 5), nk = pick(1, 3), T = long_rd ? pick(1, 3) : pick(1, 40);
+  int64_t max_seq = pick(1, 70);
   int64_t pad = pick(0, 1) * align;
   int64_t cache_mode = nsec == 3 ? pick(0, 1) : 0;
   int64_t qbig_shape[2] = {T, nq * H + pad}, ks[2] = {T, nk * H}, cshape[2] = {max_seq, rd};
