@@ -22,6 +22,10 @@ separate pass), the per-launch time of the same launches replayed from one captu
 (bench_ceiling.hip: the in-place access pattern, or a dense copy of the cache op's bytes), and
 the CPU oracle's rate on the same workload at 1 thread and on all usable host cores.  One
 JSON line on stdout; progress goes to stderr.
+
+Other modes (each one JSON line instead of the benchmark line): --sweep (the same kernels at
+growing sizes, fixed cost + marginal rate), --latency (decode-size launches of both ops),
+--calibrate (copies of known size for scaling the HBM byte counters of a profiled run).
 """
 from __future__ import annotations
 
@@ -526,6 +530,99 @@ def calibrate(torch, lib, W, dev, cyc, names):
     print(json.dumps({"calibration_copies": out}), flush=True)
 
 
+def single_launch_us(torch, call, reps: int = 50) -> dict:
+    """Latency of one launch issued to an idle GPU: events around each launch, the GPU
+    synchronized between launches (median and p90 over `reps`)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d = []
+    for _ in range(reps + 5):
+        torch.cuda.synchronize()
+        a.record()
+        call()
+        b.record()
+        torch.cuda.synchronize()
+        d.append(a.elapsed_time(b) * 1e3)
+    d = sorted(d[5:])
+    return {"median_us": round(d[len(d) // 2], 3), "p90_us": round(d[int(0.9 * (len(d) - 1))], 3)}
+
+
+def graph_calls_us(torch, make_call, n_sets: int, reps: int = 5) -> float:
+    """Per-launch time of `max(n_sets, 32)` launches captured in one HIP graph and replayed
+    back to back; make_call(i) issues launch i on the current stream (called during capture)."""
+    order = list(range(max(n_sets, 32)))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in order:
+            make_call(i % n_sets)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in order:
+            make_call(i % n_sets)
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    del g
+    return s.elapsed_time(e) * 1e3 / (reps * len(order))
+
+
+def latency(torch, ra, W, dev, cyc) -> dict:
+    """Decode-size launches: the in-place op on bf16 x [B,1,32,128] with f32 BS1D tables and the
+    cache op in rope NeoX bf16 (32 + 8 heads of 128, cache [32768,128]) at 1-1024 tokens: the
+    per-launch time of launches run back to back (stream and graph replay) and the latency of
+    one launch on an idle GPU."""
+    out = {"inplace_rope_kernel": [], "cos_sin_cache_wave_kernel": []}
+    for t in (1, 8, 64, 256, 1024):
+        case = W.inplace_case("lat", t, 1, 32, 128, torch.bfloat16, torch.float32, [0, 128],
+                              seed=1300 + t, device=dev)
+        n = n_sets_for(case.algo_bytes)
+        sets = inplace_sets(case, min(n, 256))
+        calls = inplace_calls(ra, case, len(sets), sets)
+        b2b = time_launches(torch, calls, 200, 20, cyc) * 1e3
+        one = single_launch_us(torch, calls[0])
+        gus = graph_calls_us(torch, lambda i: ra.rope_partial_inplace(
+            sets[i][0], sets[i][1], sets[i][2], 1, [0, 128]), len(sets))
+        out["inplace_rope_kernel"].append({"tokens": t, "bytes": case.algo_bytes,
+                                           "back_to_back_us": round(b2b, 3),
+                                           "graph_replay_us": round(gus, 3), "single": one})
+        log(f"latency in-place {t} tokens: {b2b:.3f} us back to back, {one['median_us']} us alone")
+        del calls, sets, case
+        cc = W.cache_case("lat", t, 32, 8, 128, 128, torch.bfloat16, True, 32768,
+                          seed=1400 + t, device=dev)
+        n = min(n_sets_for(cc.algo_bytes), 256)
+        calls = cache_calls(ra, torch, cc, n)
+        b2b = time_launches(torch, calls, 200, 20, cyc) * 1e3
+        one = single_launch_us(torch, calls[0])
+        qs = [cc.query.clone() for _ in range(n)]
+        ks = [cc.key.clone() for _ in range(n)]
+        outs = [(torch.empty_like(q), torch.empty_like(k)) for q, k in zip(qs, ks)]
+        gus = graph_calls_us(torch, lambda i: ra.rope_with_cos_sin_cache(
+            cc.positions, qs[i], ks[i], cc.cache, None, 128, True, outs[i][0], outs[i][1]), n)
+        out["cos_sin_cache_wave_kernel"].append({"tokens": t, "bytes": cc.algo_bytes,
+                                                 "back_to_back_us": round(b2b, 3),
+                                                 "graph_replay_us": round(gus, 3),
+                                                 "single": one})
+        log(f"latency cache {t} tokens: {b2b:.3f} us back to back, {one['median_us']} us alone")
+        del calls, qs, ks, outs, cc
+        torch.cuda.empty_cache()
+    floor = launch_floor_us(torch, ra, W, dev, cyc)
+    fcase = W.inplace_case("floor", 1, 1, 1, 64, torch.float32, torch.float32, [0, 64], seed=7,
+                           device=dev)
+    floor_one = single_launch_us(torch, inplace_calls(ra, fcase, 1)[0])
+    return {"latency": out, "launch_floor_us": round(floor, 3),
+            # the same single-launch measurement for the one-row launch: what the events, an
+            # idle GPU's wake-up and a minimal kernel cost before any of the work above
+            "launch_floor_single": floor_one,
+            "kernel_code_sha256_16": kernel_code_hash()}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -542,6 +639,10 @@ def main() -> int:
                     help="instead of the benchmark line, time the headline in-place shape and "
                          "the rope NeoX cache shape at 1..16x their tokens and fit fixed cost "
                          "+ bytes / marginal bandwidth (one JSON line)")
+    ap.add_argument("--latency", action="store_true",
+                    help="instead of the benchmark line, time decode-size launches of both "
+                         "operations (1-1024 tokens): back to back, graph replay, and one "
+                         "launch on an idle GPU (one JSON line)")
     ap.add_argument("--calibrate", action="store_true",
                     help="instead of the benchmark line, run one dense copy per workload that "
                          "reads as many bytes as the workload (for scaling the HBM byte "
@@ -568,6 +669,9 @@ def main() -> int:
     cyc = spin_cycles_per_ms(torch)
     if args.sweep:
         print(json.dumps(size_sweep(torch, ra, W, dev, cyc)), flush=True)
+        return 0
+    if args.latency:
+        print(json.dumps(latency(torch, ra, W, dev, cyc)), flush=True)
         return 0
     names = [w.strip() for w in args.workloads.split(",") if w.strip()]
     if args.calibrate:
