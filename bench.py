@@ -25,6 +25,7 @@ JSON line on stdout; progress goes to stderr.
 
 Other modes (each one JSON line instead of the benchmark line): --sweep (the same kernels at
 growing sizes, fixed cost + marginal rate), --latency (decode-size launches of both ops),
+--patterns (the strided-slice and NeoX pair-unit access patterns against dense ones),
 --calibrate (copies of known size for scaling the HBM byte counters of a profiled run).
 """
 from __future__ import annotations
@@ -96,6 +97,8 @@ def load_ceiling():
     lib.ceiling_rows.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, vp, i64, i64, ctypes.c_int,
                                  vp]
     lib.ceiling_rows.restype = ctypes.c_int
+    lib.ceiling_pairs.argtypes = [vp, vp, i64, i64, i64, vp]
+    lib.ceiling_pairs.restype = ctypes.c_int
     return lib
 
 
@@ -623,6 +626,64 @@ def latency(torch, ra, W, dev, cyc) -> dict:
             "kernel_code_sha256_16": kernel_code_hash()}
 
 
+def patterns(torch, ra, W, lib, dev, cyc) -> dict:
+    """The memory-side costs the design notes attribute to two layouts, measured with the
+    no-arithmetic kernels of bench_ceiling.hip beside the RoPE kernels on the same shapes:
+      - the strided slice: bf16 x [128,4096,1,576] with slice [512,576) (128 B of every 1152)
+        against dense rows with the same bytes, x [128,4096,1,64] (403 MB each, f32 BS1D
+        tables): the in-place kernel and its access pattern on each;
+      - the NeoX pair units: a copy of the rope NeoX workload's q and k rows (8192 tokens x 40
+        heads of 256 B) in the pair-unit layout (two 16-byte vectors half a head apart per
+        lane, two head rows per lane), against a dense copy of the same bytes, beside the
+        cache kernel on that workload."""
+    out = {}
+    rows = {}
+    for tag, D, sl in (("strided_1152B_rows", 576, [512, 576]), ("dense_128B_rows", 64, [0, 64])):
+        case = W.inplace_case(tag, 128, 4096, 1, D, torch.bfloat16, torch.float32, sl,
+                              seed=1500 + D, device=dev)
+        sets = inplace_sets(case, n_sets_for(case.algo_bytes))
+        k_ms = time_launches(torch, inplace_calls(ra, case, len(sets), sets), 50, 5, cyc)
+        p_ms = time_launches(torch, pattern_calls(torch, lib, case, sets), 50, 5, cyc)
+        rows[tag] = {"workload": describe_case(tag, case), "bytes": case.algo_bytes,
+                     "kernel_us": round(k_ms * 1e3, 3),
+                     "kernel_gbs": round(case.algo_bytes / (k_ms * 1e-3) / 1e9, 1),
+                     "pattern_us": round(p_ms * 1e3, 3),
+                     "pattern_gbs": round(case.algo_bytes / (p_ms * 1e-3) / 1e9, 1)}
+        log(f"{tag}: kernel {k_ms * 1e3:.2f} us, pattern {p_ms * 1e3:.2f} us")
+        del sets, case
+        torch.cuda.empty_cache()
+    out["strided_slice"] = rows
+    case = W.CONFIGS["cache_rope_neox_bf16_t8192"](dev)
+    k_ms = time_launches(torch, cache_calls(ra, torch, case, n_sets_for(case.algo_bytes)), 50, 5,
+                         cyc)
+    heads = case.tokens * (case.query.shape[1] + case.key.shape[1]) // case.head_size
+    head_bytes = case.head_size * case.query.element_size()
+    nbytes = heads * head_bytes
+    n_sets = max(1, math.ceil(MALL_DEFEAT_BYTES / (2 * nbytes)))
+    bufs = [(torch.empty(nbytes, dtype=torch.uint8, device=dev),
+             torch.empty(nbytes, dtype=torch.uint8, device=dev)) for _ in range(n_sets)]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def pair_call(a, b, k):
+        st = lib.ceiling_pairs(b.data_ptr(), a.data_ptr(), heads, head_bytes, k, stream)
+        if st != 0:
+            raise RuntimeError(f"ceiling_pairs failed ({st})")
+    res = {"workload": describe_case("cache_rope_neox_bf16_t8192", case),
+           "bytes_moved": 2 * nbytes, "kernel_us": round(k_ms * 1e3, 3)}
+    for k in (2, 1):
+        ms = time_launches(torch, [(lambda a=a, b=b, k=k: pair_call(a, b, k)) for a, b in bufs],
+                           50, 5, cyc)
+        res[f"pair_copy_{k}_rows_per_lane_us"] = round(ms * 1e3, 3)
+    del bufs
+    torch.cuda.empty_cache()
+    res["dense_copy_us"] = copy_ceiling(torch, lib, 2 * nbytes, cyc)["us"]
+    log(f"neox pairs: kernel {res['kernel_us']} us, pair copy {res['pair_copy_2_rows_per_lane_us']}"
+        f" us, dense copy {res['dense_copy_us']} us")
+    out["neox_pairs"] = res
+    out["kernel_code_sha256_16"] = kernel_code_hash()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -643,6 +704,9 @@ def main() -> int:
                     help="instead of the benchmark line, time decode-size launches of both "
                          "operations (1-1024 tokens): back to back, graph replay, and one "
                          "launch on an idle GPU (one JSON line)")
+    ap.add_argument("--patterns", action="store_true",
+                    help="instead of the benchmark line, measure the strided-slice and NeoX "
+                         "pair-unit access patterns against dense ones (one JSON line)")
     ap.add_argument("--calibrate", action="store_true",
                     help="instead of the benchmark line, run one dense copy per workload that "
                          "reads as many bytes as the workload (for scaling the HBM byte "
@@ -672,6 +736,9 @@ def main() -> int:
         return 0
     if args.latency:
         print(json.dumps(latency(torch, ra, W, dev, cyc)), flush=True)
+        return 0
+    if args.patterns:
+        print(json.dumps(patterns(torch, ra, W, lib, dev, cyc)), flush=True)
         return 0
     names = [w.strip() for w in args.workloads.split(",") if w.strip()]
     if args.calibrate:

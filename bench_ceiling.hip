@@ -13,7 +13,12 @@
 //                  lanes in 16-byte loads, loaded once per lane): the access pattern of the
 //                  in-place RoPE kernel on a [rows, D] slice with its cos/sin rows, with the
 //                  rotation taken out.
-// Both return 0, or -1 for arguments outside their documented form and -2 if the launch
+//   ceiling_pairs  a copy of `heads` rows of `head_bytes` in the cache kernel's NeoX pair-unit
+//                  layout: a lane takes 16 bytes at u*16 of a head and 16 bytes half a head
+//                  further (head_bytes / 32 lanes per head, all of a wavefront's lanes on
+//                  whole heads), in `rows_per_lane` rows of heads (1 or 2), 256-lane
+//                  workgroups; with the rotation and the cos|sin gather taken out.
+// Each returns 0, or -1 for arguments outside their documented form and -2 if the launch
 // fails.  Everything is enqueued on `stream` (a hipStream_t, NULL = the null stream).
 #include <hip/hip_runtime.h>
 
@@ -76,6 +81,36 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(char *x, int64_t groups, i
   }
 }
 
+// Lane l of a wavefront owns unit u = l % units of head l / units, in each of K rows of
+// `hpw` heads; wavefront w covers heads [w*K*hpw, (w+1)*K*hpw).  Lanes past the last head
+// copy nothing.
+template <int K>
+__global__ __launch_bounds__(256) void pairs_kernel(u32x4 *dst, const u32x4 *src, int64_t heads,
+                                                   int64_t units, int64_t hpw, int64_t waves) {
+  const int64_t lane = threadIdx.x & 63, hsub = lane / units, u = lane - hsub * units;
+  const int64_t vpr = 2 * units;  // 16-byte vectors per head
+  for (int64_t w = (int64_t(blockIdx.x) * 256 + threadIdx.x) / 64; w < waves;
+       w += int64_t(gridDim.x) * 4) {
+    u32x4 a[K], b[K];
+    int64_t base[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      int64_t h = (w * K + k) * hpw + hsub;
+      h = (hsub < hpw && h < heads) ? h : heads - 1;  // idle lanes reload the last head
+      base[k] = h * vpr + u;
+      a[k] = __builtin_nontemporal_load(src + base[k]);
+      b[k] = __builtin_nontemporal_load(src + base[k] + units);
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t h = (w * K + k) * hpw + hsub;
+      if (hsub >= hpw || h >= heads) continue;
+      __builtin_nontemporal_store(a[k], dst + base[k]);
+      __builtin_nontemporal_store(b[k], dst + base[k] + units);
+    }
+  }
+}
+
 int64_t grid_for(int64_t lanes) {
   const int64_t g = (lanes + kBlock - 1) / kBlock;
   return g < 1 ? 1 : (g > kMaxGrid ? kMaxGrid : g);
@@ -127,5 +162,30 @@ extern "C" __attribute__((visibility("default"))) int ceiling_rows(
     else ROWS_LAUNCH(8, 4);
   }
 #undef ROWS_LAUNCH
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+extern "C" __attribute__((visibility("default"))) int ceiling_pairs(void *dst, const void *src,
+                                                                    int64_t heads,
+                                                                    int64_t head_bytes,
+                                                                    int64_t rows_per_lane,
+                                                                    void *stream) {
+  if (!dst || !src || heads <= 0 || head_bytes <= 0 || head_bytes % 32 ||
+      head_bytes / 32 > 64 || (rows_per_lane != 1 && rows_per_lane != 2) || !aligned(dst, 16) ||
+      !aligned(src, 16))
+    return -1;
+  const int64_t units = head_bytes / 32, hpw = 64 / units;
+  const int64_t per_wave = hpw * rows_per_lane, waves = (heads + per_wave - 1) / per_wave;
+  int64_t blocks = (waves + 3) / 4;
+  blocks = blocks > kMaxGrid ? kMaxGrid : blocks;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  u32x4 *d = static_cast<u32x4 *>(dst);
+  const u32x4 *c = static_cast<const u32x4 *>(src);
+  if (rows_per_lane == 1)
+    hipLaunchKernelGGL(pairs_kernel<1>, dim3(uint32_t(blocks)), dim3(256), 0, s, d, c, heads,
+                       units, hpw, waves);
+  else
+    hipLaunchKernelGGL(pairs_kernel<2>, dim3(uint32_t(blocks)), dim3(256), 0, s, d, c, heads,
+                       units, hpw, waves);
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }

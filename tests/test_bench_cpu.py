@@ -131,9 +131,8 @@ def test_ceiling_kernels_refuse_arguments_outside_their_form():
     run without a GPU): null or misaligned buffers, sizes that are not whole lanes, a slice past
     the row, lane widths and rows per lane outside {8, 16} and {1, 2, 4}."""
     lib = bench.load_ceiling()
-    buf = torch.zeros(1 << 16, dtype=torch.uint8)
-    p = buf.data_ptr()
-    assert p % 256 == 0
+    buf = torch.zeros((1 << 16) + 256, dtype=torch.uint8)
+    p = (buf.data_ptr() + 255) // 256 * 256  # 256-byte aligned, with 64 KiB behind it
     assert lib.ceiling_copy(None, p, 1024, None) == -1
     assert lib.ceiling_copy(p, p + 8, 1024, None) == -1            # misaligned source
     assert lib.ceiling_copy(p, p + 4096, 1000, None) == -1         # not whole 16-byte lanes
@@ -155,3 +154,7 @@ def test_ceiling_kernels_refuse_arguments_outside_their_form():
     assert rows(side=200) == -1                # side bytes not whole 16-byte loads per lane
     assert rows(rps=2) == -1                   # rows per lane sharing different side rows
     assert rows(sa=p + 8) == -1                # misaligned side array
+    assert lib.ceiling_pairs(p, p + 8192, 4, 256, 3, None) == -1       # rows per lane
+    assert lib.ceiling_pairs(p, p + 8192, 4, 240, 2, None) == -1       # not whole 32-byte units
+    assert lib.ceiling_pairs(p, p + 8192, 4, 4096, 2, None) == -1      # more than 64 lanes a head
+    assert lib.ceiling_pairs(p + 8, p + 8192, 4, 256, 2, None) == -1   # misaligned
