@@ -697,8 +697,8 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true",
                     help="time the launches only (no percentiles, graph replay or ceilings)")
     ap.add_argument("--sweep", action="store_true",
-                    help="instead of the benchmark line, time the headline in-place shape and "
-                         "the rope NeoX cache shape at 1..16x their tokens and fit fixed cost "
+                    help="instead of the benchmark line, time the [8,4096,1,576] in-place shape "
+                         "and the rope NeoX cache shape at 1..16x their tokens and fit fixed cost "
                          "+ bytes / marginal bandwidth (one JSON line)")
     ap.add_argument("--latency", action="store_true",
                     help="instead of the benchmark line, time decode-size launches of both "

@@ -218,7 +218,7 @@ def cache_mrope_interleaved(device="cpu"):
 
 
 def inplace_half_bf16_slice(device="cpu"):
-    """Half mode (rotary_mode 0) on the headline shape: bf16 x [8,4096,1,576], slice
+    """Half mode (rotary_mode 0) on the key-side slice shape: bf16 x [8,4096,1,576], slice
     [512,576), fp32 rotate-half cos/sin [8,4096,1,64]."""
     return inplace_case("inplace_half_bf16x_f32cs_8x4096x1x576_slice512_576", 8, 4096, 1, 576,
                         torch.bfloat16, torch.float32, [512, 576], seed=1007, device=device,
@@ -234,7 +234,7 @@ def inplace_heads_bf16_bs1d(device="cpu"):
 
 
 def inplace_bf16_slice_backward(device="cpu"):
-    """The gradient op on the headline shape: incoming gradient bf16 [8,4096,1,576]."""
+    """The gradient op on the key-side slice shape: incoming gradient bf16 [8,4096,1,576]."""
     case = inplace_bf16_slice(device)
     case.name = "inplace_backward_bf16_8x4096x1x576_s512"
     case.backward = True
@@ -253,5 +253,4 @@ CONFIGS["cache_mrope_interleaved_neox_bf16_t16384"] = cache_mrope_interleaved
 CONFIGS["inplace_half_bf16_8x4096x1x576_s512"] = inplace_half_bf16_slice
 CONFIGS["inplace_heads_bf16_4x2048x32x192_s128_bs1d"] = inplace_heads_bf16_bs1d
 CONFIGS["inplace_f32_1x524288x2x64"] = inplace_f32_scaled
-HEADLINE = "inplace_bf16_8x4096x1x576_s512"
 

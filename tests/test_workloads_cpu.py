@@ -71,7 +71,7 @@ def test_mrope_positions_text_then_image_grid():
     assert torch.equal(pos4[3], pos4[0])
 
 
-def test_headline_workload_shape_and_bytes():
+def test_key_side_slice_workload_shape_and_bytes():
     case = W.CONFIGS["inplace_bf16_8x4096x1x576_s512"]("cpu")
     assert case.x.shape == (8, 4096, 1, 576) and case.x.dtype == torch.bfloat16
     assert case.cos.shape == (8, 4096, 1, 64) and case.cos.dtype == torch.float32
