@@ -409,3 +409,34 @@ def test_pages_python_interface_rotary_mode_names():
     with pytest.raises(ra.RopeError) as e:   # host tensors are refused before the library
         ra.inplace_partial_rotary_mul(x, x[..., :8], x[..., :8], partial_slice=[0, 8])
     assert e.value.code == ra.ROPE_ERR_PARAM_INVALID
+
+
+def test_error_messages_are_per_thread():
+    """rope_last_error() reports the failure of the calling thread's own last call: threads
+    validating different bad calls at once (ctypes releases the GIL, so they run in parallel)
+    each read back exactly the status and message that call gives when made alone."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    picks = [c for c in INPLACE_CASES if c[2] != 0][::3]
+    calls = []
+    for name, build, _ in picks:
+        a = build(inplace_base())
+        arr, n = ints(a[4])
+        n = a[5] if len(a) > 5 else n
+        args = (lib_desc(a[0]), lib_desc(a[1]), lib_desc(a[2]), a[3], arr, n, None)
+        calls.append(args)
+    expected = []
+    for args in calls:
+        st = ra.LIB.rope_partial_inplace(*args)
+        expected.append((st, ra.last_error()))
+    assert len({m for _, m in expected}) > 5  # distinct messages, so a mix-up would show
+
+    def worker(i):
+        for _ in range(300):
+            st = ra.LIB.rope_partial_inplace(*calls[i])
+            if (st, ra.last_error()) != expected[i]:
+                return False
+        return True
+
+    with ThreadPoolExecutor(max_workers=len(calls)) as ex:
+        assert all(ex.map(worker, range(len(calls))))
