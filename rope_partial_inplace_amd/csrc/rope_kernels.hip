@@ -889,8 +889,9 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
 // ============================================================================================
 // K2, wavefront form (the plans it covers: 16-byte q/k and cache access, a head's units on at
 // most 64 lanes, 8-byte aligned positions).  The same operation as cos_sin_cache_kernel, with
-// one wavefront per (token, group of heads) and no LDS and no barrier.  Lane l owns unit u = l % units of head l / units in each
-// of kWaveItemsPerLane rows of wave_hpw heads, so its cos|sin chunk (NeoX: the V elements
+// one wavefront per (token, group of heads) and no LDS and no barrier.  Lane l owns unit
+// u = l % units of head l / units in each of K rows of wave_hpw heads (K: the plan's
+// wave_rows), so its cos|sin chunk (NeoX: the V elements
 // u*V...; GPT-J: the V/2 pair indices u*V/2...) is the same for all of its items and is read
 // straight from the token's cache row; the lanes of one unit read the same bytes, which the
 // caches serve.  The token's positions are wave-uniform and are read through the scalar
@@ -914,14 +915,13 @@ union CsChunk {
 // LIN (NeoX): a unit is one vector, as in GPT-J, so a head's vectors lie on consecutive lanes
 // and each access covers whole heads; the pair partner (R vectors away, R = rotaryDim/(2V))
 // is read from its lane with ds_bpermute, as in XCH.
-template <typename T, bool NEOX, bool MULTI, bool XCH, bool LIN>
+template <typename T, bool NEOX, bool MULTI, bool XCH, bool LIN, int K>
 __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePlan p) {
   static_assert(!(XCH || LIN) || NEOX, "the lane exchange is a NeoX layout");
   static_assert(!(XCH && LIN), "one layout at a time");
   constexpr bool EXCH = XCH || LIN;  // rotated vectors pair across lanes
   constexpr int V = Io<T>::kPer16;
   constexpr int NV = NEOX && !LIN ? 2 : 1;  // vectors per unit
-  constexpr int K = kWaveItemsPerLane;
   constexpr int C = NEOX ? V : V / 2;  // cos (and sin) elements of the lane's chunk
   constexpr int CB = C * int(sizeof(T));  // 16 bytes (NeoX) or 8 (GPT-J)
   constexpr int PW = Io<T>::kPerWord;
@@ -1028,6 +1028,12 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
       load_words<CB, false>(row + i0, cw.w);
       load_words<CB, false>(row + half + i0, sw.w);
     }
+    // Every load of the item is out: keep the compiler from moving work that waits for the
+    // q/k data above the cos/sin loads.  Left to itself it waited for the first q/k vector
+    // between the cos and the sin load of NeoX pair units, which serialized two round trips:
+    // with one head row per lane the rope NeoX workload took 30.4 us without this barrier and
+    // 28.7 us with it (29.6 us with two rows).
+    __builtin_amdgcn_sched_barrier(0);
     // rotate the first rd of every head, copy the rest as raw bits
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -1188,19 +1194,28 @@ const void *pick_cache_rows(bool neox, bool vec) {
 #undef ROPE_K2
 }
 
+// The wavefront kernel of a layout, with the head rows per lane the plan chose (a plan that
+// disagrees gets no kernel).
+template <typename T, bool NX, bool XC, bool LI>
+const void *pick_wave(const CachePlan &p) {
+  constexpr int KP = NX && !XC && !LI ? int(kWaveRowsPairUnits) : int(kWaveRowsVectorUnits);
+  constexpr int KM = int(kWaveRowsVectorUnits);  // multi-row stitching
+  if (p.multi_row)
+    return p.wave_rows == uint32_t(KM)
+               ? reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, true, XC, LI, KM>)
+               : nullptr;
+  return p.wave_rows == uint32_t(KP)
+             ? reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, false, XC, LI, KP>)
+             : nullptr;
+}
+
 template <typename T>
 const void *pick_cache(const CachePlan &p) {
   if (p.wave) {
-#define ROPE_K2W(NX, MU, XC, LI) \
-  reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, MU, XC, LI>)
-    if (p.neox && p.wave_lin)
-      return p.multi_row ? ROPE_K2W(true, true, false, true) : ROPE_K2W(true, false, false, true);
-    if (p.neox && p.wave_xch)
-      return p.multi_row ? ROPE_K2W(true, true, true, false) : ROPE_K2W(true, false, true, false);
-    if (p.neox)
-      return p.multi_row ? ROPE_K2W(true, true, false, false) : ROPE_K2W(true, false, false, false);
-    return p.multi_row ? ROPE_K2W(false, true, false, false) : ROPE_K2W(false, false, false, false);
-#undef ROPE_K2W
+    if (p.neox && p.wave_lin) return pick_wave<T, true, false, true>(p);
+    if (p.neox && p.wave_xch) return pick_wave<T, true, true, false>(p);
+    if (p.neox) return pick_wave<T, true, false, false>(p);
+    return pick_wave<T, false, false, false>(p);
   }
   if (p.cs_direct) return pick_cache_rows<T, false, true>(p.neox, p.vector_io);
   return p.multi_row ? pick_cache_rows<T, true, false>(p.neox, p.vector_io)
@@ -1278,6 +1293,10 @@ ROPE_API int rope_with_cos_sin_cache_v2(const rope_tensor *positions, const rope
   const void *fn = plan.dt == ROPE_F32   ? pick_cache<float>(plan)
                    : plan.dt == ROPE_F16 ? pick_cache<_Float16>(plan)
                                          : pick_cache<__bf16>(plan);
+  if (fn == nullptr) {
+    g_last_error = "internal: no kernel for this plan";
+    return ROPE_ERR_RUNTIME;
+  }
   if (plan.wave)
     return launch(fn, (plan.waves + kWaveBlock / 64 - 1) / (kWaveBlock / 64), kWaveBlock, 0,
                   stream, &plan);

@@ -499,11 +499,14 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
   const uint32_t lanes = lin ? 2 * p.units : p.units;  // lanes per head
   if (p.vector_io && p.cache_vec && lanes >= 1 && lanes <= 64 &&
       (reinterpret_cast<uintptr_t>(p.positions) & 7u) == 0) {
+    const uint32_t rows =
+        p.neox && !xch && !lin && !p.multi_row ? kWaveRowsPairUnits : kWaveRowsVectorUnits;
     const uint32_t hpw = 64u / lanes;
-    const uint32_t heads = uint32_t(kWaveItemsPerLane) * hpw;
+    const uint32_t heads = rows * hpw;
     const int64_t wpt = (p.nq + p.nk + heads - 1) / heads;
     if (wpt <= int64_t(0x7fffffff) && T <= kMaxWaves / wpt) {
       p.wave = true;
+      p.wave_rows = rows;
       p.wave_hpw = hpw;
       p.wave_heads = heads;
       p.wave_wpt = uint32_t(wpt);

@@ -110,12 +110,12 @@ struct CachePlan {
   uint32_t stage_chunks = 0;    // (rd/2) / vec: vector chunks of one cos (or sin) half-row
   FastDiv div_units, div_ipt, div_stage;
   // Wavefront path (cos_sin_cache_wave_kernel): one wavefront per (token, group of heads), no
-  // LDS.  Lane l owns unit l % units of head l / units of each of kWaveItemsPerLane rows of
-  // wave_hpw heads, so its cos|sin chunk is the same for all its items and is read straight
-  // from the cache row.  Lanes from wave_hpw * units up are idle.
+  // LDS.  Lane l owns unit l % units of head l / units of each of wave_rows rows of wave_hpw
+  // heads, so its cos|sin chunk is the same for all its items and is read straight from the
+  // cache row.  Lanes from wave_hpw * units up are idle.
   bool wave = false;
   uint32_t wave_hpw = 0;        // heads per row of 64 lanes: floor(64 / units)
-  uint32_t wave_heads = 0;      // heads per wavefront: kWaveItemsPerLane * wave_hpw
+  uint32_t wave_heads = 0;      // heads per wavefront: wave_rows * wave_hpw
   uint32_t wave_wpt = 0;        // wavefronts per token: ceil((nq + nk) / wave_heads)
   int64_t waves = 0;            // T * wave_wpt (< 2^31)
   FastDiv div_wpt;
@@ -126,6 +126,10 @@ struct CachePlan {
   // NeoX with one-vector units (a head's vectors on consecutive lanes, 2 * units lanes per
   // head); rotated pairs are completed by the same cross-lane read
   bool wave_lin = false;
+  // head rows per lane: kWaveRowsPairUnits (NeoX pair units without multi-row stitching) or
+  // kWaveRowsVectorUnits; the kernel has it as a template argument (last in the struct, so
+  // the fields the kernels read keep their offsets)
+  uint32_t wave_rows = 0;
 };
 
 int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor *sin,
@@ -163,12 +167,16 @@ constexpr int kCacheBlock = 256;  // cache kernel workgroup (one token tile)
 constexpr int64_t kTaperTokens = 1280;
 constexpr int kNeoxItemsPerLane = 2;  // NeoX units are two vectors
 constexpr int kGptjItemsPerLane = 2;  // GPT-J units are one vector
-// Wavefront cache kernel: 256-lane workgroups of four independent wavefronts, two items (head
-// rows) per lane.  Measured on the rope NeoX bf16, GPT-J f16 and mrope bf16 workloads against
-// one item per lane (3-30% slower) and three (2-6% slower); 64-lane workgroups were within 1%,
-// 512- and 1024-lane ones up to 8% slower.
+// Wavefront cache kernel: 256-lane workgroups of four independent wavefronts; 64-lane
+// workgroups were within 1%, 512- and 1024-lane ones up to 8% slower.  A lane carries two
+// 16-byte q/k vectors per wavefront: NeoX pair units (two vectors each) one head row, the
+// one-vector units of the other layouts two head rows.  Measured on the rope NeoX bf16, GPT-J
+// f16 and mrope bf16 workloads: one-vector units with one row were 3-30% slower and with three
+// rows 2-6% slower; pair units with one row 3% faster than with two, except under multi-row
+// stitching (three cos|sin gathers per lane), where one row was 2-3% slower.
 constexpr int kWaveBlock = 256;
-constexpr int kWaveItemsPerLane = 2;
+constexpr uint32_t kWaveRowsPairUnits = 1;
+constexpr uint32_t kWaveRowsVectorUnits = 2;
 // Waves of one launch stay below 2^31, so a wave index plus the grid stride fits 32 bits.
 constexpr int64_t kMaxWaves = (int64_t(1) << 31) - (int64_t(1) << 24);
 

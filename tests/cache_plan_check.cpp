@@ -88,7 +88,7 @@ static int wave_multi_row(const CachePlan &p, uint32_t i0, int j) {
 
 // The wavefront path (plan.wave): waves of 64 lanes, wave gw -> token gw / wave_wpt and head
 // group gw % wave_wpt; lane l -> unit l % units of head row l / units (idle from wave_hpw up);
-// kWaveItemsPerLane head rows of wave_hpw heads.  Checks that every output element is written
+// wave_rows head rows of wave_hpw heads.  Checks that every output element is written
 // once from its own input element, that every load (idle and clamped lanes included) stays
 // inside the input rows, that a rotated element reads the cos|sin entry of its own pair, and
 // that the position row of each cos|sin element is the one the stitching assigns.
@@ -101,7 +101,10 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
   CHECK(!p.wave_lin || (neox && !p.wave_xch), "one-vector NeoX units on a GPT-J or exchange plan");
   CHECK(lanes >= 1 && lanes <= 64 && p.wave_hpw == 64 / lanes, "wave plan lanes %u hpw %u",
         lanes, p.wave_hpw);
-  CHECK(p.wave_heads == uint32_t(kWaveItemsPerLane) * p.wave_hpw, "wave heads %u", p.wave_heads);
+  const bool pair_units = neox && !p.wave_xch && !p.wave_lin && !p.multi_row;
+  CHECK(p.wave_rows == (pair_units ? kWaveRowsPairUnits : kWaveRowsVectorUnits),
+        "wave rows %u", p.wave_rows);
+  CHECK(p.wave_heads == p.wave_rows * p.wave_hpw, "wave heads %u", p.wave_heads);
   CHECK(int64_t(p.wave_wpt) * p.wave_heads >= nh &&
             int64_t(p.wave_wpt - 1) * p.wave_heads < nh, "waves per token %u", p.wave_wpt);
   CHECK(p.waves == T * int64_t(p.wave_wpt) && p.waves < kMaxWaves, "waves %lld",
@@ -168,7 +171,7 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
       } else {
         offs = {int64_t(u) * V};
       }
-      for (int k = 0; k < kWaveItemsPerLane; ++k) {
+      for (int k = 0; k < int(p.wave_rows); ++k) {
         const int64_t h = hbase + int64_t(k) * p.wave_hpw;
         const int64_t hl = h < nh ? h : nh - 1;  // the head the loads address
         const bool lq = hl < nq;
