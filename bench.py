@@ -49,7 +49,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 # write-through variant of it 7-10%); from 1 GiB to 2 GiB the times are equal, and much
 # larger rotations start to add TLB misses of their own.
 MALL_DEFEAT_BYTES = 2 << 30
-KERNEL_SRC = os.path.join(ROOT, "rope_partial_inplace_amd", "csrc", "rope_kernels.hip")
+# The sources that decide what a launch does: the kernels and the launch plans (which kernel,
+# grid and layout a workload gets).
+KERNEL_SOURCES = [os.path.join(ROOT, "rope_partial_inplace_amd", "csrc", f)
+                  for f in ("rope_kernels.hip", "rope_plan.h", "rope_plan.cpp")]
 CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
 CEILING_LIB = os.path.join(ROOT, "libbench_ceiling.so")
 HEADLINE = "cache_rope_gptj_f16_t32768_rd64"
@@ -65,12 +68,16 @@ def log(msg: str):
 
 
 def kernel_code_hash() -> str:
-    """sha256[:16] of rope_kernels.hip with its // comments, trailing blanks and blank lines
-    removed: it changes when the kernels' code does, not when a comment is edited, so a
-    traffic figure stays attached to the code it was measured on."""
-    with open(KERNEL_SRC, encoding="utf-8") as f:
-        lines = [re.sub(r"//.*$", "", line).rstrip() for line in f.read().splitlines()]
-    return hashlib.sha256("\n".join(x for x in lines if x).encode()).hexdigest()[:16]
+    """sha256[:16] of the kernel and launch-plan sources with their // comments, trailing
+    blanks and blank lines removed: it changes when their code does, not when a comment is
+    edited, so a traffic figure stays attached to the code it was measured on."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, encoding="utf-8") as f:
+            lines = [re.sub(r"//.*$", "", line).rstrip() for line in f.read().splitlines()]
+        h.update(os.path.basename(path).encode() + b"\0")
+        h.update("\n".join(x for x in lines if x).encode() + b"\0")
+    return h.hexdigest()[:16]
 
 
 def build_ceiling(verbose: bool = False) -> str:

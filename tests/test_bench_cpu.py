@@ -27,7 +27,7 @@ def test_code_hash_ignores_comments_and_blank_lines(tmp_path, monkeypatch):
     code = "int f(int a) {\n  return a + 1;\n}\n"
     src = tmp_path / "k.hip"
     src.write_text(code)
-    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(src)])
     base = bench.kernel_code_hash()
     src.write_text("// a comment\n\nint f(int a) {  // trailing\n  return a + 1;   \n}\n\n")
     assert bench.kernel_code_hash() == base
@@ -158,3 +158,15 @@ def test_ceiling_kernels_refuse_arguments_outside_their_form():
     assert lib.ceiling_pairs(p, p + 8192, 4, 240, 2, None) == -1       # not whole 32-byte units
     assert lib.ceiling_pairs(p, p + 8192, 4, 4096, 2, None) == -1      # more than 64 lanes a head
     assert lib.ceiling_pairs(p + 8, p + 8192, 4, 256, 2, None) == -1   # misaligned
+
+
+def test_code_hash_covers_the_launch_plans(tmp_path, monkeypatch):
+    """A change to the plan code (which kernel, grid or layout a workload gets) also detaches
+    the traffic figures measured before it."""
+    k, plan = tmp_path / "k.hip", tmp_path / "plan.cpp"
+    k.write_text("int f(int a) { return a; }\n")
+    plan.write_text("int rows = 2;\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(k), str(plan)])
+    base = bench.kernel_code_hash()
+    plan.write_text("int rows = 1;\n")
+    assert bench.kernel_code_hash() != base
