@@ -891,11 +891,11 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
 // most 64 lanes, 8-byte aligned positions).  The same operation as cos_sin_cache_kernel, with
 // one wavefront per (token, group of heads) and no LDS and no barrier.  Lane l owns unit
 // u = l % units of head l / units in each of K rows of wave_hpw heads (K: the plan's
-// wave_rows), so its cos|sin chunk (NeoX: the V elements
-// u*V...; GPT-J: the V/2 pair indices u*V/2...) is the same for all of its items and is read
-// straight from the token's cache row; the lanes of one unit read the same bytes, which the
-// caches serve.  The token's positions are wave-uniform and are read through the scalar
-// cache, so waiting for them does not wait for the q/k loads in flight.
+// wave_rows, so that every lane carries two 16-byte q/k vectors), so its cos|sin chunk (NeoX:
+// the V elements u*V...; GPT-J: the V/2 pair indices u*V/2...) is the same for all of its items
+// and is read straight from the token's cache row; the lanes of one unit read the same bytes,
+// which the caches serve.  The token's positions are wave-uniform and are read through the
+// scalar cache, so waiting for them does not wait for the q/k loads in flight.
 // ============================================================================================
 typedef const __attribute__((address_space(4))) int64_t const_i64;
 
