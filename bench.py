@@ -290,13 +290,17 @@ def inplace_calls(ra, case, n_sets, sets=None):
 
 
 def cache_calls(ra, torch, case, n_sets):
+    """Launches over n_sets copies of every input, the cos/sin table included: a table shared
+    by the sets would stay in the Infinity Cache between launches (4% faster on the rope NeoX
+    workload), which a model's per-layer calls, with weights streaming in between, do not see."""
     calls = []
     for i in range(n_sets):
         q = case.query if i == 0 else case.query.clone()
         k = case.key if i == 0 else case.key.clone()
         p = case.positions if i == 0 else case.positions.clone()
+        c = case.cache if i == 0 else case.cache.clone()
         qo, ko = torch.empty_like(q), torch.empty_like(k)
-        calls.append(ra.prepare_with_cos_sin_cache(p, q, k, case.cache, case.mrope_section,
+        calls.append(ra.prepare_with_cos_sin_cache(p, q, k, c, case.mrope_section,
                                                    case.head_size, case.is_neox, qo, ko,
                                                    cache_mode=case.cache_mode))
     return calls
