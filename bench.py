@@ -374,8 +374,8 @@ def kernel_name(case) -> str:
 
 
 def traffic_for(workload: str):
-    """Measured HBM bytes per launch from the committed PMC summary, when it was taken
-    on the current kernel source; else None."""
+    """Measured HBM bytes per launch from the committed PMC summary, when it was taken on
+    the current kernel and launch-plan sources (kernel_code_hash); else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
