@@ -170,3 +170,26 @@ def test_code_hash_covers_the_launch_plans(tmp_path, monkeypatch):
     base = bench.kernel_code_hash()
     plan.write_text("int rows = 1;\n")
     assert bench.kernel_code_hash() != base
+
+
+def test_cache_buffer_sets_copy_every_input():
+    """Each buffer set of the cache op has its own q, k, positions and cos/sin table (so no
+    launch finds an input its predecessors left in the caches); set 0 is the case's own."""
+    seen = []
+
+    class FakeBinding:
+        @staticmethod
+        def prepare_with_cos_sin_cache(p, q, k, c, msec, H, neox, qo, ko, cache_mode=None):
+            seen.append((p, q, k, c, qo, ko))
+            return lambda: None
+
+    case = W.cache_case("sets", 5, 2, 1, 64, 64, torch.bfloat16, True, 40, seed=4)
+    bench.cache_calls(FakeBinding, torch, case, 3)
+    assert len(seen) == 3
+    assert all(a is b for a, b in zip(seen[0][:4], (case.positions, case.query, case.key,
+                                                 case.cache)))
+    for j in range(6):
+        ptrs = {s[j].data_ptr() for s in seen}
+        assert len(ptrs) == 3, f"argument {j} shared between buffer sets"
+    for s in seen[1:]:
+        assert torch.equal(s[3], case.cache) and torch.equal(s[0], case.positions)
