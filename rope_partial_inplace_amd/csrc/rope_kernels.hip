@@ -919,11 +919,13 @@ template <typename T, bool NEOX, bool MULTI, bool XCH, bool LIN, int K>
 __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePlan p) {
   static_assert(!(XCH || LIN) || NEOX, "the lane exchange is a NeoX layout");
   static_assert(!(XCH && LIN), "one layout at a time");
-  // GPT-J: the wavefront issues its loads at raised priority and drops back once they are all
-  // out (below), so that wavefronts starting up get their loads in ahead of the rotation and
-  // stores of older ones: GPT-J workloads 0.4-1% faster (the NeoX pair units 3% slower).
-  if constexpr (!NEOX) __builtin_amdgcn_s_setprio(3);
-  constexpr bool EXCH = XCH || LIN;  // rotated vectors pair across lanes
+  constexpr bool EXCH = XCH || LIN;
+  // One-vector units (GPT-J, LIN): the wavefront issues its loads at raised priority and drops
+  // back once they are all out (below), so that wavefronts starting up get their loads in ahead
+  // of the rotation and stores of older ones: GPT-J workloads 0.4-1% faster, LIN 6%; the pair
+  // units (3%) and the exchange layout (4-5%) were slower with it.
+  constexpr bool PRIO = !NEOX || LIN;
+  if constexpr (PRIO) __builtin_amdgcn_s_setprio(3);  // rotated vectors pair across lanes
   constexpr int V = Io<T>::kPer16;
   constexpr int NV = NEOX && !LIN ? 2 : 1;  // vectors per unit
   constexpr int C = NEOX ? V : V / 2;  // cos (and sin) elements of the lane's chunk
@@ -1038,7 +1040,7 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
     // with one head row per lane the rope NeoX workload took 30.4 us without this barrier and
     // 28.7 us with it (29.6 us with two rows).
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!NEOX) __builtin_amdgcn_s_setprio(0);
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     // rotate the first rd of every head, copy the rest as raw bits
 #pragma unroll
     for (int k = 0; k < K; ++k) {
