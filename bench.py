@@ -645,8 +645,8 @@ def patterns(torch, ra, W, lib, dev, cyc) -> dict:
         tables): the in-place kernel and its access pattern on each;
       - the NeoX pair units: a copy of the rope NeoX workload's q and k rows (8192 tokens x 40
         heads of 256 B) in the pair-unit layout (two 16-byte vectors half a head apart per
-        lane, two head rows per lane), against a dense copy of the same bytes, beside the
-        cache kernel on that workload."""
+        lane; one head row per lane, as the kernel takes it, and two), against a dense copy of
+        the same bytes, beside the cache kernel on that workload."""
     out = {}
     rows = {}
     for tag, D, sl in (("strided_1152B_rows", 576, [512, 576]), ("dense_128B_rows", 64, [0, 64])):
