@@ -165,7 +165,7 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
         if (rot) {
           offs = {int64_t(u) * V, half + int64_t(u) * V};
         } else {
-          const int64_t w = int64_t(u - p.rot_units) * V;
+          const int64_t w = int64_t(u - R) * V;
           offs = {rd + w, rd + (H - rd) / 2 + w};
         }
       } else {
@@ -209,7 +209,7 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
   return true;
 }
 
-static int wave_plans = 0, xch_plans = 0, lin_plans = 0;
+static int wave_plans = 0, xch_plans = 0, lin_plans = 0, pair_plans = 0, wide_pair_plans = 0;
 // Every g_stride-th plan is walked (1: all of them); runs under the sanitizers use a sparser
 // sample of the same plans.
 static int g_stride = 1, g_seen = 0, g_walked = 0;
@@ -371,6 +371,8 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
     ++wave_plans;
     xch_plans += p.wave_xch ? 1 : 0;
     lin_plans += p.wave_lin ? 1 : 0;
+    pair_plans += neox && !p.wave_xch && !p.wave_lin ? 1 : 0;
+    wide_pair_plans += neox && !p.wave_xch && !p.wave_lin && p.units > 32 ? 1 : 0;
     return walk_waves(p, neox, T, nq, nk, H, rd, sec, cache_mode, qs);
   }
   return true;
@@ -403,6 +405,18 @@ int main(int argc, char **argv) {
                 }
         }
   }
+  // wide NeoX heads on the wavefront path: 20 to 64 units (lanes) a head, rotaryDim H and H/2
+  // (units a multiple of 4, so that H/2 is a 64-byte multiple)
+  for (rope_dtype dt : {ROPE_F32, ROPE_BF16}) {
+    const int64_t v = dt == ROPE_F32 ? 4 : 8;
+    for (int64_t units : {int64_t(20), int64_t(32), int64_t(36), int64_t(48), int64_t(64)})
+      for (int64_t T : {int64_t(1), int64_t(9), int64_t(300)}) {
+        const int64_t H = 2 * v * units;
+        if (!walk(dt, true, T, 3, 2, H, H, {}, 0, 0)) return 1;
+        if (!walk(dt, true, T, 2, 1, H, H / 2, {}, 0, 0)) return 1;
+        plans += 2;
+      }
+  }
   // plans the wavefront path does not take: heads of more than 64 units, positions not
   // 8-byte aligned
   for (rope_dtype dt : {ROPE_F32, ROPE_BF16})
@@ -424,14 +438,17 @@ int main(int argc, char **argv) {
           ++plans;
         }
     }
-  if (wave_plans == 0 || wave_plans == g_walked || xch_plans == 0 || lin_plans == 0) {
+  if (wave_plans == 0 || wave_plans == g_walked || xch_plans == 0 || lin_plans == 0 ||
+      pair_plans == 0 || wide_pair_plans == 0) {
     std::printf("FAIL: %d of %d plans take the wavefront path (%d exchange, %d one-vector "
-                "NeoX); every path and layout must be covered\n",
-                wave_plans, g_walked, xch_plans, lin_plans);
+                "NeoX, %d pair units, %d of them over 32 lanes a head); every path and layout "
+                "must be covered\n",
+                wave_plans, g_walked, xch_plans, lin_plans, pair_plans, wide_pair_plans);
     return 1;
   }
   std::printf("ok %d %llu (%d walked, %d on the wavefront path: %d exchange, %d one-vector "
-              "NeoX)\n", plans, (unsigned long long)items_checked, g_walked, wave_plans,
-              xch_plans, lin_plans);
+              "NeoX, %d pair units, %d of them over 32 lanes a head)\n", plans,
+              (unsigned long long)items_checked, g_walked, wave_plans, xch_plans, lin_plans,
+              pair_plans, wide_pair_plans);
   return 0;
 }
