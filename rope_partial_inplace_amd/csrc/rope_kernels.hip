@@ -374,15 +374,16 @@ __device__ inline void rotate_pair(float a, float b, float c0, float c1, float s
 // is that of (b, s, head g * NHL).
 template <typename XT, typename CT, bool VEC, int NHL, bool CNT, bool BWD, bool HALF, bool XCH,
           bool PAD>
-__device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, uint64_t chunk,
-                                             uint64_t b, uint64_t s, uint64_t g) {
+// xrow: first element of the item's row group in x (r * nhl * D); crow_el: first element of
+// its cos/sin row (crow * L).
+__device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t chunk, int64_t xrow,
+                                             int64_t crow_el) {
   // one 16-byte access per lane for the wider of x and cos/sin, 8 bytes for the narrower;
   // element access: one pair (2 elements) in interleave mode, one element per half in HALF
   constexpr int V =
       VEC ? 16 / (sizeof(XT) > sizeof(CT) ? int(sizeof(XT)) : int(sizeof(CT))) : (HALF ? 1 : 2);
   constexpr int NH = HALF && !XCH ? 2 : 1;  // chunks per head: one, or one in each half
   const int64_t hoff = HALF ? p.L / 2 : 0;  // offset of the second half
-  const int64_t crow = int64_t(b) * p.cb + int64_t(s) * p.cs + int64_t(g) * NHL * p.cn;
   // element offset of the chunk in the slice.  PAD (XCH with a half's chunk count below the
   // power of two xch): chunk c of the first half or of the second (chunk >= xch), the lanes
   // past a half's last chunk loading that chunk and storing nothing
@@ -393,8 +394,8 @@ __device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, u
     owns = c < p.xch_cph;
     elem = (chunk >= p.xch ? p.L / 2 : 0) + int64_t(owns ? c : p.xch_cph - 1) * V;
   }
-  const int64_t coff = crow * p.L + elem;
-  const int64_t x0 = int64_t(r) * NHL * p.D + p.start + elem;
+  const int64_t coff = crow_el + elem;
+  const int64_t x0 = xrow + p.start + elem;
   float xv[NHL][NH][V], cv[NH][V], sv[NH][V];
   float xpv[XCH ? NHL : 1][V], spv[XCH && BWD ? V : 1];  // XCH: the partner lane's x, sin
   if constexpr (VEC) {
@@ -494,19 +495,32 @@ __device__ __forceinline__ void inplace_item(const InplacePlan &p, uint64_t r, u
 template <typename XT, typename CT, bool VEC, int NHL, bool CNT, bool BWD, bool HALF, bool XCH,
           bool PAD>
 __global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
-  // item it -> (row group r = (b, s, head group g), chunk).  Two loops: 32-bit indices with
-  // multiply-high division (the usual case), and plain 64-bit division for huge tensors, kept
-  // apart so that the 64-bit division setup never runs in the 32-bit case.
+  // item it -> (row group r = (b, s, head group g), chunk) and the cos/sin row of r.  Two
+  // loops: 32-bit indices with multiply-high division (the usual case), and plain 64-bit
+  // division for huge tensors, kept apart so that the 64-bit division setup never runs in the
+  // 32-bit case.
+  // The grid stride is taken at entry, so that the grid size is read with the first round of
+  // scalar argument loads: left in the loop, it was read in a third dependent round before
+  // any lane could issue its loads (the 25 MB bf16 launch took 6.1-6.2 us that way, 5.9-6.0
+  // with the stride here).
+  const uint32_t stride = gridDim.x * p.block;
+  asm volatile("" ::"s"(stride));
   if (p.idx32) {
-    const uint32_t items = uint32_t(p.items), ng = uint32_t(p.N / NHL);
-    for (uint32_t it = blockIdx.x * p.block + threadIdx.x; it < items; it += gridDim.x * p.block) {
+    const uint32_t items = uint32_t(p.items);
+    for (uint32_t it = blockIdx.x * p.block + threadIdx.x; it < items; it += stride) {
       const uint32_t r = fdiv(p.div_cpr, it);
       const uint32_t chunk = it - r * p.chunks_per_row;
-      const uint32_t bs = fdiv(p.div_ng, r);
-      const uint32_t g = r - bs * ng;
-      const uint32_t b = fdiv(p.div_s, bs);
-      const uint32_t s = bs - b * uint32_t(p.S);
-      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF, XCH, PAD>(p, r, chunk, b, s, g);
+      // the cos/sin row from r directly (InplacePlan::crow_a; arithmetic mod 2^32, the row
+      // is below 2^31): the common layouts skip one or both divisions, and the two that
+      // remain do not wait for each other
+      uint32_t crow = r * p.crow_a;
+      if (p.crow_b != 0) crow += fdiv(p.div_ng, r) * p.crow_b;
+      if (p.crow_c != 0) crow += fdiv(p.div_ngs, r) * p.crow_c;
+      // nhl * D and L are below 2^32 here: each offset is one 32 x 32 -> 64-bit product
+      const uint64_t xrow = uint64_t(r) * uint32_t(p.D * NHL);
+      const uint64_t crow_el = uint64_t(crow) * uint32_t(p.L);
+      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF, XCH, PAD>(p, chunk, int64_t(xrow),
+                                                               int64_t(crow_el));
     }
   } else {
     const uint64_t items = uint64_t(p.items), ng = uint64_t(p.N) / NHL;
@@ -518,7 +532,9 @@ __global__ __launch_bounds__(kBlock) void inplace_rope_kernel(InplacePlan p) {
       const uint64_t g = r - bs * ng;
       const uint64_t b = bs / uint64_t(p.S);
       const uint64_t s = bs - b * uint64_t(p.S);
-      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF, XCH, PAD>(p, r, chunk, b, s, g);
+      const int64_t crow = int64_t(b) * p.cb + int64_t(s) * p.cs + int64_t(g) * NHL * p.cn;
+      inplace_item<XT, CT, VEC, NHL, CNT, BWD, HALF, XCH, PAD>(p, chunk, int64_t(r) * NHL * p.D,
+                                                               crow * p.L);
     }
   }
 }

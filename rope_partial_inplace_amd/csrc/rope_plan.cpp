@@ -252,8 +252,29 @@ int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor
   p.block = p.items > kOneRoundLanes ? uint32_t(kBlockMulti) : block;
   p.div_cpr = make_fastdiv(p.chunks_per_row);
   p.div_ng = make_fastdiv(uint32_t(std::min<int64_t>(ng, 0xffffffff)));
-  p.div_s = make_fastdiv(uint32_t(std::min<int64_t>(p.S, 0xffffffff)));
-  if (ng > 0xffffffffLL || p.S > 0xffffffffLL) p.idx32 = false;
+  if (ng > 0xffffffffLL || p.S > 0xffffffffLL || int64_t(p.nhl) * D > 0xffffffffLL)
+    p.idx32 = false;
+  if (p.idx32) {
+    // cos/sin row = r*a + (r / ng)*bq + (r / (ng*S))*c (InplacePlan::crow_a); ng * S is at most
+    // the item count, so both divisors fit 32 bits.  Terms that coincide are merged: with
+    // B = 1, b = r / (ng*S) is 0; with S = 1, r / (ng*S) = r / ng; with ng = 1, r / ng = r.
+    int64_t a = int64_t(p.nhl) * p.cn;
+    int64_t bq = p.cs - ng * a;
+    int64_t c = p.cb - p.S * p.cs;
+    if (p.B == 1) c = 0;
+    if (p.S == 1) {
+      bq += c;
+      c = 0;
+    }
+    if (ng == 1) {
+      a += bq;
+      bq = 0;
+    }
+    p.crow_a = uint32_t(a);
+    p.crow_b = uint32_t(bq);
+    p.crow_c = uint32_t(c);
+    p.div_ngs = make_fastdiv(uint32_t(ng * p.S));
+  }
   return ROPE_OK;
 }
 

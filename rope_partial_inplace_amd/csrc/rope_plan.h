@@ -67,9 +67,18 @@ struct InplacePlan {
   // cos/sin row of x-row (b, s, n) = b*cb + s*cs + n*cn (in rows of L elements)
   int64_t cb = 0, cs = 0, cn = 0;
   bool cos_stream = false;  // every cos/sin row is read by exactly one lane group (streamed)
-  bool idx32 = true;  // rows and items fit in 32 bits: use FastDiv below
-  FastDiv div_cpr, div_ng, div_s;  // by chunks_per_row, N / nhl, S
+  bool idx32 = true;  // items, N / nhl, S and nhl * D fit in 32 bits: use FastDiv below
+  FastDiv div_cpr, div_ng;  // by chunks_per_row, N / nhl
   uint32_t block = 1024;  // workgroup size: kBlock, or kBlockMulti past one round of lanes
+  // The cos/sin row of row group r = (b*S + s)*ng + g (ng = N / nhl), written without
+  // decoding b, s and g:  b*cb + s*cs + g*nhl*cn = r*crow_a + (r / ng)*crow_b + (r / (ng*S))*crow_c
+  // (as g = r - ng*(r/ng), s = r/ng - S*(r/(ng*S)) and b = r/(ng*S)).  The coefficients are
+  // taken mod 2^32 (crow_b and crow_c may be negative); the row itself is below 2^31 wherever
+  // the 32-bit item loop runs.  A zero coefficient skips its division: per-head tables, and
+  // tables shared over N when a row holds one head group, need none; tables shared by several
+  // head groups of a (b, s) need one.
+  uint32_t crow_a = 0, crow_b = 0, crow_c = 0;
+  FastDiv div_ngs;  // by ng * S
 };
 
 // ---- cos/sin cache --------------------------------------------------------------------------

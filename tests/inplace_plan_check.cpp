@@ -43,10 +43,14 @@ static rope_tensor desc(uintptr_t addr, rope_dtype dt, int64_t B, int64_t S, int
 
 static int esize(rope_dtype dt) { return dt == ROPE_F32 ? 4 : 2; }
 
-// The decode of inplace_rope_kernel: item -> (r, chunk, b, s, g), then the first x element
-// and the first cos/sin element of the item's chunk.
+// The decode of inplace_rope_kernel: item -> (r, chunk) and the cos/sin row of r, then the
+// first x element and the first cos/sin element of the item's chunk.  The 32-bit decode takes
+// the cos/sin row from the plan's coefficients (arithmetic mod 2^32, skipping the divisions
+// of zero coefficients), as the kernel does; the 64-bit one from (b, s, g).  (b, s, g) are
+// also decoded here by plain division, for the range checks.
 struct Decoded {
   uint64_t r, chunk, b, s, g;
+  int64_t crow;
 };
 
 static Decoded decode(const InplacePlan &p, uint64_t it) {
@@ -57,19 +61,19 @@ static Decoded decode(const InplacePlan &p, uint64_t it) {
     const uint32_t r = fastdiv_host(p.div_cpr, i32);
     d.r = r;
     d.chunk = i32 - r * p.chunks_per_row;
-    const uint32_t bs = fastdiv_host(p.div_ng, r);
-    d.g = r - bs * uint32_t(ng);
-    const uint32_t b = fastdiv_host(p.div_s, bs);
-    d.b = b;
-    d.s = bs - b * uint32_t(p.S);
+    uint32_t crow = r * p.crow_a;
+    if (p.crow_b != 0) crow += fastdiv_host(p.div_ng, r) * p.crow_b;
+    if (p.crow_c != 0) crow += fastdiv_host(p.div_ngs, r) * p.crow_c;
+    d.crow = int64_t(crow);
   } else {
     d.r = it / p.chunks_per_row;
     d.chunk = it - d.r * p.chunks_per_row;
-    const uint64_t bs = d.r / ng;
-    d.g = d.r - bs * ng;
-    d.b = bs / uint64_t(p.S);
-    d.s = bs - d.b * uint64_t(p.S);
   }
+  const uint64_t bs = d.r / ng;
+  d.g = d.r - bs * ng;
+  d.b = bs / uint64_t(p.S);
+  d.s = bs - d.b * uint64_t(p.S);
+  if (!p.idx32) d.crow = int64_t(d.b) * p.cb + int64_t(d.s) * p.cs + int64_t(d.g) * p.nhl * p.cn;
   return d;
 }
 
@@ -113,6 +117,11 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
         p.xch_cph, p.chunks_per_row, (long long)V, (long long)L);
   CHECK(!p.idx32 || uint64_t(p.items) - 1 + uint64_t(kMaxGrid) * p.block < (uint64_t(1) << 32),
         "32-bit item index can wrap: items %lld, block %u", (long long)p.items, p.block);
+  // the 32-bit loop forms its offsets as 32 x 32 -> 64-bit products of r with nhl * D, and of
+  // the cos/sin row with L
+  CHECK(!p.idx32 || (uint64_t(p.nhl) * uint64_t(D) < (uint64_t(1) << 32) &&
+                     uint64_t(L) < (uint64_t(1) << 32)),
+        "32-bit plan with nhl * D = %llu", (unsigned long long)(p.nhl * D));
   {
     // the largest power-of-two workgroup (1024 down to 64) that gives each CU one, or 512
     // lanes past one round of resident lanes
@@ -138,7 +147,7 @@ static bool walk(int64_t B, int64_t S, int64_t N, int64_t D, int64_t start, int6
     CHECK(d.b < uint64_t(B) && d.s < uint64_t(S) && d.g * NHL < uint64_t(N) &&
               d.chunk < p.chunks_per_row,
           "item %llu decodes out of range", (unsigned long long)it);
-    const int64_t crow = int64_t(d.b) * p.cb + int64_t(d.s) * p.cs + int64_t(d.g) * NHL * p.cn;
+    const int64_t crow = d.crow;
     // the kernel's element offset of a chunk (XCH: half, then chunk of the half; a lane past
     // a half's last chunk loads that chunk and stores nothing)
     auto elem_of = [&](uint64_t chunk, bool *owns) {
@@ -243,6 +252,38 @@ static bool huge() {
   return true;
 }
 
+// The layouts that skip divisions in the kernel's cos/sin row: per-head tables and tables
+// shared by one head group per row need none, tables shared by several head groups one (by
+// the head groups per row); broadcast over B or S needs both.
+static bool division_free() {
+  struct Case {
+    int64_t B, S, N, D, start, end, Bc, Sc, Nc;
+    rope_dtype xdt;
+    bool want_b, want_c;
+  };
+  const Case cases[] = {
+      {8, 4096, 1, 576, 512, 576, 8, 4096, 1, ROPE_BF16, false, false},  // one head, BS1D
+      {4, 2048, 32, 192, 128, 192, 4, 2048, 1, ROPE_BF16, true, false},  // 32 heads, BS1D
+      {1, 524288, 2, 64, 0, 64, 1, 524288, 1, ROPE_F32, false, false},   // 2 heads on a lane
+      {2, 16, 8, 128, 0, 128, 2, 16, 8, ROPE_BF16, false, false},        // BSND
+      {2, 16, 8, 128, 0, 128, 1, 16, 8, ROPE_BF16, false, true},         // 1SND
+      {2, 16, 8, 128, 0, 128, 2, 1, 8, ROPE_BF16, true, true},           // B1ND
+  };
+  for (const Case &k : cases) {
+    const rope_tensor x = desc(0x10000000, k.xdt, k.B, k.S, k.N, k.D);
+    const rope_tensor c = desc(0x90000000, ROPE_F32, k.Bc, k.Sc, k.Nc, k.end - k.start);
+    const int64_t sl[2] = {k.start, k.end};
+    InplacePlan p;
+    std::string err;
+    CHECK(plan_inplace(&x, &c, &c, 1, sl, 2, &p, &err) == ROPE_OK, "%s", err.c_str());
+    CHECK(p.idx32 && (p.crow_b != 0) == k.want_b && (p.crow_c != 0) == k.want_c,
+          "[%lld,%lld,%lld,%lld] cos [%lld,%lld,%lld]: coefficients %u %u %u",
+          (long long)k.B, (long long)k.S, (long long)k.N, (long long)k.D, (long long)k.Bc,
+          (long long)k.Sc, (long long)k.Nc, p.crow_a, p.crow_b, p.crow_c);
+  }
+  return true;
+}
+
 int main() {
   int plans = 0;
   const rope_dtype pairs[5][2] = {{ROPE_F32, ROPE_F32}, {ROPE_F16, ROPE_F16}, {ROPE_F16, ROPE_F32},
@@ -258,19 +299,19 @@ int main() {
   for (const auto &sh : shapes)
     for (const auto &pr : pairs)
       for (int mode = 0; mode < 2; ++mode)
-        for (int lay = 0; lay < 6; ++lay)
+        for (int lay = 0; lay < 8; ++lay)
           for (uintptr_t mis : {uintptr_t(0), uintptr_t(2)}) {
             if (mis && pr[0] == ROPE_F32) continue;  // a 2-byte offset of an f32 tensor
-            const int64_t Bc = (lay == 4 || lay == 5) ? 1 : sh.B;
-            const int64_t Sc = (lay == 2 || lay == 3 || lay == 4) ? 1 : sh.S;
-            const int64_t Nc = (lay == 0 || lay == 2 || lay == 5) ? sh.N : 1;
-            // lay: 0 BSND, 1 BS1D, 2 B1ND, 3 B11D, 4 111D, 5 1SND
+            const int64_t Bc = (lay >= 4) ? 1 : sh.B;
+            const int64_t Sc = (lay == 2 || lay == 3 || lay == 4 || lay == 7) ? 1 : sh.S;
+            const int64_t Nc = (lay == 0 || lay == 2 || lay == 5 || lay == 7) ? sh.N : 1;
+            // lay: 0 BSND, 1 BS1D, 2 B1ND, 3 B11D, 4 111D, 5 1SND, 6 1S1D, 7 11ND
             if (!walk(sh.B, sh.S, sh.N, sh.D, sh.start, sh.end, Bc, Sc, Nc, pr[0], pr[1], mode,
                       mis * esize(pr[0]) / 2))
               return 1;
             ++plans;
           }
-  if (!limits() || !huge()) return 1;
+  if (!limits() || !huge() || !division_free()) return 1;
   if (padded_plans == 0) {
     std::printf("FAIL: no half-mode plan pads its lane pairs\n");
     return 1;
