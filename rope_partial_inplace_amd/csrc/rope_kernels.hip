@@ -931,10 +931,13 @@ union CsChunk {
 // LIN (NeoX): a unit is one vector, as in GPT-J, so a head's vectors lie on consecutive lanes
 // and each access covers whole heads; the pair partner (R vectors away, R = rotaryDim/(2V))
 // is read from its lane with ds_bpermute, as in XCH.
-template <typename T, bool NEOX, bool MULTI, bool XCH, bool LIN, int K>
+// MR: mrope (several position rows; always with MULTI); otherwise rope mode, whose wavefronts
+// read one position and no section table.
+template <typename T, bool NEOX, bool MULTI, bool XCH, bool LIN, bool MR, int K>
 __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePlan p) {
   static_assert(!(XCH || LIN) || NEOX, "the lane exchange is a NeoX layout");
   static_assert(!(XCH && LIN), "one layout at a time");
+  static_assert(MR || !MULTI, "multi-row stitching is an mrope layout");
   constexpr bool EXCH = XCH || LIN;
   // One-vector units (GPT-J, LIN): the wavefront issues its loads at raised priority and drops
   // back once they are all out (below), so that wavefronts starting up get their loads in ahead
@@ -990,17 +993,20 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
     multi_rows<C>(p, uint32_t(i0), rows);
 #pragma unroll
     for (int j = 0; j < C; ++j) rmask |= uint32_t(rows[j]) << (2 * j);
-  } else if (p.mrope) {
+  } else if constexpr (MR) {
     sec = mrope_section_of(p, i0);
   }
   const_i64 *pos_s = reinterpret_cast<const_i64 *>(reinterpret_cast<uintptr_t>(p.positions));
-  // offsets of position rows 0..3 (rows past the last one repeat it): four unconditional
-  // loads, which the compiler keeps in flight across the q/k loads (loads under a branch
-  // were waited for before the q/k loads went out)
-  const int nrows = p.mrope ? p.nsec : 1;
-  int64_t roff[4];
+  // mrope: offsets of position rows 0..3 (rows past the last one repeat it): four
+  // unconditional loads, which the compiler keeps in flight across the q/k loads (loads under
+  // a branch were waited for before the q/k loads went out).  Rope mode reads one row: with
+  // the four loads of one address, the rope NeoX bf16 workload took 29.7-29.9 us, 28.8-28.9
+  // with one.
+  constexpr int NR = MR ? 4 : 1;
+  const int nrows = MR ? p.nsec : 1;
+  int64_t roff[NR];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) roff[r] = int64_t(r < nrows ? r : nrows - 1) * p.pos_stride_row;
+  for (int r = 0; r < NR; ++r) roff[r] = int64_t(r < nrows ? r : nrows - 1) * p.pos_stride_row;
   constexpr uint32_t kWpb = kWaveBlock / 64;
   for (uint32_t gw = __builtin_amdgcn_readfirstlane(blockIdx.x * kWpb + threadIdx.x / 64);
        gw < uint32_t(p.waves); gw += gridDim.x * kWpb) {
@@ -1009,9 +1015,9 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
     const int64_t hbase = int64_t(gw - t32 * p.wave_wpt) * p.wave_heads + hs;
     // the token's position rows (wave-uniform scalar loads; they go out with the q/k loads
     // below and are waited for only after those, see the asm statement)
-    int64_t prow[4];
+    int64_t prow[NR];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) prow[r] = pos_s[roff[r] + t * p.pos_stride_tok];
+    for (int r = 0; r < NR; ++r) prow[r] = pos_s[roff[r] + t * p.pos_stride_tok];
     // q/k loads of every item (a lane past the last head loads the last head again and
     // stores nothing)
     RawN<T, V, true> v[K][NV];
@@ -1027,7 +1033,8 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
     }
     // All four positions are needed here, after the q/k loads went out: otherwise the compiler
     // moves each scalar load under the per-lane row choice below and waits for them in turn.
-    asm volatile("" ::"s"(prow[0]), "s"(prow[1]), "s"(prow[2]), "s"(prow[3]));
+    if constexpr (MR) asm volatile("" ::"s"(prow[0]), "s"(prow[1]), "s"(prow[2]), "s"(prow[3]));
+    else asm volatile("" ::"s"(prow[0]));
     // the lane's cos and sin chunks: gather, split, stitch
     CsChunk<T, CB> cw, sw;
     if constexpr (MULTI) {
@@ -1045,7 +1052,9 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
         sw.e[j] = r == 0 ? sr[0].e[j] : r == 1 ? sr[1].e[j] : sr[2].e[j];
       }
     } else {
-      const int64_t pos = sec == 0 ? prow[0] : sec == 1 ? prow[1] : sec == 2 ? prow[2] : prow[3];
+      int64_t pos = prow[0];
+      if constexpr (MR)
+        pos = sec == 0 ? prow[0] : sec == 1 ? prow[1] : sec == 2 ? prow[2] : prow[3];
       const T *row = static_cast<const T *>(p.cache) + clamp_position(p, pos) * p.cache_stride;
       load_words<CB, false>(row + i0, cw.w);
       load_words<CB, false>(row + half + i0, sw.w);
@@ -1223,13 +1232,12 @@ template <typename T, bool NX, bool XC, bool LI>
 const void *pick_wave(const CachePlan &p) {
   constexpr int KP = NX && !XC && !LI ? int(kWaveRowsPairUnits) : int(kWaveRowsVectorUnits);
   constexpr int KM = int(kWaveRowsVectorUnits);  // multi-row stitching
-  if (p.multi_row)
-    return p.wave_rows == uint32_t(KM)
-               ? reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, true, XC, LI, KM>)
-               : nullptr;
-  return p.wave_rows == uint32_t(KP)
-             ? reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, false, XC, LI, KP>)
-             : nullptr;
+#define ROPE_KW(MU, MR, KK) \
+  reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, MU, XC, LI, MR, KK>)
+  if (p.multi_row) return p.wave_rows == uint32_t(KM) ? ROPE_KW(true, true, KM) : nullptr;
+  if (p.wave_rows != uint32_t(KP)) return nullptr;
+  return p.mrope ? ROPE_KW(false, true, KP) : ROPE_KW(false, false, KP);
+#undef ROPE_KW
 }
 
 template <typename T>
