@@ -931,13 +931,15 @@ union CsChunk {
 // LIN (NeoX): a unit is one vector, as in GPT-J, so a head's vectors lie on consecutive lanes
 // and each access covers whole heads; the pair partner (R vectors away, R = rotaryDim/(2V))
 // is read from its lane with ds_bpermute, as in XCH.
-// MR: mrope (several position rows; always with MULTI); otherwise rope mode, whose wavefronts
-// read one position and no section table.
-template <typename T, bool NEOX, bool MULTI, bool XCH, bool LIN, bool MR, int K>
+// NR: position rows read per token: 1 in rope mode (no section table), else the mrope
+// section count (3 or 4; multi-row stitching has 3).
+template <typename T, bool NEOX, bool MULTI, bool XCH, bool LIN, int NR, int K>
 __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePlan p) {
   static_assert(!(XCH || LIN) || NEOX, "the lane exchange is a NeoX layout");
   static_assert(!(XCH && LIN), "one layout at a time");
-  static_assert(MR || !MULTI, "multi-row stitching is an mrope layout");
+  static_assert(NR == 1 || NR == 3 || NR == 4, "rope mode or an mrope section count");
+  static_assert(!MULTI || NR == 3, "multi-row stitching reads three rows");
+  constexpr bool MR = NR > 1;
   constexpr bool EXCH = XCH || LIN;
   // One-vector units (GPT-J, LIN): the wavefront issues its loads at raised priority and drops
   // back once they are all out (below), so that wavefronts starting up get their loads in ahead
@@ -997,16 +999,13 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
     sec = mrope_section_of(p, i0);
   }
   const_i64 *pos_s = reinterpret_cast<const_i64 *>(reinterpret_cast<uintptr_t>(p.positions));
-  // mrope: offsets of position rows 0..3 (rows past the last one repeat it): four
-  // unconditional loads, which the compiler keeps in flight across the q/k loads (loads under
-  // a branch were waited for before the q/k loads went out).  Rope mode reads one row: with
-  // the four loads of one address, the rope NeoX bf16 workload took 29.7-29.9 us, 28.8-28.9
-  // with one.
-  constexpr int NR = MR ? 4 : 1;
-  const int nrows = MR ? p.nsec : 1;
+  // Offsets of the NR position rows: unconditional loads, which the compiler keeps in flight
+  // across the q/k loads (loads under a branch were waited for before the q/k loads went
+  // out).  Exactly the rows the plan has: with four loads of one address in rope mode, the
+  // rope NeoX bf16 workload took 29.7-29.9 us, 28.8-28.9 with one.
   int64_t roff[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) roff[r] = int64_t(r < nrows ? r : nrows - 1) * p.pos_stride_row;
+  for (int r = 0; r < NR; ++r) roff[r] = int64_t(r) * p.pos_stride_row;
   constexpr uint32_t kWpb = kWaveBlock / 64;
   for (uint32_t gw = __builtin_amdgcn_readfirstlane(blockIdx.x * kWpb + threadIdx.x / 64);
        gw < uint32_t(p.waves); gw += gridDim.x * kWpb) {
@@ -1033,7 +1032,8 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
     }
     // All four positions are needed here, after the q/k loads went out: otherwise the compiler
     // moves each scalar load under the per-lane row choice below and waits for them in turn.
-    if constexpr (MR) asm volatile("" ::"s"(prow[0]), "s"(prow[1]), "s"(prow[2]), "s"(prow[3]));
+    if constexpr (NR == 4) asm volatile("" ::"s"(prow[0]), "s"(prow[1]), "s"(prow[2]), "s"(prow[3]));
+    else if constexpr (NR == 3) asm volatile("" ::"s"(prow[0]), "s"(prow[1]), "s"(prow[2]));
     else asm volatile("" ::"s"(prow[0]));
     // the lane's cos and sin chunks: gather, split, stitch
     CsChunk<T, CB> cw, sw;
@@ -1053,7 +1053,8 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
       }
     } else {
       int64_t pos = prow[0];
-      if constexpr (MR)
+      if constexpr (NR == 3) pos = sec == 0 ? prow[0] : sec == 1 ? prow[1] : prow[2];
+      if constexpr (NR == 4)
         pos = sec == 0 ? prow[0] : sec == 1 ? prow[1] : sec == 2 ? prow[2] : prow[3];
       const T *row = static_cast<const T *>(p.cache) + clamp_position(p, pos) * p.cache_stride;
       load_words<CB, false>(row + i0, cw.w);
@@ -1232,11 +1233,13 @@ template <typename T, bool NX, bool XC, bool LI>
 const void *pick_wave(const CachePlan &p) {
   constexpr int KP = NX && !XC && !LI ? int(kWaveRowsPairUnits) : int(kWaveRowsVectorUnits);
   constexpr int KM = int(kWaveRowsVectorUnits);  // multi-row stitching
-#define ROPE_KW(MU, MR, KK) \
-  reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, MU, XC, LI, MR, KK>)
-  if (p.multi_row) return p.wave_rows == uint32_t(KM) ? ROPE_KW(true, true, KM) : nullptr;
+#define ROPE_KW(MU, NR, KK) \
+  reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, MU, XC, LI, NR, KK>)
+  if (p.multi_row)
+    return p.wave_rows == uint32_t(KM) && p.nsec == 3 ? ROPE_KW(true, 3, KM) : nullptr;
   if (p.wave_rows != uint32_t(KP)) return nullptr;
-  return p.mrope ? ROPE_KW(false, true, KP) : ROPE_KW(false, false, KP);
+  if (!p.mrope) return ROPE_KW(false, 1, KP);
+  return p.nsec == 3 ? ROPE_KW(false, 3, KP) : p.nsec == 4 ? ROPE_KW(false, 4, KP) : nullptr;
 #undef ROPE_KW
 }
 
