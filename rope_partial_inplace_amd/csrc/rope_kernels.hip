@@ -915,6 +915,26 @@ __global__ __launch_bounds__(kCacheBlock) void cos_sin_cache_kernel(CachePlan p)
 // ============================================================================================
 typedef const __attribute__((address_space(4))) int64_t const_i64;
 
+// Output rows of the wavefront kernel as buffer ranges.  Its q/k stores go out as buffer stores
+// with the device-scope and streaming cache bits (sc1 | nt): on MI355X those copy 0.4-2.5%
+// faster than the plain non-temporal global stores of the same bytes, where nt alone is no
+// faster and sc1 alone slower.  A range is one token's q (or k) output row, below 2^31 bytes
+// on this path, so every offset is a 32-bit byte offset inside it.
+constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, no swizzle, no index stride
+constexpr int kStoreSc1Nt = 16 | 2;     // cache-policy bits of the store: sc1 | nt
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_range(void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, int(bytes), kRsrcWord3);
+}
+
+template <typename T, int V>
+__device__ __forceinline__ void row_store(__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rk,
+                                          bool is_q, int64_t elem, const RawN<T, V, true> &r) {
+  const int off = int(elem * int64_t(sizeof(T)));
+  if (is_q) __builtin_amdgcn_raw_buffer_store_b128(r.v[0], rq, off, 0, kStoreSc1Nt);
+  else __builtin_amdgcn_raw_buffer_store_b128(r.v[0], rk, off, 0, kStoreSc1Nt);
+}
+
 // The lane's cos (or sin) chunk as raw elements of T.
 template <typename T, int CB>
 union CsChunk {
@@ -1012,6 +1032,11 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
     const uint32_t t32 = fdiv(p.div_wpt, gw);
     const int64_t t = t32;
     const int64_t hbase = int64_t(gw - t32 * p.wave_wpt) * p.wave_heads + hs;
+    const int64_t qrow = p.nq * p.H, krow = p.nk * p.H;  // elements of a token's output rows
+    const __amdgpu_buffer_rsrc_t rq =
+        row_range(static_cast<T *>(p.q_out) + t * qrow, qrow * int64_t(sizeof(T)));
+    const __amdgpu_buffer_rsrc_t rk =
+        row_range(static_cast<T *>(p.k_out) + t * krow, krow * int64_t(sizeof(T)));
     // the token's position rows (wave-uniform scalar loads; they go out with the q/k loads
     // below and are waited for only after those, see the asm statement)
     int64_t prow[NR];
@@ -1086,12 +1111,11 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
       const int64_t h = hbase + int64_t(k) * p.wave_hpw;
       if (!lane_on || h >= nh) continue;
       const bool is_q = h < p.nq;
-      const int64_t out_row = t * ((is_q ? p.nq : p.nk) * p.H) + (is_q ? h : h - p.nq) * p.H;
-      void *out = is_q ? p.q_out : p.k_out;
+      const int64_t out_row = (is_q ? h : h - p.nq) * p.H;  // inside the token's output row
       if constexpr (EXCH) {
-        if constexpr (XCH) store_raw<T, V, true, true>(out, out_row + off_b, v[k][NV - 1]);
+        if constexpr (XCH) row_store<T, V>(rq, rk, is_q, out_row + off_b, v[k][NV - 1]);
         if (!rot) {
-          store_raw<T, V, true, true>(out, out_row + off_a, v[k][0]);
+          row_store<T, V>(rq, rk, is_q, out_row + off_a, v[k][0]);
           continue;
         }
         // [RSCC §rotate_half（GPT-NeoX style）旋转模式]: the x1 lane (u < R) writes
@@ -1114,12 +1138,12 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
           }
           float_to_raw_word<T, V, true>(y, q, oa);
         }
-        store_raw<T, V, true, true>(out, out_row + off_a, oa);
+        row_store<T, V>(rq, rk, is_q, out_row + off_a, oa);
         continue;
       }
       if (!rot) {
-        store_raw<T, V, true, true>(out, out_row + off_a, v[k][0]);
-        if constexpr (NV == 2) store_raw<T, V, true, true>(out, out_row + off_b, v[k][NV - 1]);
+        row_store<T, V>(rq, rk, is_q, out_row + off_a, v[k][0]);
+        if constexpr (NV == 2) row_store<T, V>(rq, rk, is_q, out_row + off_b, v[k][NV - 1]);
         continue;
       }
       if constexpr (NEOX) {
@@ -1140,8 +1164,8 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
           float_to_raw_word<T, V, true>(ya, q, oa);
           float_to_raw_word<T, V, true>(yb, q, ob);
         }
-        store_raw<T, V, true, true>(out, out_row + off_a, oa);
-        store_raw<T, V, true, true>(out, out_row + off_b, ob);
+        row_store<T, V>(rq, rk, is_q, out_row + off_a, oa);
+        row_store<T, V>(rq, rk, is_q, out_row + off_b, ob);
       } else {
         // [RSCC §rotate_interleaved（GPT-J style）旋转模式]: pairs (x[2m], x[2m+1]) inside the
         // vector, with cos/sin entry m of the lane's chunk
@@ -1154,7 +1178,10 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
           ya[2 * m] = a[2 * m] * cv[m] - a[2 * m + 1] * sv[m];
           ya[2 * m + 1] = a[2 * m + 1] * cv[m] + a[2 * m] * sv[m];
         }
-        store_n<T, V, true, true>(out, out_row + off_a, ya);
+        RawN<T, V, true> oy;
+#pragma unroll
+        for (int q = 0; q < V / PW; ++q) float_to_raw_word<T, V, true>(ya + q * PW, q, oy);
+        row_store<T, V>(rq, rk, is_q, out_row + off_a, oy);
       }
     }
   }

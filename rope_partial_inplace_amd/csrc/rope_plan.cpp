@@ -518,7 +518,10 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
   const bool xch = p.neox && !pair_lines && 2 * rd <= head_size && (head_size / 2 * es) % line == 0;
   const bool lin = p.neox && !pair_lines && !xch && 2 * p.units <= 64;
   const uint32_t lanes = lin ? 2 * p.units : p.units;  // lanes per head
-  if (p.vector_io && p.cache_vec && lanes >= 1 && lanes <= 64 &&
+  // Its stores address one token's q or k output row as a buffer range of 32-bit offsets.
+  const int64_t row_limit = int64_t(1) << 31;
+  const bool rows_fit = p.nq * head_size * es < row_limit && p.nk * head_size * es < row_limit;
+  if (p.vector_io && p.cache_vec && lanes >= 1 && lanes <= 64 && rows_fit &&
       (reinterpret_cast<uintptr_t>(p.positions) & 7u) == 0) {
     const uint32_t rows =
         p.neox && !xch && !lin && !p.multi_row ? kWaveRowsPairUnits : kWaveRowsVectorUnits;

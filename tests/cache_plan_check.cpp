@@ -181,7 +181,12 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
                 "load outside the input rows");
         if (!on || h >= nh) continue;
         const bool is_q = h < nq;
-        const int64_t out_row = t * ((is_q ? nq : nk) * H) + (is_q ? h : h - nq) * H;
+        // stores address the token's q (or k) output row as one buffer range, in bytes
+        const int64_t row_len = (is_q ? nq : nk) * H, es = 16 / V;
+        CHECK(row_len * es < (int64_t(1) << 31), "output row of %lld bytes on the wave path",
+              (long long)(row_len * es));
+        const int64_t in_row = (is_q ? h : h - nq) * H;
+        const int64_t out_row = t * row_len + in_row;
         std::vector<uint8_t> &hit = is_q ? hq : hk;
         for (size_t a = 0; a < offs.size(); ++a)
           for (int64_t e = 0; e < V; ++e) {
@@ -190,6 +195,8 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
             const bool rotated = exch ? (rot && a == 0) : rot;
             CHECK(rotated == (col < rd), "column %lld on the wrong side of rotaryDim",
                   (long long)col);
+            CHECK(in_row + col >= 0 && in_row + col < row_len,
+                  "store outside the token's output row");
             const size_t oi = size_t(out_row + col);
             CHECK(hit[oi] == 0, "wave output %zu written twice", oi);
             hit[oi] = 1;
@@ -360,7 +367,9 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
   // the wavefront path: taken exactly when its conditions hold (16-byte access everywhere,
   // at most 64 units per head, aligned positions); then walked as the kernel walks it
   const uint32_t lanes = p.wave_lin ? 2 * p.units : p.units;
-  const bool wave_ok = p.vector_io && p.cache_vec && lanes <= 64 && pos_offset % 8 == 0;
+  const int64_t row_limit = int64_t(1) << 31;
+  const bool wave_ok = p.vector_io && p.cache_vec && lanes <= 64 && pos_offset % 8 == 0 &&
+                       nq * H * es < row_limit && nk * H * es < row_limit;
   CHECK(p.wave == wave_ok, "wave path %d, conditions say %d", int(p.wave), int(wave_ok));
   // the NeoX layout is a speed choice; each is walked below, and the exchange layout needs
   // rd <= H/2 (all rotated vectors in the first access)
@@ -376,6 +385,31 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
     return walk_waves(p, neox, T, nq, nk, H, rd, sec, cache_mode, qs);
   }
   return true;
+}
+
+// Plan only (no walk): whether a one-token rope-mode plan with nq + nk heads of H elements
+// takes the wavefront path.  Tensors sit 2^40 bytes apart, so that rows of several GiB overlap
+// nothing.
+static int wave_taken(rope_dtype dt, int64_t nq, int64_t nk, int64_t H) {
+  rope_tensor pos{};
+  pos.data = reinterpret_cast<void *>(uintptr_t(6) << 40);
+  pos.dtype = ROPE_I64;
+  pos.ndim = 1;
+  pos.shape[0] = 1;
+  pos.stride[0] = 1;
+  const rope_tensor q = t2(uintptr_t(1) << 40, dt, 1, nq * H, nq * H);
+  const rope_tensor k = t2(uintptr_t(2) << 40, dt, 1, nk * H, nk * H);
+  const rope_tensor c = t2(uintptr_t(5) << 40, dt, 1024, H, H);
+  const rope_tensor qo = t2(uintptr_t(3) << 40, dt, 1, nq * H, nq * H);
+  const rope_tensor ko = t2(uintptr_t(4) << 40, dt, 1, nk * H, nk * H);
+  CachePlan p;
+  std::string err;
+  const int st = plan_cache(&pos, &q, &k, &c, nullptr, 0, H, 1, 0, &qo, &ko, &p, &err);
+  if (st != ROPE_OK) {
+    std::printf("FAIL: plan rejected: %s\n", err.c_str());
+    return -1;
+  }
+  return p.wave ? 1 : 0;
 }
 
 int main(int argc, char **argv) {
@@ -438,6 +472,19 @@ int main(int argc, char **argv) {
           ++plans;
         }
     }
+  // the wavefront kernel stores through one buffer range per token's q (or k) output row, of
+  // 32-bit offsets: a row of 2^31 bytes or more goes to the tile form (bf16 heads of 256 B)
+  for (int64_t nk : {int64_t(1), (int64_t(1) << 23) - 1, int64_t(1) << 23}) {
+    const int64_t nq = nk == 1 ? (int64_t(1) << 23) : 1;
+    const int want = (nq < (int64_t(1) << 23) && nk < (int64_t(1) << 23)) ? 1 : 0;
+    const int got = wave_taken(ROPE_BF16, nq, nk, 128);
+    if (got != want) {
+      std::printf("FAIL: nq %lld nk %lld heads of 256 B: wavefront path %d, want %d\n",
+                  (long long)nq, (long long)nk, got, want);
+      return 1;
+    }
+    ++plans;
+  }
   if (wave_plans == 0 || wave_plans == g_walked || xch_plans == 0 || lin_plans == 0 ||
       pair_plans == 0 || wide_pair_plans == 0) {
     std::printf("FAIL: %d of %d plans take the wavefront path (%d exchange, %d one-vector "
