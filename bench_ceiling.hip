@@ -1,15 +1,17 @@
 // bench_ceiling.hip -- measurement kernels for bench.py (not part of the RoPE library).
 //
-// Two reference streams that do no arithmetic, built in the way the RoPE kernels stream
-// (16-byte lanes, one item per lane, non-temporal loads and stores), to put a measured
-// ceiling beside each kernel's time:
+// Reference streams that do no arithmetic, built in the way the RoPE kernels stream (16-byte
+// lanes, one item per lane, non-temporal loads; stores as the kernel they stand beside issues
+// them), to put a measured ceiling beside each kernel's time:
 //   ceiling_copy   a dense copy of `bytes` bytes: the attainable rate of a mixed read/write
 //                  stream, and a copy of known size for scaling the HBM byte counters.  It
-//                  runs one 16-byte vector per lane in one-wavefront workgroups and one pass:
-//                  of the forms measured on MI355X (64- to 1024-lane workgroups, 1 to 8
-//                  vectors per lane, grid-stride loops of 2 to 8 passes, persistent grids,
-//                  per-XCD contiguous ranges, cached or streamed accesses), this one copies
-//                  85 MB to 1 GiB 3-5% faster than any other;
+//                  runs one 16-byte vector per lane in one-wavefront workgroups and one pass,
+//                  storing with the sc1 and nt cache bits: of the forms measured on MI355X (64-
+//                  to 1024-lane workgroups, 1 to 8 vectors per lane, grid-stride loops of 2 to
+//                  8 passes, persistent grids, per-XCD contiguous ranges, cached or streamed
+//                  accesses, every combination of the sc0, sc1 and nt bits on loads and
+//                  stores, loads and stores held to alternating time slots), this one copies
+//                  85 MB to 1 GiB fastest (nt-only stores: 1-2% slower);
 //   ceiling_rows   an in-place pass over a strided slice of each row (read `len` bytes at
 //                  `off` of each `row_bytes`-byte row in lanes of `lane_bytes` (8 or 16), a lane
 //                  taking its chunk in `rows_per_lane` consecutive rows (1, 2 or 4), write them
@@ -17,12 +19,13 @@
 //                  arrays, row r using side row r / rows_per_side, split evenly over the row's
 //                  lanes in 16-byte loads, loaded once per lane): the access pattern of the
 //                  in-place RoPE kernel on a [rows, D] slice with its cos/sin rows, with the
-//                  rotation taken out.
+//                  rotation taken out (non-temporal stores, as that kernel's).
 //   ceiling_pairs  a copy of `heads` rows of `head_bytes` in the cache kernel's NeoX pair-unit
 //                  layout: a lane takes 16 bytes at u*16 of a head and 16 bytes half a head
 //                  further (head_bytes / 32 lanes per head, all of a wavefront's lanes on
 //                  whole heads), in `rows_per_lane` rows of heads (1 or 2), 256-lane
-//                  workgroups; with the rotation and the cos|sin gather taken out.
+//                  workgroups, stores with the sc1 and nt bits as the cache kernel's; with the
+//                  rotation and the cos|sin gather taken out.
 // Each returns 0, or -1 for arguments outside their documented form and -2 if the launch
 // fails.  Everything is enqueued on `stream` (a hipStream_t, NULL = the null stream).
 #include <hip/hip_runtime.h>
@@ -43,11 +46,27 @@ constexpr int64_t kMaxGrid = int64_t(1) << 20;
 constexpr int kCopyBlock = 64;
 constexpr int64_t kCopyMaxGrid = int64_t(1) << 25;
 
+// Stores as the cache kernel issues them: buffer stores with the device-scope and streaming
+// cache bits (sc1 | nt), into a buffer range that starts at a wave-uniform base.
+constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, no swizzle, no index stride
+constexpr int kStoreSc1Nt = 16 | 2;
+
+__device__ __forceinline__ void store_sc1nt(void *base, int64_t range_bytes, int off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      v, __builtin_amdgcn_make_buffer_rsrc(base, 0, int(range_bytes), kRsrcWord3), off, 0,
+      kStoreSc1Nt);
+}
+
 __global__ __launch_bounds__(kCopyBlock) void copy_kernel(u32x4 *dst, const u32x4 *src,
                                                           int64_t n) {
-  for (int64_t i = int64_t(blockIdx.x) * kCopyBlock + threadIdx.x; i < n;
-       i += int64_t(gridDim.x) * kCopyBlock)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  // ib: the first vector of this workgroup's pass (uniform), so the store range is scalar
+  for (int64_t ib = int64_t(blockIdx.x) * kCopyBlock; ib < n;
+       ib += int64_t(gridDim.x) * kCopyBlock) {
+    const int64_t i = ib + threadIdx.x, left = n - ib;
+    if (i < n)
+      store_sc1nt(dst + ib, (left < kCopyBlock ? left : kCopyBlock) * 16, int(threadIdx.x) * 16,
+                  __builtin_nontemporal_load(src + i));
+  }
 }
 
 // One lane: W bytes (8 or 16) of the slice in each of R consecutive rows (rows that share one
@@ -100,8 +119,10 @@ __global__ __launch_bounds__(256) void pairs_kernel(u32x4 *dst, const u32x4 *src
                                                    int64_t units, int64_t hpw, int64_t waves) {
   const int64_t lane = threadIdx.x & 63, hsub = lane / units, u = lane - hsub * units;
   const int64_t vpr = 2 * units;  // 16-byte vectors per head
-  for (int64_t w = (int64_t(blockIdx.x) * 256 + threadIdx.x) / 64; w < waves;
-       w += int64_t(gridDim.x) * 4) {
+  const int64_t w0 = __builtin_amdgcn_readfirstlane(int(blockIdx.x * 4 + threadIdx.x / 64));
+  for (int64_t w = w0; w < waves; w += int64_t(gridDim.x) * 4) {
+    // the wavefront's heads [h0, h0 + nh) as one store range
+    const int64_t h0 = w * K * hpw, hl = heads - h0, nh = hl < K * hpw ? hl : K * hpw;
     u32x4 a[K], b[K];
     int64_t base[K];
 #pragma unroll
@@ -116,8 +137,9 @@ __global__ __launch_bounds__(256) void pairs_kernel(u32x4 *dst, const u32x4 *src
     for (int k = 0; k < K; ++k) {
       const int64_t h = (w * K + k) * hpw + hsub;
       if (hsub >= hpw || h >= heads) continue;
-      __builtin_nontemporal_store(a[k], dst + base[k]);
-      __builtin_nontemporal_store(b[k], dst + base[k] + units);
+      const int off = int((base[k] - h0 * vpr) * 16);
+      store_sc1nt(dst + h0 * vpr, nh * vpr * 16, off, a[k]);
+      store_sc1nt(dst + h0 * vpr, nh * vpr * 16, off + int(units) * 16, b[k]);
     }
   }
 }
