@@ -575,6 +575,41 @@ def test_cache_units_per_head_either_side_of_64(H, neox):
     compare_cache_case(case, qo, ko, f"H{H} rd{rd} neox={neox}")
 
 
+@pytest.mark.parametrize(
+    "dt,H,rd,neox,sec,cache_mode",
+    [(torch.float16, 128, 64, False, None, None),       # GPT-J one-vector units
+     (torch.bfloat16, 128, 128, True, None, None),      # NeoX pair units
+     (torch.bfloat16, 128, 64, True, None, None),       # NeoX exchange layout (rd <= H/2)
+     (torch.bfloat16, 128, 96, True, None, None),       # NeoX one-vector units
+     (torch.float32, 64, 64, True, None, None),
+     (torch.bfloat16, 128, 128, True, [16, 24, 24], 0),
+     (torch.bfloat16, 128, 128, True, [16, 16, 16, 16], 0),
+     (torch.bfloat16, 128, 128, True, [24, 20, 20], 1),  # interleaved stitching
+     (torch.bfloat16, 1056, 1024, True, None, None)],   # 66 units a head: the tile form
+    ids=["gptj_f16", "neox_pairs", "neox_exchange", "neox_one_vector", "neox_f32", "mrope3",
+         "mrope4", "mrope_interleaved", "tile_form"])
+def test_cache_every_output_element_written(dt, H, rd, neox, sec, cache_mode):
+    """The outputs start as all-ones bit patterns (a NaN in every dtype, which finite inputs
+    never produce), so a store that never lands cannot pass as a correct value left over in
+    reused memory: every element must be overwritten, and all of them must match the oracle.
+    [RSCC §设计动机]: every element of query_out/key_out is either rotated or passed through."""
+    T, nq, nk = 333, 5, 3
+    pos = None
+    if sec is not None:
+        pos = W.mrope_positions(T - 2 * 8 * 8, 2, 8, 8, len(sec))
+    case = W.cache_case("written", T, nq, nk, H, rd, dt, neox, 700, seed=4242 + H + rd,
+                        mrope_section=sec, positions=pos, device=DEV, cache_mode=cache_mode)
+    qo, ko = torch.empty_like(case.query), torch.empty_like(case.key)
+    ibits = torch.int32 if dt == torch.float32 else torch.int16
+    for t in (qo, ko):
+        t.view(ibits).fill_(-1)
+    run_cache_case(case, query_out=qo, key_out=ko)
+    for name, t in (("q", qo), ("k", ko)):
+        left = int((t.view(ibits) == -1).sum())
+        assert left == 0, f"{left} {name} output elements never written"
+    compare_cache_case(case, qo, ko, f"every element H{H} rd{rd} neox={neox} sec={sec}")
+
+
 @pytest.mark.parametrize("neox", [True, False], ids=["neox", "gptj"])
 @pytest.mark.parametrize("sec,cache_mode", [(None, None), ([16, 24, 24], 0), ([24, 20, 20], 1),
                                             ([11, 11, 10], 0)],
