@@ -953,8 +953,9 @@ union CsChunk {
 // is read from its lane with ds_bpermute, as in XCH.
 // NR: position rows read per token: 1 in rope mode (no section table), else the mrope
 // section count (3 or 4; multi-row stitching has 3).
-template <typename T, bool NEOX, bool MULTI, bool XCH, bool LIN, int NR, int K>
-__global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePlan p) {
+// WB: lanes per workgroup (the plan's wave_block).
+template <typename T, bool NEOX, bool MULTI, bool XCH, bool LIN, int NR, int K, int WB>
+__global__ __launch_bounds__(WB) void cos_sin_cache_wave_kernel(CachePlan p) {
   static_assert(!(XCH || LIN) || NEOX, "the lane exchange is a NeoX layout");
   static_assert(!(XCH && LIN), "one layout at a time");
   static_assert(NR == 1 || NR == 3 || NR == 4, "rope mode or an mrope section count");
@@ -1026,7 +1027,7 @@ __global__ __launch_bounds__(kWaveBlock) void cos_sin_cache_wave_kernel(CachePla
   int64_t roff[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) roff[r] = int64_t(r) * p.pos_stride_row;
-  constexpr uint32_t kWpb = kWaveBlock / 64;
+  constexpr uint32_t kWpb = WB / 64;
   for (uint32_t gw = __builtin_amdgcn_readfirstlane(blockIdx.x * kWpb + threadIdx.x / 64);
        gw < uint32_t(p.waves); gw += gridDim.x * kWpb) {
     const uint32_t t32 = fdiv(p.div_wpt, gw);
@@ -1260,8 +1261,10 @@ template <typename T, bool NX, bool XC, bool LI>
 const void *pick_wave(const CachePlan &p) {
   constexpr int KP = NX && !XC && !LI ? int(kWaveRowsPairUnits) : int(kWaveRowsVectorUnits);
   constexpr int KM = int(kWaveRowsVectorUnits);  // multi-row stitching
+  constexpr int WB = NX ? kWaveBlockNeox : kWaveBlockGptj;
+  if (p.wave_block != uint32_t(WB)) return nullptr;
 #define ROPE_KW(MU, NR, KK) \
-  reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, MU, XC, LI, NR, KK>)
+  reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, MU, XC, LI, NR, KK, WB>)
   if (p.multi_row)
     return p.wave_rows == uint32_t(KM) && p.nsec == 3 ? ROPE_KW(true, 3, KM) : nullptr;
   if (p.wave_rows != uint32_t(KP)) return nullptr;
@@ -1358,9 +1361,10 @@ ROPE_API int rope_with_cos_sin_cache_v2(const rope_tensor *positions, const rope
     g_last_error = "internal: no kernel for this plan";
     return ROPE_ERR_RUNTIME;
   }
-  if (plan.wave)
-    return launch(fn, (plan.waves + kWaveBlock / 64 - 1) / (kWaveBlock / 64), kWaveBlock, 0,
-                  stream, &plan);
+  if (plan.wave) {
+    const int64_t wpb = plan.wave_block / 64;  // wavefronts per workgroup
+    return launch(fn, (plan.waves + wpb - 1) / wpb, int(plan.wave_block), 0, stream, &plan);
+  }
   const size_t esize = plan.dt == ROPE_F32 ? 4 : 2;
   const size_t lds = plan.cs_direct ? 0 : size_t(plan.tile_tokens) * size_t(plan.rd) * esize;
   return launch(fn, plan.tiles, kCacheBlock, lds, stream, &plan);

@@ -531,6 +531,7 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
     if (wpt <= int64_t(0x7fffffff) && T <= kMaxWaves / wpt) {
       p.wave = true;
       p.wave_rows = rows;
+      p.wave_block = uint32_t(p.neox ? kWaveBlockNeox : kWaveBlockGptj);
       p.wave_hpw = hpw;
       p.wave_heads = heads;
       p.wave_wpt = uint32_t(wpt);

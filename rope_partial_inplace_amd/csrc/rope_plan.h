@@ -139,6 +139,7 @@ struct CachePlan {
   // kWaveRowsVectorUnits; the kernel has it as a template argument (last in the struct, so
   // the fields the kernels read keep their offsets)
   uint32_t wave_rows = 0;
+  uint32_t wave_block = 0;      // lanes per workgroup: kWaveBlockNeox or kWaveBlockGptj
 };
 
 int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor *sin,
@@ -176,14 +177,17 @@ constexpr int kCacheBlock = 256;  // cache kernel workgroup (one token tile)
 constexpr int64_t kTaperTokens = 1280;
 constexpr int kNeoxItemsPerLane = 2;  // NeoX units are two vectors
 constexpr int kGptjItemsPerLane = 2;  // GPT-J units are one vector
-// Wavefront cache kernel: 256-lane workgroups of four independent wavefronts; 64-lane
-// workgroups were within 1%, 512- and 1024-lane ones up to 8% slower.  A lane carries two
-// 16-byte q/k vectors per wavefront: NeoX pair units (two vectors each) one head row, the
+// Wavefront cache kernel: workgroups of independent wavefronts, 64 lanes for GPT-J and 256
+// for the NeoX layouts.  GPT-J with 64-lane workgroups: 1-2.5% faster on five of seven shapes
+// (the 1 GiB f16 one 1.1%), 0.5-0.8% slower on two; the NeoX layouts were up to 1% slower with
+// them, and 128-, 512- and 1024-lane workgroups were slower still (up to 8%).  A lane carries
+// two 16-byte q/k vectors per wavefront: NeoX pair units (two vectors each) one head row, the
 // one-vector units of the other layouts two head rows.  Measured on the rope NeoX bf16, GPT-J
 // f16 and mrope bf16 workloads: one-vector units with one row were 3-30% slower and with three
 // rows 2-6% slower; pair units with one row 3% faster than with two, except under multi-row
 // stitching (three cos|sin gathers per lane), where one row was 2-3% slower.
-constexpr int kWaveBlock = 256;
+constexpr int kWaveBlockNeox = 256;
+constexpr int kWaveBlockGptj = 64;
 constexpr uint32_t kWaveRowsPairUnits = 1;
 constexpr uint32_t kWaveRowsVectorUnits = 2;
 // Waves of one launch stay below 2^31, so a wave index plus the grid stride fits 32 bits.

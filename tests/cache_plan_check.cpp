@@ -105,6 +105,8 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
   CHECK(p.wave_rows == (pair_units ? kWaveRowsPairUnits : kWaveRowsVectorUnits),
         "wave rows %u", p.wave_rows);
   CHECK(p.wave_heads == p.wave_rows * p.wave_hpw, "wave heads %u", p.wave_heads);
+  CHECK(p.wave_block == uint32_t(neox ? kWaveBlockNeox : kWaveBlockGptj) && p.wave_block % 64 == 0,
+        "wave workgroup of %u lanes", p.wave_block);
   CHECK(int64_t(p.wave_wpt) * p.wave_heads >= nh &&
             int64_t(p.wave_wpt - 1) * p.wave_heads < nh, "waves per token %u", p.wave_wpt);
   CHECK(p.waves == T * int64_t(p.wave_wpt) && p.waves < kMaxWaves, "waves %lld",
