@@ -964,8 +964,9 @@ __global__ __launch_bounds__(WB) void cos_sin_cache_wave_kernel(CachePlan p) {
   constexpr bool EXCH = XCH || LIN;
   // One-vector units (GPT-J, LIN): the wavefront issues its loads at raised priority and drops
   // back once they are all out (below), so that wavefronts starting up get their loads in ahead
-  // of the rotation and stores of older ones: GPT-J workloads 0.4-1% faster, LIN 6%; the pair
-  // units (3%) and the exchange layout (4-5%) were slower with it.
+  // of the rotation and stores of older ones.  GPT-J in one-wavefront workgroups: the 1 GiB f16
+  // workload 1.8% faster, 64 and 512 tokens 5-7%, other shapes within 2% either way; LIN 6%
+  // faster.  The pair units (3%) and the exchange layout (4-5%) were slower with it.
   constexpr bool PRIO = !NEOX || LIN;
   if constexpr (PRIO) __builtin_amdgcn_s_setprio(3);  // rotated vectors pair across lanes
   constexpr int V = Io<T>::kPer16;
