@@ -739,6 +739,35 @@ def test_cache_query_beyond_2e31_elements():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("heads", [(1 << 23) - 1, 1 << 23], ids=["row_below_2e31_bytes",
+                                                              "row_of_2e31_bytes"])
+def test_cache_output_row_at_the_buffer_range_limit(heads):
+    """One token with a query row of 2^31 - 256 bytes (bf16 heads of 128: the wavefront kernel,
+    whose stores address a token's output row as one buffer range of 32-bit offsets, up to the
+    last head) and of exactly 2^31 bytes (the plan sends it to the tile form).  The output starts
+    as all-ones bit patterns and must be overwritten everywhere; the first and the last 64 heads
+    are compared with the oracle (heads are independent, so a slice of them is a valid call)."""
+    T, H, nk = 1, 128, 3
+    g = W.generator(2023, DEV)
+    q = W.randn((T, heads * H), torch.bfloat16, g)
+    k = W.randn((T, nk * H), torch.bfloat16, g)
+    cache = W.cos_sin_cache(512, H, torch.bfloat16).to(DEV)
+    pos = torch.tensor([333], dtype=torch.int64, device=DEV)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    for t in (qo, ko):
+        t.view(torch.int16).fill_(-1)
+    ra.rope_with_cos_sin_cache(pos, q, k, cache, None, H, True, query_out=qo, key_out=ko)
+    torch.cuda.synchronize()
+    for name, t in (("q", qo), ("k", ko)):
+        left = int((t.view(torch.int16) == -1).sum())
+        assert left == 0, f"{left} {name} output elements never written"
+    for part in (slice(0, 64 * H), slice((heads - 64) * H, heads * H)):
+        compare_cache(pos.cpu(), q[:, part].cpu(), k.cpu(), cache.cpu(), None, H, True,
+                      qo[:, part].cpu(), ko.cpu(), f"{heads} heads, {part}")
+    del q, qo
+    torch.cuda.empty_cache()
+
+
 def test_cache_deterministic():
     case = W.cache_mrope(DEV)
     a = run_cache_case(case)
