@@ -38,7 +38,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBlock = 512;
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
 
 // The dense copy: one wavefront per workgroup, one vector per lane; the grid covers the copy in
@@ -72,41 +71,60 @@ __global__ __launch_bounds__(kCopyBlock) void copy_kernel(u32x4 *dst, const u32x
 // One lane: W bytes (8 or 16) of the slice in each of R consecutive rows (rows that share one
 // side row), and its share of that side row (16-byte loads from each side array, loaded once for
 // the R rows).  `flip` is zero at run time; folding it into the data keeps every word of the
-// stores live.
-template <int W, int R>
-__global__ __launch_bounds__(kBlock) void rows_kernel(char *x, int64_t groups, int64_t row_bytes,
-                                                      int64_t off, int64_t lanes_per_row,
-                                                      const char *side_a, const char *side_b,
-                                                      int64_t side_bytes, int64_t rows_per_side,
-                                                      uint32_t flip, bool side_stream) {
+// stores live.  SIDE: 0 no side arrays, 1 cached side loads, 2 non-temporal ones.  The cache
+// policy of every access is fixed per instantiation (the stores are buffer stores with the nt
+// bit as an operand: with plain non-temporal stores the compiler merged the store paths and
+// dropped the bit).  Item decode as cheap as the RoPE kernel's: shifts when the lanes of a row
+// and the row groups of a side row are powers of two (every pattern the benchmark times), 32-bit
+// division otherwise; lshift/sshift < 0 selects the division.
+template <int W, int R, int SIDE>
+__global__ __launch_bounds__(1024) void rows_kernel(char *x, uint32_t x_bytes, uint32_t lanes,
+                                                    int64_t row_bytes, int64_t off,
+                                                    uint32_t lanes_per_row, int lshift,
+                                                    const char *side_a, const char *side_b,
+                                                    int64_t side_bytes, uint32_t per_lane,
+                                                    uint32_t groups_per_side, int sshift,
+                                                    uint32_t flip) {
   using V = typename std::conditional<W == 16, u32x4, u32x2>::type;
-  const int64_t per_lane = side_bytes / lanes_per_row;  // a multiple of 16 (host-checked)
-  for (int64_t it = int64_t(blockIdx.x) * kBlock + threadIdx.x; it < groups * lanes_per_row;
-       it += int64_t(gridDim.x) * kBlock) {
-    const int64_t g = it / lanes_per_row, c = it - g * lanes_per_row;
-    V *p = reinterpret_cast<V *>(x + g * R * row_bytes + off + c * W);
+  // per_lane: the side bytes each lane loads from each side row, a multiple of 16 (host)
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(x, 0, int(x_bytes), kRsrcWord3);
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t it = blockIdx.x * blockDim.x + threadIdx.x; it < lanes; it += stride) {
+    const uint32_t g = lshift >= 0 ? it >> lshift : it / lanes_per_row;
+    const uint32_t c = it - g * lanes_per_row;
+    const int64_t o = int64_t(g) * R * row_bytes + off + int64_t(c) * W;  // below x_bytes
     V v[R];
 #pragma unroll
-    for (int j = 0; j < R; ++j) v[j] = __builtin_nontemporal_load(p + j * (row_bytes / W));
+    for (int j = 0; j < R; ++j)
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const V *>(x + o + j * row_bytes));
     uint32_t acc = 0;
-    const int64_t so = (g * R / rows_per_side) * side_bytes + c * per_lane;
-    for (int64_t k = 0; k < per_lane; k += 16) {
-      const u32x4 *qa = reinterpret_cast<const u32x4 *>(side_a + so + k);
-      const u32x4 *qb = reinterpret_cast<const u32x4 *>(side_b + so + k);
-      const u32x4 a = side_stream ? __builtin_nontemporal_load(qa) : *qa;
-      const u32x4 b = side_stream ? __builtin_nontemporal_load(qb) : *qb;
-      acc |= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
+    if constexpr (SIDE != 0) {
+      const uint32_t sr = sshift >= 0 ? g >> sshift : g / groups_per_side;  // the side row
+      const int64_t so = int64_t(sr) * side_bytes + int64_t(c) * per_lane;
+      uint32_t k = 0;
+      do {
+        const u32x4 *qa = reinterpret_cast<const u32x4 *>(side_a + so + k);
+        const u32x4 *qb = reinterpret_cast<const u32x4 *>(side_b + so + k);
+        const u32x4 a = SIDE == 2 ? __builtin_nontemporal_load(qa) : *qa;
+        const u32x4 b = SIDE == 2 ? __builtin_nontemporal_load(qb) : *qb;
+        acc |= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
+        k += 16;
+      } while (k < per_lane);
     }
     const uint32_t m = flip & acc;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       v[j].x ^= m;
       v[j].y ^= m;
+      const int os = int(o + j * row_bytes);
       if constexpr (W == 16) {
         v[j].z ^= m;
         v[j].w ^= m;
+        __builtin_amdgcn_raw_buffer_store_b128(v[j], rx, os, 0, 2);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b64(v[j], rx, os, 0, 2);
       }
-      __builtin_nontemporal_store(v[j], p + j * (row_bytes / W));
     }
   }
 }
@@ -144,10 +162,6 @@ __global__ __launch_bounds__(256) void pairs_kernel(u32x4 *dst, const u32x4 *src
   }
 }
 
-int64_t grid_for(int64_t lanes) {
-  const int64_t g = (lanes + kBlock - 1) / kBlock;
-  return g < 1 ? 1 : (g > kMaxGrid ? kMaxGrid : g);
-}
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -179,23 +193,48 @@ extern "C" __attribute__((visibility("default"))) int ceiling_rows(
   if (side_bytes % (16 * lanes_per_row) != 0) return -1;
   if (side_bytes > 0 && (!side_a || !side_b || !aligned(side_a, 16) || !aligned(side_b, 16)))
     return -1;
-  const int64_t groups = rows / r, lanes = groups * lanes_per_row;
+  const int64_t groups = rows / r, lanes = groups * lanes_per_row, x_bytes = rows * row_bytes;
+  if (lanes >= (int64_t(1) << 31) || x_bytes >= (int64_t(1) << 31))
+    return -1;  // 32-bit item decode and store offsets
+  // the in-place RoPE kernel's launch shape: within one round of resident lanes (256 CUs x
+  // 2048) the largest workgroup from 1024 down to 64 lanes that still gives every CU one,
+  // 512-lane workgroups past it
+  int64_t bl = 1024;
+  while (bl > 64 && lanes < 256 * bl) bl /= 2;
+  if (lanes > int64_t(256) * 2048) bl = 512;
+  int64_t nb = (lanes + bl - 1) / bl;
+  nb = nb < 1 ? 1 : (nb > kMaxGrid ? kMaxGrid : nb);
+  const auto log2_exact = [](int64_t v) {
+    int k = 0;
+    while ((int64_t(1) << k) < v) ++k;
+    return (int64_t(1) << k) == v ? k : -1;
+  };
+  const int64_t gps = rows_per_side / r;  // row groups per side row
+  const int lsh = log2_exact(lanes_per_row), ssh = log2_exact(gps);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const char *a = static_cast<const char *>(side_a), *b = static_cast<const char *>(side_b);
-  const dim3 grid(uint32_t(grid_for(lanes))), block(kBlock);
+  const dim3 grid(static_cast<uint32_t>(nb)), block(static_cast<uint32_t>(bl));
   char *xc = static_cast<char *>(x);
-#define ROWS_LAUNCH(W, R)                                                                    \
-  hipLaunchKernelGGL((rows_kernel<W, R>), grid, block, 0, s, xc, groups, row_bytes, off,      \
-                     lanes_per_row, a, b, side_bytes, rows_per_side, 0u, side_stream != 0)
+#define ROWS_LAUNCH(W, R, SIDE)                                                              \
+  hipLaunchKernelGGL((rows_kernel<W, R, SIDE>), grid, block, 0, s, xc, uint32_t(x_bytes),     \
+                     uint32_t(lanes), row_bytes, off, uint32_t(lanes_per_row), lsh, a, b,      \
+                     side_bytes, uint32_t(side_bytes / lanes_per_row), uint32_t(gps), ssh, 0u)
+#define ROWS_SIDE(W, R)                                                                      \
+  do {                                                                                       \
+    if (side_bytes == 0) ROWS_LAUNCH(W, R, 0);                                               \
+    else if (side_stream) ROWS_LAUNCH(W, R, 2);                                              \
+    else ROWS_LAUNCH(W, R, 1);                                                               \
+  } while (0)
   if (w == 16) {
-    if (r == 1) ROWS_LAUNCH(16, 1);
-    else if (r == 2) ROWS_LAUNCH(16, 2);
-    else ROWS_LAUNCH(16, 4);
+    if (r == 1) ROWS_SIDE(16, 1);
+    else if (r == 2) ROWS_SIDE(16, 2);
+    else ROWS_SIDE(16, 4);
   } else {
-    if (r == 1) ROWS_LAUNCH(8, 1);
-    else if (r == 2) ROWS_LAUNCH(8, 2);
-    else ROWS_LAUNCH(8, 4);
+    if (r == 1) ROWS_SIDE(8, 1);
+    else if (r == 2) ROWS_SIDE(8, 2);
+    else ROWS_SIDE(8, 4);
   }
+#undef ROWS_SIDE
 #undef ROWS_LAUNCH
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }
