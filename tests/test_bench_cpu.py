@@ -129,7 +129,8 @@ def test_read_write_split_of_the_algorithmic_bytes():
 def test_ceiling_kernels_refuse_arguments_outside_their_form():
     """bench_ceiling's entry points check their arguments before any launch (so these calls
     run without a GPU): null or misaligned buffers, sizes that are not whole lanes, a slice past
-    the row, lane widths and rows per lane outside {8, 16} and {1, 2, 4}."""
+    the row, lane widths and rows per lane outside {8, 16} and {1, 2, 4}, an x of 2^31 bytes or
+    more (the row pattern's store offsets are 32-bit)."""
     lib = bench.load_ceiling()
     buf = torch.zeros((1 << 16) + 256, dtype=torch.uint8)
     p = (buf.data_ptr() + 255) // 256 * 256  # 256-byte aligned, with 64 KiB behind it
@@ -154,6 +155,8 @@ def test_ceiling_kernels_refuse_arguments_outside_their_form():
     assert rows(side=200) == -1                # side bytes not whole 16-byte loads per lane
     assert rows(rps=2) == -1                   # rows per lane sharing different side rows
     assert rows(sa=p + 8) == -1                # misaligned side array
+    assert rows(rows=1 << 23, row_bytes=256, off=0, len=128, rps=32) == -1  # x of 2^31 bytes:
+    # beyond the 32-bit store offsets (refused before any launch, so no memory is touched)
     assert lib.ceiling_pairs(p, p + 8192, 4, 256, 3, None) == -1       # rows per lane
     assert lib.ceiling_pairs(p, p + 8192, 4, 240, 2, None) == -1       # not whole 32-byte units
     assert lib.ceiling_pairs(p, p + 8192, 4, 4096, 2, None) == -1      # more than 64 lanes a head
