@@ -953,8 +953,9 @@ union CsChunk {
 // is read from its lane with ds_bpermute, as in XCH.
 // NR: position rows read per token: 1 in rope mode (no section table), else the mrope
 // section count (3 or 4; multi-row stitching has 3).
-// WB: lanes per workgroup (the plan's wave_block).
-template <typename T, bool NEOX, bool MULTI, bool XCH, bool LIN, int NR, int K, int WB>
+// WB: lanes per workgroup (the plan's wave_block).  SR: the token's cos|sin row is read with
+// scalar loads (the plan's wave_scalar_row: GPT-J rope mode, 128-byte rows).
+template <typename T, bool NEOX, bool MULTI, bool XCH, bool LIN, int NR, int K, int WB, bool SR>
 __global__ __launch_bounds__(WB) void cos_sin_cache_wave_kernel(CachePlan p) {
   static_assert(!(XCH || LIN) || NEOX, "the lane exchange is a NeoX layout");
   static_assert(!(XCH && LIN), "one layout at a time");
@@ -1084,8 +1085,41 @@ __global__ __launch_bounds__(WB) void cos_sin_cache_wave_kernel(CachePlan p) {
       if constexpr (NR == 4)
         pos = sec == 0 ? prow[0] : sec == 1 ? prow[1] : sec == 2 ? prow[2] : prow[3];
       const T *row = static_cast<const T *>(p.cache) + clamp_position(p, pos) * p.cache_stride;
-      load_words<CB, false>(row + i0, cw.w);
-      load_words<CB, false>(row + half + i0, sw.w);
+      if constexpr (SR) {
+        static_assert(!NEOX && NR == 1 && CB == 8, "GPT-J rope mode, 8-byte chunks");
+        // The whole 128-byte row in scalar registers (two 64-byte scalar loads: the row is
+        // wave-uniform): cos chunk c is words 2c, 2c + 1 and its sin chunk words 16 + 2c,
+        // 17 + 2c, c < 8; each lane selects its own chunk cu.  The empty asm keeps the words in
+        // SGPRs (otherwise the compiler turns the selection back into per-lane vector loads).
+        typedef const __attribute__((address_space(4))) uint32_t const_u32;
+        const_u32 *rw = reinterpret_cast<const_u32 *>(reinterpret_cast<uintptr_t>(row));
+        uint32_t w[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) w[i] = rw[i];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) asm volatile("" : "+s"(w[i]));
+        // word `first` of chunk cu: a three-level select on the bits of cu
+        const bool b0 = (cu & 1u) != 0, b1 = (cu & 2u) != 0, b2 = (cu & 4u) != 0;
+        const auto pick = [&](int first) {
+          const uint32_t l0 = b0 ? w[first + 2] : w[first];
+          const uint32_t l1 = b0 ? w[first + 6] : w[first + 4];
+          const uint32_t l2 = b0 ? w[first + 10] : w[first + 8];
+          const uint32_t l3 = b0 ? w[first + 14] : w[first + 12];
+          return b2 ? (b1 ? l3 : l2) : (b1 ? l1 : l0);
+        };
+        cw.w.w[0] = pick(0);
+        cw.w.w[1] = pick(1);
+        sw.w.w[0] = pick(16);
+        sw.w.w[1] = pick(17);
+        // Every row's q/k data is needed here, before any store, as the vector cos/sin loads
+        // make the other path wait: waiting only for the first row, the compiler had the
+        // second row wait for the first row's store as well (the counter is in order).
+#pragma unroll
+        for (int k = 0; k < K; ++k) asm volatile("" ::"v"(v[k][0].v[0].x));
+      } else {
+        load_words<CB, false>(row + i0, cw.w);
+        load_words<CB, false>(row + half + i0, sw.w);
+      }
     }
     // Every load of the item is out: keep the compiler from moving work that waits for the
     // q/k data above the cos/sin loads.  Left to itself it waited for the first q/k vector
@@ -1264,13 +1298,21 @@ const void *pick_wave(const CachePlan &p) {
   constexpr int KM = int(kWaveRowsVectorUnits);  // multi-row stitching
   constexpr int WB = NX ? kWaveBlockNeox : kWaveBlockGptj;
   if (p.wave_block != uint32_t(WB)) return nullptr;
-#define ROPE_KW(MU, NR, KK) \
-  reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, MU, XC, LI, NR, KK, WB>)
+  if (p.wave_scalar_row && (NX || p.mrope || p.rd * int64_t(sizeof(T)) != kScalarRowBytes))
+    return nullptr;
+#define ROPE_KW(MU, NR, KK, SR) \
+  reinterpret_cast<const void *>(&cos_sin_cache_wave_kernel<T, NX, MU, XC, LI, NR, KK, WB, SR>)
   if (p.multi_row)
-    return p.wave_rows == uint32_t(KM) && p.nsec == 3 ? ROPE_KW(true, 3, KM) : nullptr;
+    return p.wave_rows == uint32_t(KM) && p.nsec == 3 ? ROPE_KW(true, 3, KM, false) : nullptr;
   if (p.wave_rows != uint32_t(KP)) return nullptr;
-  if (!p.mrope) return ROPE_KW(false, 1, KP);
-  return p.nsec == 3 ? ROPE_KW(false, 3, KP) : p.nsec == 4 ? ROPE_KW(false, 4, KP) : nullptr;
+  if (!p.mrope) {
+    if constexpr (!NX)
+      if (p.wave_scalar_row) return ROPE_KW(false, 1, KP, true);
+    return ROPE_KW(false, 1, KP, false);
+  }
+  return p.nsec == 3   ? ROPE_KW(false, 3, KP, false)
+         : p.nsec == 4 ? ROPE_KW(false, 4, KP, false)
+                       : nullptr;
 #undef ROPE_KW
 }
 

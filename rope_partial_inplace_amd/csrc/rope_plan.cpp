@@ -536,6 +536,8 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
       p.wave_heads = heads;
       p.wave_wpt = uint32_t(wpt);
       p.waves = T * wpt;
+      p.wave_scalar_row = !p.neox && !p.mrope && rd * es == kScalarRowBytes &&
+                          p.waves >= kScalarRowMinWaves;
       p.div_wpt = make_fastdiv(p.wave_wpt);
       p.wave_lin = lin;
       p.wave_xch = xch;

@@ -140,6 +140,10 @@ struct CachePlan {
   // the fields the kernels read keep their offsets)
   uint32_t wave_rows = 0;
   uint32_t wave_block = 0;      // lanes per workgroup: kWaveBlockNeox or kWaveBlockGptj
+  // GPT-J rope mode with a 128-byte cos|sin row, in a launch of at least kScalarRowMinWaves
+  // wavefronts: each wavefront reads its token's whole row with two scalar loads, and each
+  // lane selects its chunk from those registers (no vector loads for cos/sin)
+  bool wave_scalar_row = false;
 };
 
 int plan_inplace(const rope_tensor *x, const rope_tensor *cos, const rope_tensor *sin,
@@ -188,6 +192,12 @@ constexpr int kGptjItemsPerLane = 2;  // GPT-J units are one vector
 // stitching (three cos|sin gathers per lane), where one row was 2-3% slower.
 constexpr int kWaveBlockNeox = 256;
 constexpr int kWaveBlockGptj = 64;
+// The scalar cos|sin row: on the 1 GiB GPT-J f16 workload (rotaryDim 64 of 128) 2.2% faster
+// than the two vector loads per lane, other GPT-J shapes with 128-byte rows 0.6-2.5%; at 64
+// tokens (512 wavefronts) 6% slower, where the extra scalar round trip is not hidden.  Taken
+// from eight wavefronts per compute unit up.
+constexpr int64_t kScalarRowBytes = 128;
+constexpr int64_t kScalarRowMinWaves = int64_t(kComputeUnits) * 8;
 constexpr uint32_t kWaveRowsPairUnits = 1;
 constexpr uint32_t kWaveRowsVectorUnits = 2;
 // Waves of one launch stay below 2^31, so a wave index plus the grid stride fits 32 bits.

@@ -107,6 +107,14 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
   CHECK(p.wave_heads == p.wave_rows * p.wave_hpw, "wave heads %u", p.wave_heads);
   CHECK(p.wave_block == uint32_t(neox ? kWaveBlockNeox : kWaveBlockGptj) && p.wave_block % 64 == 0,
         "wave workgroup of %u lanes", p.wave_block);
+  // the scalar cos|sin row: GPT-J rope mode, a 128-byte row (two 64-byte scalar loads, eight
+  // 8-byte chunks per half), launches of at least kScalarRowMinWaves wavefronts
+  const int64_t esz = 16 / V;
+  CHECK(p.wave_scalar_row == (!neox && sec.empty() && rd * esz == kScalarRowBytes &&
+                              p.waves >= kScalarRowMinWaves),
+        "scalar row %d for neox=%d rd %lld waves %lld", int(p.wave_scalar_row), int(neox),
+        (long long)rd, (long long)p.waves);
+  CHECK(!p.wave_scalar_row || (C * esz == 8 && half / C == 8), "scalar-row chunks");
   CHECK(int64_t(p.wave_wpt) * p.wave_heads >= nh &&
             int64_t(p.wave_wpt - 1) * p.wave_heads < nh, "waves per token %u", p.wave_wpt);
   CHECK(p.waves == T * int64_t(p.wave_wpt) && p.waves < kMaxWaves, "waves %lld",
@@ -218,7 +226,8 @@ static bool walk_waves(const CachePlan &p, bool neox, int64_t T, int64_t nq, int
   return true;
 }
 
-static int wave_plans = 0, xch_plans = 0, lin_plans = 0, pair_plans = 0, wide_pair_plans = 0;
+static int wave_plans = 0, xch_plans = 0, lin_plans = 0, pair_plans = 0, wide_pair_plans = 0,
+           scalar_row_plans = 0;
 // Every g_stride-th plan is walked (1: all of them); runs under the sanitizers use a sparser
 // sample of the same plans.
 static int g_stride = 1, g_seen = 0, g_walked = 0;
@@ -384,6 +393,7 @@ static bool walk(rope_dtype dt, bool neox, int64_t T, int64_t nq, int64_t nk, in
     lin_plans += p.wave_lin ? 1 : 0;
     pair_plans += neox && !p.wave_xch && !p.wave_lin ? 1 : 0;
     wide_pair_plans += neox && !p.wave_xch && !p.wave_lin && p.units > 32 ? 1 : 0;
+    scalar_row_plans += p.wave_scalar_row ? 1 : 0;
     return walk_waves(p, neox, T, nq, nk, H, rd, sec, cache_mode, qs);
   }
   return true;
@@ -488,16 +498,17 @@ int main(int argc, char **argv) {
     ++plans;
   }
   if (wave_plans == 0 || wave_plans == g_walked || xch_plans == 0 || lin_plans == 0 ||
-      pair_plans == 0 || wide_pair_plans == 0) {
+      pair_plans == 0 || wide_pair_plans == 0 || (scalar_row_plans == 0 && g_stride == 1)) {
     std::printf("FAIL: %d of %d plans take the wavefront path (%d exchange, %d one-vector "
-                "NeoX, %d pair units, %d of them over 32 lanes a head); every path and layout "
-                "must be covered\n",
-                wave_plans, g_walked, xch_plans, lin_plans, pair_plans, wide_pair_plans);
+                "NeoX, %d pair units, %d of them over 32 lanes a head, %d scalar-row GPT-J); "
+                "every path and layout must be covered\n",
+                wave_plans, g_walked, xch_plans, lin_plans, pair_plans, wide_pair_plans,
+                scalar_row_plans);
     return 1;
   }
   std::printf("ok %d %llu (%d walked, %d on the wavefront path: %d exchange, %d one-vector "
-              "NeoX, %d pair units, %d of them over 32 lanes a head)\n", plans,
-              (unsigned long long)items_checked, g_walked, wave_plans, xch_plans, lin_plans,
-              pair_plans, wide_pair_plans);
+              "NeoX, %d pair units, %d of them over 32 lanes a head, %d scalar-row GPT-J)\n",
+              plans, (unsigned long long)items_checked, g_walked, wave_plans, xch_plans,
+              lin_plans, pair_plans, wide_pair_plans, scalar_row_plans);
   return 0;
 }

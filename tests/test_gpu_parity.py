@@ -550,6 +550,38 @@ def test_cache_positions_out_of_range_are_clamped():
                   qo.cpu(), ko.cpu(), "clamped")
 
 
+@pytest.mark.parametrize(
+    "dt,H,T,nq,nk",
+    [(torch.float16, 128, 4096, 5, 3),    # rotaryDim 64 of 128: a pass-through half
+     (torch.bfloat16, 64, 3000, 7, 5),    # full rotary
+     (torch.float32, 96, 2500, 3, 2),     # rotaryDim 32 of 96 floats, two wavefronts a token
+     (torch.float16, 192, 2100, 1, 1)],   # 2 heads of 24 lanes: idle lanes in every wavefront
+    ids=["f16_rd64_of_128", "bf16_full", "f32_rd32_of_96", "f16_idle_lanes"])
+def test_cache_gptj_scalar_cos_sin_row(dt, H, T, nq, nk):
+    """GPT-J rope mode with a 128-byte cos|sin row in launches of at least eight wavefronts per
+    compute unit: each wavefront reads its token's row with scalar loads and every lane selects
+    its own chunk ([RSCC §rotate_interleaved（GPT-J style）旋转模式]).  Outputs start as all-ones
+    bit patterns and must all be overwritten; positions include out-of-range values (clamped,
+    so compared with the oracle at the clamped positions); every token is compared."""
+    rd = 128 // torch.empty(0, dtype=dt).element_size()
+    case = W.cache_case("srow", T, nq, nk, H, rd, dt, False, 900, seed=7000 + H, device=DEV)
+    pos = case.positions.clone()
+    pos[5] = 1 << 40
+    pos[T - 1] = -3
+    qo, ko = torch.empty_like(case.query), torch.empty_like(case.key)
+    ibits = torch.int32 if dt == torch.float32 else torch.int16
+    for t in (qo, ko):
+        t.view(ibits).fill_(-1)
+    ra.rope_with_cos_sin_cache(pos, case.query, case.key, case.cache, None, H, False,
+                               query_out=qo, key_out=ko)
+    torch.cuda.synchronize()
+    for name, t in (("q", qo), ("k", ko)):
+        left = int((t.view(ibits) == -1).sum())
+        assert left == 0, f"{left} {name} output elements never written"
+    compare_cache(pos.clamp(0, 899).cpu(), case.query.cpu(), case.key.cpu(), case.cache.cpu(),
+                  None, H, False, qo.cpu(), ko.cpu(), f"scalar row {dt} H{H}")
+
+
 def test_cache_max_tokens_and_large_rotary_dim():
     case = W.cache_case("maxT", 131073, 1, 1, 32, 32, torch.bfloat16, False, 1000, seed=11,
                         device=DEV)
