@@ -6,7 +6,7 @@ In-place op: dtype pair, D, slice (even or odd start, any even length), B/S/N, c
 rotary mode and direction.  Cache op: dtype, style, rope / mrope (every whitelisted list) and
 cacheMode, headSize and rotaryDim (including heads of 8 to 34 64-byte blocks, either side of
 64 units per head), head counts (up to 48 + 16), token count, cache length, positions and
-row strides.
+row strides; GPT-J rope mode with a 128-byte cos|sin row over 2048+ tokens on its own.
 """
 import numpy as np
 import pytest
@@ -150,3 +150,40 @@ def test_cache_fuzz_long_rotary_dim(seed):
     torch.cuda.synchronize()
     compare_cache(pos.cpu(), q.cpu(), k.cpu(), cache.cpu(), None, H, cfg["neox"], qo.cpu(),
                   ko.cpu(), f"long-rd fuzz {seed}: {cfg}")
+
+
+def cache_fuzz_scalar_row(seed):
+    """GPT-J rope mode with a 128-byte cos|sin row and at least 2048 tokens, so that every launch
+    has eight or more wavefronts per compute unit and each wavefront reads its token's row with
+    scalar loads (an own generator, so the seeds above keep their configurations)."""
+    rng = np.random.default_rng(6000 + seed)
+    dt = [torch.float32, torch.float16, torch.bfloat16][int(rng.integers(3))]
+    align = 64 // torch.empty(0, dtype=dt).element_size()
+    rd = 2 * align
+    H = rd + align * int(rng.integers(0, 4))
+    nq, nk = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+    if rng.random() < 0.2:
+        nq, nk = int(rng.integers(9, 33)), int(rng.integers(1, 9))
+    return dict(dt=dt, rd=rd, H=H, nq=nq, nk=nk, T=int(rng.integers(2048, 4097)),
+                max_seq=int(rng.integers(1, 3000)),
+                pad_q=int(rng.integers(1, 3)) * align if rng.random() < 0.3 else 0,
+                v2=bool(rng.integers(0, 2)))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_cache_fuzz_gptj_scalar_row(seed):
+    cfg = cache_fuzz_scalar_row(seed)
+    g = W.generator(7000 + seed, DEV)
+    T, H, rd, dt = cfg["T"], cfg["H"], cfg["rd"], cfg["dt"]
+    qbig = W.randn((T, cfg["nq"] * H + cfg["pad_q"]), dt, g)
+    q = qbig[:, :cfg["nq"] * H]
+    k = W.randn((T, cfg["nk"] * H), dt, g)
+    cache = W.randn((cfg["max_seq"], rd), dt, g)
+    pos = torch.randint(0, cfg["max_seq"], (T,), generator=g, device=DEV)
+    if cfg["v2"]:
+        qo, ko = ra.rope_with_cos_sin_cache_v2(pos, q, k, cache, None, H, False, 0)
+    else:
+        qo, ko = ra.rope_with_cos_sin_cache(pos, q, k, cache, None, H, False)
+    torch.cuda.synchronize()
+    compare_cache(pos.cpu(), q.cpu(), k.cpu(), cache.cpu(), None, H, False, qo.cpu(), ko.cpu(),
+                  f"scalar-row fuzz {seed}: {cfg}")
