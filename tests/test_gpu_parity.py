@@ -582,6 +582,41 @@ def test_cache_gptj_scalar_cos_sin_row(dt, H, T, nq, nk):
                   None, H, False, qo.cpu(), ko.cpu(), f"scalar row {dt} H{H}")
 
 
+@pytest.mark.parametrize("dt,H,rd,T,nq,nk,sec", [
+    (torch.bfloat16, 128, 96, 700, 5, 3, None), (torch.float16, 192, 192, 300, 3, 2, None),
+    (torch.float32, 96, 96, 500, 4, 4, None), (torch.bfloat16, 64, 64, 2500, 6, 2, None),
+    (torch.float16, 160, 32, 400, 3, 1, None), (torch.bfloat16, 64, 64, 600, 3, 2, [11, 11, 10])],
+    ids=["bf16_H128_rd96", "f16_H192_rd192", "f32_H96_rd96", "bf16_H64_rd64_T2500",
+         "f16_H160_rd32", "bf16_mrope_11_11_10"])
+def test_cache_neox_one_vector_units_shared_gather(dt, H, rd, T, nq, nk, sec):
+    """NeoX shapes whose rotated half is not a whole number of 128-byte lines and too wide for
+    the exchange layout: one vector per lane, the pair partner two or more lanes away, and the
+    pair's cos and sin halves gathered one by each lane and swapped
+    ([RSCC §rotate_half（GPT-NeoX style）旋转模式]).  Outputs start as all-ones bit patterns and
+    must all be overwritten; positions include out-of-range values (clamped, so compared with
+    the oracle at the clamped positions)."""
+    m = len(sec) if sec else 0
+    g = W.generator(7100 + H + rd, DEV)
+    pos = torch.randint(0, 800, (m, T) if m else (T,), generator=g, device=DEV)
+    case = W.cache_case("lin", T, nq, nk, H, rd, dt, True, 800, seed=7200 + H, device=DEV,
+                        mrope_section=sec, positions=pos)
+    pos = case.positions.clone()
+    pos.view(-1)[3] = 1 << 40
+    pos.view(-1)[-1] = -5
+    qo, ko = torch.empty_like(case.query), torch.empty_like(case.key)
+    ibits = torch.int32 if dt == torch.float32 else torch.int16
+    for t in (qo, ko):
+        t.view(ibits).fill_(-1)
+    ra.rope_with_cos_sin_cache(pos, case.query, case.key, case.cache, sec, H, True,
+                               query_out=qo, key_out=ko)
+    torch.cuda.synchronize()
+    for name, t in (("q", qo), ("k", ko)):
+        left = int((t.view(ibits) == -1).sum())
+        assert left == 0, f"{left} {name} output elements never written"
+    compare_cache(pos.clamp(0, 799).cpu(), case.query.cpu(), case.key.cpu(), case.cache.cpu(),
+                  sec, H, True, qo.cpu(), ko.cpu(), f"one-vector NeoX {dt} H{H} rd{rd} {sec}")
+
+
 def test_cache_max_tokens_and_large_rotary_dim():
     case = W.cache_case("maxT", 131073, 1, 1, 32, 32, torch.bfloat16, False, 1000, seed=11,
                         device=DEV)
