@@ -950,10 +950,10 @@ union CsChunk {
 // lane holds, and is read from there with ds_bpermute.  Each lane rotates its own vector.
 // LIN (NeoX): a unit is one vector, as in GPT-J, so a head's vectors lie on consecutive lanes
 // and each access covers whole heads; the pair partner (R vectors away, R = rotaryDim/(2V))
-// is read from its lane with ds_bpermute, as in XCH.  Outside multi-row stitching the two
-// lanes of a pair also share the gather of their cos|sin chunk (one 16-byte load each, swapped
-// over the same exchange): rope-mode shapes 4-7% faster than with both halves gathered per
-// lane, three-section mrope within noise.
+// is read from its lane with ds_bpermute, as in XCH.  In both, outside multi-row stitching,
+// the two lanes of a pair also share the gather of their cos|sin chunk (one 16-byte load each,
+// swapped over the same exchange).  Against both halves gathered per lane: LIN rope-mode shapes
+// 4-7% faster, XCH 1% (4% at 512 tokens), three-section mrope within noise.
 // NR: position rows read per token: 1 in rope mode (no section table), else the mrope
 // section count (3 or 4; multi-row stitching has 3).
 // WB: lanes per workgroup (the plan's wave_block).  SR: the token's cos|sin row is read with
@@ -1119,7 +1119,7 @@ __global__ __launch_bounds__(WB) void cos_sin_cache_wave_kernel(CachePlan p) {
         // second row wait for the first row's store as well (the counter is in order).
 #pragma unroll
         for (int k = 0; k < K; ++k) asm volatile("" ::"v"(v[k][0].v[0].x));
-      } else if constexpr (LIN) {
+      } else if constexpr (EXCH) {
         // the pair's two lanes share one chunk: the x1 lane gathers its cos half, the x2 lane
         // its sin half, and each takes the other half from its partner below
         load_words<CB, false>(row + (u < R ? int64_t(0) : half) + i0, cw.w);
@@ -1135,8 +1135,8 @@ __global__ __launch_bounds__(WB) void cos_sin_cache_wave_kernel(CachePlan p) {
     // 28.7 us with it (29.6 us with two rows).
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
-    if constexpr (LIN && !MULTI) {
-      // LIN: swap the gathered halves with the pair partner (idle and copy-only lanes read
+    if constexpr (EXCH && !MULTI) {
+      // XCH, LIN: swap the gathered halves with the pair partner (idle and copy-only lanes read
       // their own registers)
       const bool x1 = u < R;
 #pragma unroll

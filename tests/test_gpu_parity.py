@@ -585,13 +585,17 @@ def test_cache_gptj_scalar_cos_sin_row(dt, H, T, nq, nk):
 @pytest.mark.parametrize("dt,H,rd,T,nq,nk,sec", [
     (torch.bfloat16, 128, 96, 700, 5, 3, None), (torch.float16, 192, 192, 300, 3, 2, None),
     (torch.float32, 96, 96, 500, 4, 4, None), (torch.bfloat16, 64, 64, 2500, 6, 2, None),
-    (torch.float16, 160, 32, 400, 3, 1, None), (torch.bfloat16, 64, 64, 600, 3, 2, [11, 11, 10])],
+    (torch.float16, 160, 32, 400, 3, 1, None), (torch.bfloat16, 64, 64, 600, 3, 2, [11, 11, 10]),
+    (torch.bfloat16, 128, 64, 700, 5, 3, None), (torch.float32, 128, 32, 500, 3, 3, None),
+    (torch.bfloat16, 128, 64, 600, 3, 2, [11, 11, 10])],
     ids=["bf16_H128_rd96", "f16_H192_rd192", "f32_H96_rd96", "bf16_H64_rd64_T2500",
-         "f16_H160_rd32", "bf16_mrope_11_11_10"])
+         "f16_H160_rd32", "bf16_mrope_11_11_10", "xch_bf16_H128_rd64", "xch_f32_H128_rd32",
+         "xch_bf16_mrope_11_11_10"])
 def test_cache_neox_one_vector_units_shared_gather(dt, H, rd, T, nq, nk, sec):
-    """NeoX shapes whose rotated half is not a whole number of 128-byte lines and too wide for
-    the exchange layout: one vector per lane, the pair partner two or more lanes away, and the
-    pair's cos and sin halves gathered one by each lane and swapped
+    """NeoX shapes whose rotated half is not a whole number of 128-byte lines: one-vector units
+    (the pair partner two or more lanes away) and, with rotaryDim at most half the head, the
+    exchange layout; in both the pair's cos and sin halves are gathered one by each lane and
+    swapped
     ([RSCC §rotate_half（GPT-NeoX style）旋转模式]).  Outputs start as all-ones bit patterns and
     must all be overwritten; positions include out-of-range values (clamped, so compared with
     the oracle at the clamped positions)."""
