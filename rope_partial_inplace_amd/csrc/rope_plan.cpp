@@ -512,7 +512,9 @@ int plan_cache(const rope_tensor *positions, const rope_tensor *query_in,
   //  - otherwise one-vector units (accesses span whole heads).
   // Measured with bf16 q/k: rd 64 or 32 of H 128 36.7-43.2 -> 29.8-30.0 us with the exchange
   // layout; rd 96 of H 128 43.0 -> 33.1 us and H = rd = 64 36.2 -> 31.4 us with one-vector
-  // units, which are 5-12% slower than pair units on whole-line shapes.
+  // units (28.5 and 28.4 us once a pair's lanes shared the cos|sin gather).  On whole-line
+  // shapes one-vector units stay 1-2% slower than pair units in rope and three-section mrope,
+  // 26% with multi-row stitching.
   const int64_t line = 128;
   const bool pair_lines = (rd / 2 * es) % line == 0;
   const bool xch = p.neox && !pair_lines && 2 * rd <= head_size && (head_size / 2 * es) % line == 0;
